@@ -1,0 +1,205 @@
+"""Pins for the oracle's GEMM references and acceptance test (CPU only).
+
+The float64 references are pinned against exact rational brute force on tiny
+inputs (decoded with the scalar field formulas of ``oracle.scalar``), closed
+forms (constant codes, one-hot rows), an invariance (a consistent permutation
+of K blocks leaves C unchanged), and reductions between the variants.  Planted
+mistakes (wrong nibble order, wrong scale index, dropped tensor scale, a
+transposed operand) must make these pins fail: that is checked too."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from block_scaled_precision_bsgemm_amd import synth
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import quantize as Q
+from oracle import scalar as S
+
+
+def _exact_nvfp4(codes, scales, st):
+    """Rational dequantisation from the scalar field formulas."""
+    un = F.unpack_nibbles(codes)
+    R, K = un.shape
+    stf = Fraction(float(np.float32(st)))
+    return [[S.e2m1_frac(int(un[r, k])) * S.e4m3_frac(int(scales[r, k // 16])) * stf
+             for k in range(K)] for r in range(R)]
+
+
+def _exact_mxfp8(codes, scales):
+    R, K = codes.shape
+    return [[S.e4m3_frac(int(codes[r, k])) * Fraction(2) ** (int(scales[r, k // 32]) - 127)
+             for k in range(K)] for r in range(R)]
+
+
+def _exact_gemm(a, b):
+    return [[sum((x * y for x, y in zip(ra, rb)), Fraction(0)) for rb in b] for ra in a]
+
+
+def _exact_mag(a, b):
+    return [[sum((abs(x * y) for x, y in zip(ra, rb)), Fraction(0)) for rb in b] for ra in a]
+
+
+def _nvfp4_tiny(seed, m=4, k=64):
+    x = synth.normal_f32((m, k), seed)
+    x[:, 16:32] *= np.float32(0.01)          # mixed block scales
+    x[1, 40:48] *= np.float32(30.0)
+    return Q.quantize_nvfp4(x)
+
+
+def test_nvfp4_gemm_equals_exact_bruteforce():
+    a = _nvfp4_tiny(31)
+    b = _nvfp4_tiny(32)
+    c, t = G.gemm_nvfp4(*a, *b)
+    ea, eb = _exact_nvfp4(*a), _exact_nvfp4(*b)
+    ce, te = _exact_gemm(ea, eb), _exact_mag(ea, eb)
+    for i in range(4):
+        for j in range(4):
+            assert abs(Fraction(float(c[i, j])) - ce[i][j]) <= Fraction(1e-12) * te[i][j]
+            assert abs(Fraction(float(t[i, j])) - te[i][j]) <= Fraction(1e-12) * te[i][j]
+
+
+def test_mxfp8_gemm_equals_exact_bruteforce():
+    xa = synth.normal_f32((4, 32), 41)
+    xb = synth.normal_f32((4, 32), 42)
+    xa[2] *= np.float32(1e3)
+    a, b = Q.quantize_mxfp8(xa), Q.quantize_mxfp8(xb)
+    c, t = G.gemm_mxfp8(*a, *b)
+    ea, eb = _exact_mxfp8(*a), _exact_mxfp8(*b)
+    ce, te = _exact_gemm(ea, eb), _exact_mag(ea, eb)
+    for i in range(4):
+        for j in range(4):
+            assert abs(Fraction(float(c[i, j])) - ce[i][j]) <= Fraction(1e-12) * te[i][j]
+
+
+def test_nvfp4_constant_codes_closed_form():
+    M, N, K = 3, 5, 64
+    va, vb = 0x3, 0xA                                   # 1.5 and -1.0
+    sa, sb = 0x41, 0x2C                                 # e4m3: 2.25 and 0.375
+    a = (np.full((M, K // 2), va | (va << 4), np.uint8), np.full((M, K // 16), sa, np.uint8), np.float32(0.5))
+    b = (np.full((N, K // 2), vb | (vb << 4), np.uint8), np.full((N, K // 16), sb, np.uint8), np.float32(3.0))
+    c, t = G.gemm_nvfp4(*a, *b)
+    want = K * 1.5 * -1.0 * 2.25 * 0.375 * 0.5 * 3.0
+    assert np.all(c == want) and np.all(t == abs(want))
+
+
+def test_nvfp4_one_hot_rows_select_scaled_b():
+    K = 64
+    b = _nvfp4_tiny(5, m=6, k=K)
+    bd = G.dequant_nvfp4(*b)
+    codes = np.zeros((2, K), np.uint8)
+    codes[0, 17] = 0x2                                   # 1.0 at k = 17
+    codes[1, 50] = 0xC                                   # -2.0 at k = 50
+    scales = np.full((2, K // 16), 0x38, np.uint8)       # 1.0
+    c, _ = G.gemm_nvfp4(F.pack_nibbles(codes), scales, np.float32(1.0), *b)
+    assert np.array_equal(c[0], bd[:, 17]) and np.array_equal(c[1], -2.0 * bd[:, 50])
+
+
+def test_mxfp8_block_permutation_invariance():
+    xa, xb = synth.normal_f32((8, 256), 51), synth.normal_f32((8, 256), 52)
+    a, b = Q.quantize_mxfp8(xa), Q.quantize_mxfp8(xb)
+    c, t = G.gemm_mxfp8(*a, *b)
+    perm = np.random.Generator(np.random.PCG64(3)).permutation(8)
+    def pb(codes, scales):
+        return (codes.reshape(8, 8, 32)[:, perm].reshape(8, 256), scales[:, perm])
+    c2, t2 = G.gemm_mxfp8(*pb(*a), *pb(*b))
+    assert np.allclose(c, c2, rtol=0, atol=1e-12 * t.max()) and np.allclose(t, t2, rtol=1e-14)
+
+
+def test_grouped_reduces_to_per_group_products_and_handles_empty_groups():
+    K, N = 64, 6
+    counts = np.array([3, 0, 5, 0, 1])
+    off = synth.offsets_from_counts(counts)
+    x = synth.normal_f32((int(counts.sum()), K), 61)
+    a = Q.quantize_nvfp4(x)
+    w = synth.bf16_bits(synth.normal_f32((len(counts), N, K), 62, std=0.02))
+    c, t = G.grouped_nvfp4_bf16(*a, off, w)
+    ea = _exact_nvfp4(*a)
+    for g in range(len(counts)):
+        wg = [[Fraction(float(v)) for v in row] for row in F.decode_bf16(w[g])]
+        for r in range(off[g], off[g + 1]):
+            ce = _exact_gemm([ea[r]], wg)[0]
+            for n in range(N):
+                assert abs(Fraction(float(c[r, n])) - ce[n]) <= Fraction(1e-12) * (1 + abs(ce[n]))
+    # restricting rows returns the same rows
+    rows = np.array([8, 0, 4])
+    c2, _ = G.grouped_nvfp4_bf16(*a, off, w, rows=rows)
+    assert np.array_equal(c2, c[rows])
+
+
+def test_w4a16_equals_exact_bruteforce():
+    M, N, K = 3, 4, 64
+    x = synth.bf16_bits(synth.normal_f32((M, K), 71))
+    wq = Q.quantize_nvfp4(synth.normal_f32((N, K), 72, std=0.02))
+    c, t = G.w4a16(x, *wq)
+    xe = [[Fraction(float(v)) for v in row] for row in F.decode_bf16(x)]
+    ce = _exact_gemm(xe, _exact_nvfp4(*wq))
+    for i in range(M):
+        for j in range(N):
+            assert abs(Fraction(float(c[i, j])) - ce[i][j]) <= Fraction(1e-12) * (1 + abs(ce[i][j]))
+
+
+def test_check_accepts_rounded_reference_and_rejects_errors():
+    a, b = _nvfp4_tiny(81, m=8), _nvfp4_tiny(82, m=8)
+    c, t = G.gemm_nvfp4(*a, *b)
+    bits = synth.bf16_bits(c.astype(np.float32))
+    assert G.check(bits, c, t)["ok"]
+    bad = bits.copy()
+    bad[0, 0] ^= 0x0040                                  # a large mantissa bit
+    assert not G.check(bad, c, t)["ok"]
+    nan = bits.copy()
+    nan[1, 1] = 0x7FC0
+    r = G.check(nan, c, t)
+    assert not r["ok"] and r["n_nonfinite"] == 1
+
+
+# ---------------------------------------------------- negative controls --
+
+def _planted(monkeypatch, what):
+    if what == "nibble_order":
+        def wrong(p):
+            p = np.asarray(p, np.uint8)
+            out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.uint8)
+            out[..., 0::2], out[..., 1::2] = p >> 4, p & 0xF
+            return out
+        monkeypatch.setattr(G, "unpack_nibbles", wrong)
+    elif what == "scale_index":
+        orig = G.nvfp4_units
+        def wrong(codes, scales):
+            return orig(codes, np.roll(scales, 1, axis=1))
+        monkeypatch.setattr(G, "nvfp4_units", wrong)
+    elif what == "tensor_scale":
+        orig = G.gemm_nvfp4
+        monkeypatch.setattr(G, "gemm_nvfp4", lambda ac, asc, ats, bc, bs, bts, rows=None: orig(ac, asc, 1.0, bc, bs, bts, rows))
+    elif what == "transpose":
+        monkeypatch.setattr(G, "_matmul_and_mag", lambda a, b: ((a @ b.T).T, np.abs(a) @ np.abs(b).T))
+
+
+@pytest.mark.parametrize("what", ["scale_index", "tensor_scale", "transpose"])
+def test_planted_oracle_mistakes_fail_the_bruteforce_pin(monkeypatch, what):
+    a = _nvfp4_tiny(91)
+    b = _nvfp4_tiny(92)
+    a = (a[0], a[1], np.float32(0.75) if what == "tensor_scale" else a[2])
+    ea, eb = _exact_nvfp4(*a), _exact_nvfp4(*b)
+    ce, te = _exact_gemm(ea, eb), _exact_mag(ea, eb)
+    _planted(monkeypatch, what)
+    c, _ = G.gemm_nvfp4(*a, *b)
+    worst = max(abs(Fraction(float(c[i, j])) - ce[i][j]) / te[i][j] for i in range(4) for j in range(4))
+    assert worst > Fraction(1e-6), what
+
+
+def test_planted_nibble_swap_fails_the_one_sided_pins(monkeypatch):
+    """Swapping the nibble order on BOTH operands of an NVFP4 x NVFP4 product is
+    a consistent K permutation inside each 16-block, so C cannot see it; the
+    elementwise dequantisation and the mixed NVFP4 x dense products can."""
+    a = _nvfp4_tiny(93)
+    ea = _exact_nvfp4(*a)
+    x = synth.bf16_bits(synth.normal_f32((3, 64), 94))
+    c0, _ = G.w4a16(x, *a)
+    _planted(monkeypatch, "nibble_order")
+    d = G.dequant_nvfp4(*a)
+    assert any(Fraction(float(d[r, k])) != ea[r][k] for r in range(4) for k in range(64))
+    c1, t1 = G.w4a16(x, *a)
+    assert np.max(np.abs(c1 - c0) / t1) > 1e-6

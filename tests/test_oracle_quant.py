@@ -1,0 +1,216 @@
+"""Pins for the oracle's NVFP4 and MXFP8 quantizers (CPU only).
+
+The quantizers are pinned by properties that the recipe and the formats fix
+(what the tensor-absmax element and each block maximum must encode to, error
+bounds, minimal exponents, round trips, idempotence) and by byte-for-byte
+agreement with the independent scalar rational implementation in
+``oracle.scalar`` on inputs rich in ties, subnormal scales, zeros and -0.0."""
+
+import numpy as np
+import pytest
+
+from block_scaled_precision_bsgemm_amd import synth
+from oracle import formats as F
+from oracle import quantize as Q
+from oracle import scalar as S
+from oracle.gemm import dequant_mxfp8, dequant_nvfp4
+
+
+def _nvfp4_data(seed, rows=64, k=256):
+    x = synth.normal_f32((rows, k), seed)
+    x, _ = synth.with_outlier_rows(x, seed + 1, frac=0.05, factor=100.0)
+    return x
+
+
+def test_nvfp4_tensor_absmax_encodes_to_six_with_top_scale():
+    x = _nvfp4_data(1)
+    codes, scales, st = Q.quantize_nvfp4(x)
+    r, k = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    c = F.unpack_nibbles(codes)[r, k]
+    assert F.E2M1_TABLE[c] == np.sign(x[r, k]) * 6.0
+    assert scales[r, k // 16] == 0x7E
+    assert st == np.float32(np.float32(np.max(np.abs(x))) / np.float32(2688))
+
+
+def test_nvfp4_block_max_encodes_to_six_for_normal_scales():
+    x = _nvfp4_data(2)
+    codes, scales, _ = Q.quantize_nvfp4(x)
+    c = F.unpack_nibbles(codes).reshape(x.shape[0], -1, 16)
+    blocks = x.reshape(x.shape[0], -1, 16)
+    i = np.argmax(np.abs(blocks), axis=2)
+    cmax = np.take_along_axis(c, i[..., None], 2)[..., 0]
+    normal = (scales >= 0x08) & (scales <= 0x7E)
+    assert normal.mean() > 0.9
+    assert np.all(np.abs(F.E2M1_TABLE[cmax[normal]]) == 6.0)
+
+
+def test_nvfp4_elementwise_error_bound_and_monotone():
+    x = _nvfp4_data(3)
+    codes, scales, st = Q.quantize_nvfp4(x)
+    xh = dequant_nvfp4(codes, scales, st)
+    S_blk = np.repeat(F.decode_e4m3(scales) * np.float64(st), 16, axis=1)
+    q = np.abs(x.astype(np.float64)) / S_blk
+    # gap of the E2M1 grid at |q|; within the grid error <= half the gap (+ FP32 rounding of q)
+    grid = F.E2M1_TABLE[:8]
+    hi = np.minimum(np.searchsorted(grid, q), 7)
+    gap = grid[hi] - grid[np.maximum(hi - 1, 0)]
+    inside = q <= 6.0
+    err = np.abs(x - xh) / S_blk
+    assert np.all(err[inside] <= 0.5 * gap[inside] * (1 + 1e-6) + 1e-6 * q[inside])
+    # saturated elements sit at +-6 * S and are the block's largest
+    assert np.all(np.abs(xh[~inside]) == 6.0 * S_blk[~inside])
+    # within a block, |x| ordering is preserved by the magnitude codes
+    mag = F.unpack_nibbles(codes) & 7
+    xb, mb = np.abs(x).reshape(-1, 16), mag.reshape(-1, 16)
+    o = np.argsort(xb, axis=1, kind="stable")
+    assert np.all(np.diff(np.take_along_axis(mb, o, 1).astype(int), axis=1) >= 0)
+
+
+def _roundtrip_codes(rng, rows=32, k=128):
+    """Codes/scales meeting the round-trip conditions: every block has a
+    non-zero scale code and a +-6 element, one block uses scale 0x7E."""
+    scales = rng.integers(0x01, 0x7F, size=(rows, k // 16)).astype(np.uint8)
+    scales[0, 0] = 0x7E
+    codes = rng.integers(0, 16, size=(rows, k)).astype(np.uint8)
+    pos = rng.integers(0, 16, size=(rows, k // 16))
+    cb = codes.reshape(rows, -1, 16)
+    np.put_along_axis(cb, pos[..., None], (rng.integers(0, 2, size=pos.shape)[..., None] << 3) | 7, 2)
+    return F.pack_nibbles(cb.reshape(rows, k)), scales
+
+
+def test_nvfp4_roundtrip_quantize_of_dequantize():
+    rng = np.random.Generator(np.random.PCG64(5))
+    for st in (np.float32(2.0 ** -3), np.float32(1.0), np.float32(2.0 ** 5)):
+        codes, scales = _roundtrip_codes(rng)
+        x = dequant_nvfp4(codes, scales, st)
+        assert np.all(x.astype(np.float32) == x)          # exactly representable
+        # decoding keeps -0.0 (sign of zero codes survives)
+        un = F.unpack_nibbles(codes)
+        assert np.array_equal(np.signbit(x), (un >> 3).astype(bool))
+        c2, s2, st2 = Q.quantize_nvfp4(x.astype(np.float32))
+        assert st2 == st
+        assert np.array_equal(s2, scales)
+        assert np.array_equal(c2, codes)
+
+
+def test_nvfp4_zero_tensor_and_signed_zero():
+    x = np.zeros((2, 32), np.float32)
+    x[1, 3] = -0.0
+    codes, scales, st = Q.quantize_nvfp4(x)
+    assert st == 0 and not scales.any()
+    un = F.unpack_nibbles(codes)
+    assert un[1, 3] == 8 and un.sum() == 8
+    # a zero block inside a non-zero tensor: scale 0, sign-only codes
+    x = _nvfp4_data(9, rows=4, k=64)
+    x[2, 16:32] = 0.0
+    x[2, 17] = -0.0
+    codes, scales, _ = Q.quantize_nvfp4(x)
+    assert scales[2, 1] == 0
+    assert F.unpack_nibbles(codes)[2, 16:32].tolist() == [0, 8] + [0] * 14
+
+
+def test_nvfp4_subnormal_scales_are_kept_and_tiny_blocks_vanish():
+    x = np.zeros((1, 64), np.float32)
+    x[0, 0] = 2688.0                       # s_t = 1
+    x[0, 16] = 6 * 2.0 ** -9               # scale 2**-9 -> code 0x01
+    x[0, 32] = 6 * 3 * 2.0 ** -9           # scale 3 * 2**-9 -> code 0x03 (subnormal)
+    x[0, 48] = 6 * 2.0 ** -10              # scale 2**-10 ties to 0 (even) -> block vanishes
+    codes, scales, st = Q.quantize_nvfp4(x)
+    assert st == 1.0
+    assert scales[0].tolist() == [0x7E, 0x01, 0x03, 0x00]
+    un = F.unpack_nibbles(codes)[0]
+    assert un[16] == 7 and un[32] == 7 and un[48] == 0
+
+
+def test_mxfp8_scale_minimal_and_block_max_in_range():
+    x = synth.normal_f32((64, 512), 21)
+    x[3] *= np.float32(1e-30)
+    x[4] *= np.float32(1e30)
+    codes, scales = Q.quantize_mxfp8(x)
+    bamax = np.abs(x.astype(np.float64)).reshape(64, -1, 32).max(2)
+    e = scales.astype(np.int64) - 127
+    assert np.all(448.0 * np.ldexp(1.0, e) >= bamax)
+    assert np.all(448.0 * np.ldexp(1.0, e - 1) < bamax)
+    xh = dequant_mxfp8(codes, scales).reshape(64, -1, 32)
+    qmax = np.abs(xh).max(2) / np.ldexp(1.0, e)
+    assert np.all((qmax >= 224) & (qmax <= 448))
+    assert not np.any((codes & 0x7F) == 0x7F)            # never NaN codes
+
+
+def test_mxfp8_zero_and_tiny_blocks():
+    x = np.zeros((1, 96), np.float32)
+    x[0, 1] = -0.0
+    x[0, 32] = np.float32(1e-39)                         # float32 subnormal
+    x[0, 64] = 3.0
+    codes, scales = Q.quantize_mxfp8(x)
+    assert scales[0, 0] == 0 and codes[0, 1] == 0x80 and codes[0, :32].sum() == 0x80
+    assert scales[0, 1] == 0                             # clamped at 2**-127
+    assert scales[0, 2] == 127 - 7                       # 448 * 2**-7 = 3.5 >= 3 > 1.75
+    assert F.decode_e4m3(codes[0, 64]) * 2.0 ** -7 == 3.0
+
+
+def test_mxfp8_roundtrip_and_idempotence():
+    rng = np.random.Generator(np.random.PCG64(8))
+    rows, k = 16, 256
+    codes = rng.integers(0, 256, size=(rows, k)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x10                 # no NaN codes
+    cb = codes.reshape(rows, -1, 32)
+    pos = rng.integers(0, 32, size=(rows, k // 32))
+    top = rng.integers(0x78, 0x7F, size=pos.shape).astype(np.uint8)   # |max| in [256, 448]
+    mags = cb & 0x7F
+    mags = np.minimum(mags, 0x73)
+    np.put_along_axis(mags, pos[..., None], top[..., None], 2)
+    cb = (cb & 0x80) | mags
+    codes = cb.reshape(rows, k)
+    scales = rng.integers(100, 150, size=(rows, k // 32)).astype(np.uint8)
+    x = dequant_mxfp8(codes, scales)
+    c2, s2 = Q.quantize_mxfp8(x.astype(np.float32))
+    assert np.array_equal(s2, scales) and np.array_equal(c2, codes)
+    y = synth.normal_f32((8, 128), 4)
+    c, s = Q.quantize_mxfp8(y)
+    d1 = dequant_mxfp8(c, s)
+    c3, s3 = Q.quantize_mxfp8(d1.astype(np.float32))
+    assert np.array_equal(dequant_mxfp8(c3, s3), d1)
+
+
+def _tricky_rows(seed, rows, k):
+    r = np.random.Generator(np.random.PCG64(seed))
+    x = r.standard_normal((rows, k)).astype(np.float32)
+    x[0] = 0.0
+    x[1, ::3] = -0.0
+    x[2] = (r.integers(-12, 13, k) * 0.25).astype(np.float32)          # exact ties
+    x[3] *= np.float32(1e-3)
+    x[4, :16] = np.float32(1e-4)                                        # small blocks
+    x[5] = np.exp2(r.uniform(-20, 8, k)).astype(np.float32) * np.sign(r.standard_normal(k)).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nvfp4_vector_equals_scalar(seed):
+    x = _tricky_rows(seed, 8, 64)
+    codes, scales, st = Q.quantize_nvfp4(x)
+    sc, ss, sst = S.quantize_nvfp4_scalar(x.tolist())
+    assert float(sst) == float(st)
+    assert np.array_equal(F.unpack_nibbles(codes), np.array(sc, dtype=np.uint8))
+    assert np.array_equal(scales, np.array(ss, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mxfp8_vector_equals_scalar(seed):
+    x = _tricky_rows(seed + 10, 8, 64)
+    codes, scales = Q.quantize_mxfp8(x)
+    sc, ss = S.quantize_mxfp8_scalar(x.tolist())
+    assert np.array_equal(codes, np.array(sc, dtype=np.uint8))
+    assert np.array_equal(scales, np.array(ss, dtype=np.uint8))
+
+
+def test_nvfp4_random_blocks_vector_equals_scalar_many():
+    """~10^4 blocks: random magnitudes spanning the E4M3 scale range, with a
+    fixed tensor scale so subnormal and saturated scales both occur."""
+    r = np.random.Generator(np.random.PCG64(77))
+    x = (r.standard_normal((40, 16 * 16)) * np.exp2(r.uniform(-16, 10, (40, 1)))).astype(np.float32)
+    codes, scales, st = Q.quantize_nvfp4(x, tensor_scale=np.float32(0.01))
+    sc, ss, _ = S.quantize_nvfp4_scalar(x.tolist(), tensor_scale=0.009999999776482582)
+    assert np.array_equal(F.unpack_nibbles(codes), np.array(sc, dtype=np.uint8))
+    assert np.array_equal(scales, np.array(ss, dtype=np.uint8))
+    assert (scales < 8).any() and (scales == 0x7E).any()
