@@ -1,0 +1,187 @@
+// Shared device helpers for the bsgemm kernels (gfx950 / CDNA4).
+//
+// The codecs below encode and decode the element and scale formats with integer
+// operations on IEEE binary32 bit patterns:
+//   - E2M1, E4M3 (FN) and E8M0, as in the OCP Microscaling Formats (MX) v1.0 spec;
+//   - BF16.
+// Every encoder rounds to nearest with ties to even and saturates at the
+// format's largest finite value, so the quantizers are bit-exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef unsigned short v8us __attribute__((ext_vector_type(8)));
+
+// ------------------------------------------------------------------ encoders
+
+// |a| -> 7-bit E4M3 magnitude code.  RNE, saturating at 0x7E (448).
+// Below 2^-6 the E4M3 grid is uniform with step 2^-9: scale by 512 (exact) and
+// round to an integer (ties to even).  At and above 2^-6, keep 3 mantissa bits
+// of the binary32 pattern with a round-half-even carry, then rebias the
+// exponent from 127 to 7.
+__device__ __forceinline__ uint32_t e4m3_encode_mag(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
+  const uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;   // [exp8 | mant3]
+  const uint32_t nrm = r - (120u << 3);
+  const uint32_t c = (a < 0.015625f) ? sub : nrm;
+  return c > 0x7Eu ? 0x7Eu : c;
+}
+
+// |a| -> 3-bit E2M1 magnitude code.  RNE, saturating at 7 (6.0).
+// Below 1 the grid is uniform with step 0.5.  At and above 1, keep 1 mantissa
+// bit and rebias the exponent from 127 to 1.
+__device__ __forceinline__ uint32_t e2m1_encode_mag(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const uint32_t sub = (uint32_t)__builtin_rintf(a * 2.0f);
+  const uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;  // [exp8 | mant1]
+  const uint32_t nrm = r - (126u << 1);
+  const uint32_t c = (a < 1.0f) ? sub : nrm;
+  return c > 7u ? 7u : c;
+}
+
+// ------------------------------------------------------------------ decoders
+
+// E4M3 magnitude code (0..0x7E) -> its exact FP32 value.
+__device__ __forceinline__ float e4m3_decode_mag(uint32_t c) {
+  const float nrm = __uint_as_float((c + 960u) << 20);   // rebias exponent 7 -> 127
+  const float sub = (float)c * 0.001953125f;             // c * 2^-9, exact
+  return c < 8u ? sub : nrm;
+}
+
+// Exact FP32 value of an E4M3 scale code.  NVFP4 scales are non-negative; the
+// sign bit is ignored.  The NaN code 0x7F is not produced by the quantizer.
+__device__ __forceinline__ float e4m3_scale_value(uint32_t code) {
+  return e4m3_decode_mag(code & 0x7Fu);
+}
+
+// The gfx950 scaled conversions (v_cvt_scalef32_pk_*_fp4) multiply by 2^E,
+// where E is the exponent field of their FP32 scale operand; the mantissa is
+// ignored.  An E4M3 scale s = 2^E * (1 + f), with f in {0, 1/8, ..., 7/8}, is
+// therefore applied in two exact steps:
+//   - the conversion, given s itself, supplies 2^E;
+//   - a multiply supplies (1 + f).
+// This returns 1 + f as an FP16 pair, for v_pk_mul_f16.  For s == 0 it
+// returns 0, so a zero scale gives exact zeros: the conversion alone would
+// scale by 2^-127.
+__device__ __forceinline__ uint32_t scale_mantissa_f16x2(float s) {
+  const uint32_t m = ((__float_as_uint(s) >> 13) & 0x3FFu) | 0x3C00u;  // 1.f as FP16
+  return s == 0.0f ? 0u : (m | (m << 16));
+}
+
+// The same mantissa factor as an FP32 value, for the FP32 dequantisation
+// path; 0 for a zero scale.
+__device__ __forceinline__ float scale_mantissa_f32(float s) {
+  const float m = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
+  return s == 0.0f ? 0.0f : m;
+}
+
+// ---------------------------------------------------------------------- BF16
+
+// FP32 -> BF16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Two FP32 -> packed BF16 pair (lo in bits 15:0), RNE.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ------------------------------------------------------- FP4 -> 16-bit dequant
+
+// Eight E2M1 codes (one dword; element j in nibble j) scaled by an E4M3 scale
+// `s` (its FP32 value) and its mantissa factor `mant2` (scale_mantissa_f16x2(s)).
+// Returns the eight exact FP16 products e2m1 * s, element j in lane j.
+// Each product has at most 6 significant bits and lies in [2^-10, 2688], so it
+// is exact in FP16.
+__device__ __forceinline__ v8h dequant8_f16(uint32_t codes, float s, uint32_t mant2) {
+  v2h m;
+  __builtin_memcpy(&m, &mant2, 4);
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 0) * m;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 1) * m;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 2) * m;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 3) * m;
+  v8h out;
+  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
+  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
+  return out;
+}
+
+// Eight E2M1 codes times an E4M3 scale, as exact BF16 values.  The BF16
+// products have at most 6 significant bits, so they are exact.  The
+// conversion gives v * 2^E as FP32; one FP32 multiply by (1 + f) completes the
+// scale; the high halves of the exact FP32 results are the BF16 patterns.
+template <int J>
+__device__ __forceinline__ uint32_t dequant2_bf16(uint32_t codes, float s, float mant) {
+  const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, s, J);
+  return (__float_as_uint(p[0] * mant) >> 16) | (__float_as_uint(p[1] * mant) & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ v8bf dequant8_bf16(uint32_t codes, float s, float mant) {
+  const uint32_t w[4] = {dequant2_bf16<0>(codes, s, mant), dequant2_bf16<1>(codes, s, mant),
+                         dequant2_bf16<2>(codes, s, mant), dequant2_bf16<3>(codes, s, mant)};
+  v8bf out;
+  __builtin_memcpy(&out, w, 16);
+  return out;
+}
+
+// ----------------------------------------------------------- buffer loads
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads at offsets outside it
+// return zero.  `bytes` must be < 2^31.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load_x4(rsrc_t r, int off) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint32_t buffer_load_u32(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t buffer_load_u8(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+
+// -------------------------------------------------------------------- misc
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8), and each XCD has its own L2.  Remap the linear workgroup index so
+// that each XCD processes one contiguous range of tile indices; neighbouring
+// tiles then share operands in one L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+  constexpr int XCD = 8;
+  const int per = nblocks / XCD;       // full rounds
+  const int rem = nblocks % XCD;
+  const int x = bid % XCD, i = bid / XCD;
+  // XCD x owns per (+1 if x < rem) consecutive indices.
+  const int base = x * per + (x < rem ? x : rem);
+  return base + i;
+}
+
+}  // namespace bsg

@@ -1,0 +1,222 @@
+// Ragged grouped GEMM: NVFP4 activations x dense BF16 weights, BF16 output.
+//
+// Source: "Triton #11171 -- Why Two New NVFP4 Test Cases Produced Twelve
+// Tensor-Memory Failures", sections "Ragged mode added routing rather than a
+// plain matrix" and "NVFP4 x dense matmul".  Routed activation rows are
+// grouped per slice (expert), and each slice meets its own dense operand.
+// That page stages an expanded (dequantised) copy of the NVFP4 operand for
+// the dense MMA.  Here each wave expands its own fragments in registers
+// instead, exactly, to BF16.
+//
+// Scheduling.  The host knows only G, m_total and n; the row counts stay on
+// the device.  The grid therefore covers an upper bound on the number of
+// tiles: sum_g ceil(c_g / BM) <= m_total / BM + G.  Each workgroup finds its
+// (group, m-tile) with a wave-wide prefix scan over the offsets.  Workgroups
+// past the real tile count exit at once.  Tiles are ordered m-tile-major, so
+// the n-tiles of one m-tile (same A rows) and the m-tiles of one group (same
+// W panel) run close together.  xcd_remap keeps neighbours on one XCD's L2.
+//
+// Tile: 256 rows x 256 columns, 4 waves of 128 x 128, K step 64 elements:
+//   - A codes [256][32] bytes, A scales [256] dwords (4 E4M3 bytes);
+//   - W [256][64] BF16, 16-byte chunks swizzled by (row & 7).
+// K assignment (A and W agree): lane (r = l % 32, g = l / 32) takes K
+// elements [32g, 32g + 32) of the step.  Dword sp of that range feeds MFMA
+// sub-step sp at positions 8g..8g+7; its scale block is 2g + sp/2, and its W
+// chunk is 4g + sp.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bsg {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int AROWB = BK / 2;        // A code bytes per row per step
+constexpr int WROWB = BK * 2;        // W bytes per row per step
+
+struct Smem {
+  uint8_t a[2][BM * AROWB];
+  uint32_t as[2][BM];
+  uint8_t w[2][BN * WROWB];
+  int tile_info[4];
+};
+
+__device__ __forceinline__ int wswz(int row, int chunk) { return row * WROWB + ((chunk ^ (row & 7)) << 4); }
+
+// Find the group holding global m-tile `mt` (tiles of BM rows counted group by
+// group).  Run by wave 0.  Writes {group, first row, end row} to `info`, or
+// group = -1 when mt is past the last tile.
+__device__ void find_tile(const int32_t* __restrict__ off, int G, int mt, int lane, int* info) {
+  int base = 0;   // m-tiles before the current chunk of 64 groups
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    int tiles = 0, lo = 0;
+    if (g < G) {
+      lo = off[g];
+      tiles = (off[g + 1] - lo + BM - 1) / BM;
+    }
+    int incl = tiles;   // inclusive prefix sum over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int excl = incl - tiles;
+    if (g < G && mt >= base + excl && mt < base + incl) {
+      const int local = mt - base - excl;
+      info[0] = g;
+      info[1] = lo + local * BM;
+      info[2] = min(lo + (local + 1) * BM, (int)off[g + 1]);
+    }
+    base += __shfl(incl, 63);
+    if (mt < base) return;
+  }
+  if (lane == 0) info[0] = -1;
+}
+
+__global__ __launch_bounds__(NT, 1) void grouped_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
+    const int32_t* __restrict__ off, const uint16_t* __restrict__ W, uint16_t* __restrict__ C,
+    int G, int M, int N, int K, int tiles_n) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int mt = t / tiles_n, nt = t - mt * tiles_n;
+  if (wave == 0) find_tile(off, G, mt, lane, sm.tile_info);
+  __syncthreads();
+  const int grp = sm.tile_info[0];
+  if (grp < 0) return;                      // uniform over the workgroup
+  // Offsets are a documented precondition; clamping keeps even malformed
+  // ones inside the A and C buffers.
+  const int r0 = min(max(sm.tile_info[1], 0), M), r1 = min(max(sm.tile_info[2], r0), M);
+  const int n0 = nt * BN;
+  const int KT = (K + BK - 1) / BK;
+  const int KH = K / 2, KB = K / 16;
+  const bool al4 = (KB & 3) == 0;
+
+  const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
+  const auto ca_rsrc = make_rsrc(A + (int64_t)r0 * KH, rows_a * KH);
+  const auto sa_rsrc = make_rsrc(As + (int64_t)r0 * KB, rows_a * KB);
+  const auto w_rsrc = make_rsrc(W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+
+  // staging: A chunk (tid & 1) of rows (tid >> 1) + 128 i; A scale dword of
+  // row tid; W chunk (tid & 7) of rows (tid >> 3) + 32 i.
+  const int alc = tid & 1, alr = tid >> 1;
+  const int wlc = tid & 7, wlr = tid >> 3;
+  uint4 ra[2], rw[8];
+  uint32_t rsa;
+  auto gload = [&](int kt) {
+    const bool akin = kt * AROWB + alc * 16 < KH;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      ra[i] = akin ? buffer_load_x4(ca_rsrc, (alr + 128 * i) * KH + kt * AROWB + alc * 16)
+                   : make_uint4(0, 0, 0, 0);
+    const int soff = tid * KB + kt * 4;
+    uint32_t s;
+    if (al4) {
+      s = buffer_load_u32(sa_rsrc, soff);
+    } else {
+      s = __builtin_amdgcn_raw_buffer_load_b16(sa_rsrc, soff, 0, 0) |
+          ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sa_rsrc, soff + 2, 0, 0) << 16);
+    }
+    const int valid = KB - kt * 4;
+    if (valid < 4) s &= valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
+    rsa = s;
+    const bool wkin = kt * BK + wlc * 8 < K;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      rw[i] = wkin ? buffer_load_x4(w_rsrc, ((wlr + 32 * i) * K + kt * BK + wlc * 8) * 2)
+                   : make_uint4(0, 0, 0, 0);
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(&sm.a[buf][(alr + 128 * i) * AROWB + alc * 16]) = ra[i];
+    sm.as[buf][tid] = rsa;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint4*>(&sm.w[buf][wswz(wlr + 32 * i, wlc)]) = rw[i];
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  if (KT > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    uint4 ca[4];
+    float s[4][2], mant[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r;
+      ca[i] = *reinterpret_cast<const uint4*>(&sm.a[buf][row * AROWB + g * 16]);
+      const uint32_t sc = sm.as[buf][row];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        s[i][b] = e4m3_scale_value((sc >> (16 * g + 8 * b)) & 0xFFu);
+        mant[i][b] = scale_mantissa_f32(s[i][b]);
+      }
+    }
+#pragma unroll
+    for (int sp = 0; sp < 4; ++sp) {
+      v8bf av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t d = sp == 0 ? ca[i].x : sp == 1 ? ca[i].y : sp == 2 ? ca[i].z : ca[i].w;
+        av[i] = dequant8_bf16(d, s[i][sp >> 1], mant[i][sp >> 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wn * 128 + j * 32 + r;
+        const uint4 q = *reinterpret_cast<const uint4*>(&sm.w[buf][wswz(row, 4 * g + sp)]);
+        __builtin_memcpy(&bv[j], &q, 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  const float alpha = *Ats;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = r0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (row < r1 && col < N)
+          C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
+                          const uint8_t* a, const uint8_t* as, const float* ats,
+                          const int32_t* offsets, const uint16_t* w, uint16_t* c,
+                          hipStream_t stream) {
+  const int tiles_n = (int)ceil_div(n, BN);
+  const int64_t mtiles_max = m_total / BM + num_groups;   // >= sum_g ceil(c_g / BM)
+  hipLaunchKernelGGL(grouped_kernel, dim3((unsigned)(mtiles_max * tiles_n)), dim3(NT), 0, stream,
+                     a, as, ats, offsets, w, c, num_groups, (int)m_total, (int)n, (int)k, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace bsg

@@ -1,0 +1,31 @@
+// Host-side launchers of the bsgemm kernels.  Arguments are validated by the
+// C ABI layer (api.cpp) before any of these is called; the launchers only
+// choose a configuration and enqueue kernels on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsg {
+
+hipError_t launch_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream, int num_cus);
+hipError_t launch_quantize_nvfp4(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                                 uint8_t* scales, float* tensor_scale, hipStream_t stream,
+                                 int num_cus);
+
+hipError_t launch_gemm_mxfp8(int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                             const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
+                             hipStream_t stream);
+hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                             const uint8_t* as, const float* ats, const uint8_t* b,
+                             const uint8_t* bs, const float* bts, uint16_t* c,
+                             hipStream_t stream);
+hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
+                          const uint8_t* a, const uint8_t* as, const float* ats,
+                          const int32_t* offsets, const uint16_t* w, uint16_t* c,
+                          hipStream_t stream);
+hipError_t launch_w4a16(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
+                        const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream);
+
+}  // namespace bsg

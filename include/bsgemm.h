@@ -1,0 +1,224 @@
+/*
+ * bsgemm -- block-scaled low-precision GEMM for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of the library.  Plain pointers and sizes only.
+ *
+ * The operation is C[m][n] = sum_k deq(A)[m][k] * deq(B)[n][k]:
+ *   - A is [M][K] and B is [N][K], both K-contiguous;
+ *   - FP32 accumulation;
+ *   - C is [M][N] BF16, rounded to nearest-even.
+ * Sources:
+ *   - "Together AI Ports ThunderKittens GEMM Kernels to NVIDIA Vera Rubin NVL72",
+ *     section "Building the GEMM": block-scaled NVFP4 and FP8 E4M3 GEMMs; M x N
+ *     output tiles sharing B along M; a K loop over staged operand chunks.
+ *   - "Triton #11171 -- Why Two New NVFP4 Test Cases Produced Twelve
+ *     Tensor-Memory Failures", sections "The missing case was defined by shape,
+ *     layout, and execution mode together" and "Ragged mode added routing rather
+ *     than a plain matrix": NVFP4 activations x a dense BF16 operand, ragged
+ *     (routed) rows, BF16 output.
+ *   - "Add sm121 (GB10) tier to the 4-bit GEMM dispatch heuristic" (bitsandbytes
+ *     PR #2030), sections "Methodology" and "The SIMT / MMA layer": a fused
+ *     small-M GEMM with 4-bit weights and BF16 activations.
+ *
+ * Formats (bit layouts per the OCP Microscaling Formats (MX) v1.0 spec):
+ *   NVFP4 operand [R][K], K % 32 == 0:
+ *     codes  uint8 [R][K/2]   E2M1 values; element 2j in the low nibble of byte j
+ *     scales uint8 [R][K/16]  E4M3 (FN) scale of each 16-element block along K
+ *     tscale float            FP32 per-tensor decode scale
+ *     value  = e2m1(code) * e4m3(scale) * tscale
+ *   MXFP8 operand [R][K], K % 32 == 0:
+ *     codes  uint8 [R][K]     E4M3 (FN) values
+ *     scales uint8 [R][K/32]  E8M0 scale of each 32-element block along K
+ *     value  = e4m3(code) * 2^(scale - 127)
+ *   BF16 operands and outputs are uint16 bit patterns, row-major.
+ *
+ * Conventions common to every call:
+ *   - Pointers are DEVICE pointers (visible to the current HIP device), unless
+ *     noted.  The caller allocates and owns every buffer.  The library never
+ *     allocates, frees or keeps a pointer after the call returns.
+ *   - Buffers are dense and row-major; pitches are implied by the sizes.  Code
+ *     buffers, x, w_bf16, x_bf16 and c_bf16 must be 16-byte aligned.  Scale
+ *     buffers and scalar slots need only their natural alignment.
+ *   - Work is queued on `stream` (a hipStream_t; NULL = the null stream).  The
+ *     call returns without waiting.  Keep the buffers alive until the stream
+ *     has finished.
+ *   - Every call returns a bsgemm_status.  All arguments are validated before
+ *     anything is launched: a failing call launches nothing, and a passing call
+ *     always launches its work (never a silent no-op).  bsgemm_last_error()
+ *     gives a message for the last failure on the calling thread.
+ *   - Preconditions that are documented but not checked on the device: inputs
+ *     are finite, and group offsets are monotone.
+ *   - Results do not depend on the launch configuration chosen internally
+ *     beyond FP32 summation order (quantizers: bit-exact).
+ */
+#ifndef BSGEMM_H
+#define BSGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum bsgemm_status {
+  BSGEMM_OK = 0,
+  BSGEMM_ERR_INVALID_ARG = 1,   /* null pointer, negative size, num_groups < 1 */
+  BSGEMM_ERR_UNSUPPORTED = 2,   /* k % 32 != 0, unknown format, bad format/scale combination */
+  BSGEMM_ERR_BAD_ALIGNMENT = 3, /* a pointer required to be 16-byte aligned is not */
+  BSGEMM_ERR_DEVICE = 4,        /* no HIP device, or the current device is not gfx950 */
+  BSGEMM_ERR_RESOURCE = 5,      /* no kernel configuration fits the problem */
+  BSGEMM_ERR_LAUNCH = 6         /* the HIP runtime reported a launch failure */
+};
+
+enum bsgemm_format {
+  BSGEMM_NVFP4 = 1,
+  BSGEMM_MXFP8 = 2
+};
+
+/*
+ * NVFP4 quantizer: x[rows][k] (FP32) -> codes, scales, *tensor_scale.
+ *
+ *   1. amax = max |x| over the whole tensor;
+ *      s_t  = fl32(amax / 2688), where 2688 = 6 * 448.
+ *   2. For each 16-element block along k:
+ *        bamax  = max |x|;
+ *        s_real = fl32(fl32(bamax / 6) / s_t);
+ *        scale  = E4M3_RNE_satfinite(s_real).  Subnormal scales are kept.
+ *        If s_t == 0, scale = 0.
+ *   3. S = fl32(e4m3(scale) * s_t).  For each element:
+ *        code = signbit(x) << 3 | E2M1_RNE_satfinite(|fl32(x / S)|).
+ *      If S == 0, code = signbit(x) << 3.
+ * Every FP32 step is IEEE round-to-nearest-even.  The output is bit-exact.
+ *
+ * Scale recipe: "scale = block absmax / 6, over the tensor scale"; "tensor
+ * scale = absmax / (6 * 448)".  The pages name the format ("Together AI Ports
+ * ThunderKittens ...", section "Building the GEMM"; "Triton #11171 ...",
+ * section "The existing tests already mentioned NVFP4") but do not print the
+ * recipe.
+ *
+ * Arguments:
+ *   x            device float[rows][k], 16-byte aligned
+ *   codes        device uint8[rows][k/2], 16-byte aligned (written)
+ *   scales       device uint8[rows][k/16] (written)
+ *   tensor_scale device float[1] (written).  Used as the amax slot during the
+ *                call: it holds amax bits until the call's last kernel has run.
+ * Sizes: rows >= 0, k >= 0, k % 32 == 0.
+ * With rows * k == 0, *tensor_scale is set to 0.
+ * Launches 4 kernels on `stream`: reset slot, amax, finalize, encode.
+ */
+int bsgemm_quantize_nvfp4(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                          uint8_t* scales, float* tensor_scale, void* stream);
+
+/*
+ * MXFP8 quantizer: x[rows][k] (FP32) -> codes uint8[rows][k], scales uint8[rows][k/32].
+ *
+ *   For each 32-element block along k:
+ *     bamax = max |x|;
+ *     e     = ceil(log2(bamax / 448)), computed exactly as
+ *             min{e : 448 * 2^e >= bamax}, clamped to [-127, 127]
+ *             (bamax == 0 gives -127);
+ *     scale = e + 127 (E8M0);
+ *     code  = signbit(x) << 7 | E4M3_RNE_satfinite(|x * 2^-e|).
+ * The output is bit-exact.  Format named on the pages: "MXFP" ("Triton
+ * #11171 ...", section "The broader related matrix protected neighboring
+ * policy"); "FP8 E4M3" ("Together AI Ports ThunderKittens ...", section
+ * "Building the GEMM").
+ *
+ * Arguments:
+ *   x      device float[rows][k], 16-byte aligned
+ *   codes  device uint8[rows][k], 16-byte aligned (written)
+ *   scales device uint8[rows][k/32] (written)
+ * Sizes: rows >= 0, k >= 0, k % 32 == 0.
+ */
+int bsgemm_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                          uint8_t* scales, void* stream);
+
+/*
+ * Dense block-scaled GEMM with both operands in format `fmt`:
+ *   C[m][n] = bf16_RNE( sum_k deq(A)[m][k] * deq(B)[n][k] )
+ * with FP32 accumulation.  For NVFP4 the sum runs over
+ * (e2m1 * e4m3)_A * (e2m1 * e4m3)_B and is then multiplied by
+ * (*a_tscale) * (*b_tscale).
+ * Source: "Together AI Ports ThunderKittens GEMM Kernels to NVIDIA Vera Rubin
+ * NVL72", section "Building the GEMM" (NVFP4 and FP8 E4M3 GEMMs, 16k square).
+ *
+ * Arguments:
+ *   fmt                 BSGEMM_NVFP4 or BSGEMM_MXFP8
+ *   a, a_scales         operand A [m][k] in the layout of `fmt`
+ *   a_tscale, b_tscale  device float[1] for NVFP4; must be NULL for MXFP8
+ *   b, b_scales         operand B [n][k], in the same format
+ *   c_bf16              device uint16[m][n] (written)
+ * Sizes: m, n, k >= 0, k % 32 == 0.
+ *   m == 0 or n == 0: returns BSGEMM_OK and launches nothing.
+ *   k == 0: C is all zeros.
+ */
+int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k,
+               const uint8_t* a, const uint8_t* a_scales, const float* a_tscale,
+               const uint8_t* b, const uint8_t* b_scales, const float* b_tscale,
+               uint16_t* c_bf16, void* stream);
+
+/*
+ * Ragged grouped GEMM: NVFP4 activations x dense BF16 weights.
+ * Rows off[g] .. off[g+1]-1 of A belong to group g and are multiplied with
+ * W[g]:
+ *   C[r][n] = bf16_RNE( s_t * sum_k (e2m1 * e4m3)(A)[r][k] * W[g][n][k] )
+ * Source: "Triton #11171 -- Why Two New NVFP4 Test Cases Produced Twelve
+ * Tensor-Memory Failures", sections "Ragged mode added routing rather than a
+ * plain matrix" and "NVFP4 x dense matmul": routed per-slice activations meet
+ * their slice's dense RHS, BF16 output.
+ *
+ * Arguments:
+ *   num_groups    G >= 1
+ *   m_total       total rows of A and C
+ *   a, a_scales, a_tscale
+ *                 NVFP4 activations [m_total][k], one tensor scale for all rows
+ *   group_offsets device int32[G+1], with off[0] = 0, off[G] = m_total, and
+ *                 non-decreasing.  Empty groups are allowed.  Read on the
+ *                 device; the host never waits for it.
+ *   w_bf16        device uint16[G][n][k]
+ *   c_bf16        device uint16[m_total][n] (written)
+ * Sizes: m_total, n, k >= 0, k % 32 == 0.
+ *   m_total == 0 or n == 0: BSGEMM_OK and nothing is launched.
+ */
+int bsgemm_grouped_run(int num_groups, int64_t m_total, int64_t n, int64_t k,
+                       const uint8_t* a, const uint8_t* a_scales, const float* a_tscale,
+                       const int32_t* group_offsets, const uint16_t* w_bf16,
+                       uint16_t* c_bf16, void* stream);
+
+/*
+ * Small-M weight-only 4-bit GEMM: BF16 activations x NVFP4 weights.
+ *   C[m][n] = bf16_RNE( s_tW * sum_k X[m][k] * (e2m1 * e4m3)(W)[n][k] )
+ * Each weight byte is read from HBM once.  The kernel family is chosen by m:
+ *   - VALU dot products for the smallest m;
+ *   - BF16 MFMA tiles for larger m.
+ * Source: "Add sm121 (GB10) tier to the 4-bit GEMM dispatch heuristic",
+ * sections "Methodology", "The SIMT / MMA layer" and the tile-selection
+ * follow-up: a fused dequant + GEMM for small M, choosing SIMT vs matrix-core
+ * kernels and the tile width along N by M.
+ *
+ * Arguments:
+ *   x_bf16                device uint16[m][k]
+ *   w, w_scales, w_tscale NVFP4 weights [n][k]
+ *   c_bf16                device uint16[m][n] (written)
+ * Sizes: m, n, k >= 0, k % 32 == 0.
+ *   m == 0 or n == 0: BSGEMM_OK and nothing is launched.
+ */
+int bsgemm_w4a16_run(int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
+                     const uint8_t* w, const uint8_t* w_scales, const float* w_tscale,
+                     uint16_t* c_bf16, void* stream);
+
+/* Static name of a status code ("BSGEMM_OK", ...); "unknown status" otherwise. */
+const char* bsgemm_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none).  Valid until
+ * the next call into the library on this thread. */
+const char* bsgemm_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int bsgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSGEMM_H */

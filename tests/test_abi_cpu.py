@@ -1,0 +1,119 @@
+"""Host-side tests of the C ABI (CPU only, no GPU compute).
+
+The library must load and export every entry point that include/bsgemm.h
+declares.  Argument validation must return the documented status codes
+before anything is launched; pointers in these tests are fake and are never
+dereferenced.  The "no device" case runs only where no GPU is visible."""
+
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+from block_scaled_precision_bsgemm_amd import lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 0x10000          # fake, 16-byte aligned "device" address
+MIS = 0x10004        # fake, misaligned
+
+
+@pytest.fixture(scope="module")
+def so():
+    return L.load()
+
+
+def test_exports_every_declared_symbol(so):
+    header = open(os.path.join(ROOT, "include", "bsgemm.h")).read()
+    declared = set(re.findall(r"\b(bsgemm_\w+)\s*\(", header))
+    assert declared == set(L.SIGNATURES), (declared, set(L.SIGNATURES))
+    for name in declared:
+        assert hasattr(so, name)
+    nm = os.popen(f"nm -D --defined-only {L.LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}\b", nm), name
+
+
+def test_status_strings_and_version(so):
+    assert so.bsgemm_status_string(0) == b"BSGEMM_OK"
+    for code, name in [(1, b"BSGEMM_ERR_INVALID_ARG"), (2, b"BSGEMM_ERR_UNSUPPORTED"),
+                       (3, b"BSGEMM_ERR_BAD_ALIGNMENT"), (4, b"BSGEMM_ERR_DEVICE"),
+                       (5, b"BSGEMM_ERR_RESOURCE"), (6, b"BSGEMM_ERR_LAUNCH")]:
+        assert so.bsgemm_status_string(code) == name
+    assert so.bsgemm_status_string(99) == b"unknown status"
+    assert so.bsgemm_version() == 100
+
+
+def run(so, fmt=L.BSGEMM_NVFP4, m=64, n=64, k=64, a=P, sa=P, ta=P, b=P, sb=P, tb=P, c=P):
+    return so.bsgemm_run(fmt, m, n, k, a, sa, ta, b, sb, tb, c, None)
+
+
+def test_run_validation(so):
+    assert run(so, a=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert b"a is NULL" in so.bsgemm_last_error()
+    assert run(so, c=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert run(so, m=-1) == L.BSGEMM_ERR_INVALID_ARG
+    assert run(so, ta=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert run(so, k=48) == L.BSGEMM_ERR_UNSUPPORTED
+    assert run(so, fmt=7) == L.BSGEMM_ERR_UNSUPPORTED
+    assert run(so, fmt=L.BSGEMM_MXFP8) == L.BSGEMM_ERR_UNSUPPORTED      # tensor scales given
+    assert run(so, a=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert run(so, c=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert run(so, k=1 << 22) == L.BSGEMM_ERR_RESOURCE
+    # an empty operand may be NULL; the error then comes from the next check
+    assert run(so, m=0, a=None, sa=None, c=None, k=48) == L.BSGEMM_ERR_UNSUPPORTED
+
+
+def test_quantize_validation(so):
+    q4, q8 = so.bsgemm_quantize_nvfp4, so.bsgemm_quantize_mxfp8
+    assert q4(4, 64, None, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert q4(4, 64, P, P, P, None, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert q4(4, 40, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert q4(4, 64, MIS, P, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert q8(-1, 64, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert q8(4, 64, P, None, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert q8(4, 16, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert q8(4, 64, P, MIS, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+
+
+def test_grouped_and_w4a16_validation(so):
+    g = so.bsgemm_grouped_run
+    assert g(0, 64, 64, 64, P, P, P, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert g(2, 64, 64, 64, P, P, P, None, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert g(2, 64, 64, 64, P, P, None, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert g(2, 64, 64, 33, P, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert g(2, 64, 64, 64, P, P, P, P, MIS, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    w = so.bsgemm_w4a16_run
+    assert w(1, 64, 64, None, P, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert w(1, 64, 64, P, P, P, None, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert w(1, 64, 80, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert w(1, 64, 64, MIS, P, P, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+
+
+def test_last_error_is_per_thread(so):
+    assert run(so, a=None) == L.BSGEMM_ERR_INVALID_ARG
+    seen = {}
+
+    def other():
+        seen["msg"] = so.bsgemm_last_error()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == b""
+    assert b"a is NULL" in so.bsgemm_last_error()
+
+
+def test_no_device_is_reported_not_launched(so):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible; this case checks the no-device path")
+    assert run(so) == L.BSGEMM_ERR_DEVICE
+    assert so.bsgemm_quantize_mxfp8(4, 64, P, P, P, None) == L.BSGEMM_ERR_DEVICE
+
+
+def test_binding_raises_on_error():
+    import torch
+    x = torch.zeros(4, 40)
+    with pytest.raises(Exception):
+        L.bsgemm_quantize_mxfp8(x)   # CPU tensor: rejected before any call

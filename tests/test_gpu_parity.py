@@ -1,0 +1,339 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Quantizers must be bit-exact.  GEMM outputs must satisfy, element by element,
+|C_gpu - C_ref| <= 2^-8 |C_ref| + 1e-5 sum_k |a_k b_k|, with no NaN.  Every
+output buffer is prefilled with a NaN sentinel, so an element the kernel never
+writes fails.
+
+Inputs come from the seeded generators.  Small and mid-size cases quantize
+them with the oracle and feed the oracle's bytes to the GPU GEMMs.  The
+full-size workloads (16k^3 NVFP4, the 32-group ragged GEMM, the 14336 x 4096
+W4A16 weight) quantize on the GPU; the oracle then independently quantizes a
+sample of rows (with the tensor scale of the whole tensor).  Those rows must
+match bit for bit, and the outputs that depend only on them are compared.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_bsgemm_amd import lib as L
+from block_scaled_precision_bsgemm_amd import synth
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import quantize as Q
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0x7FC0   # BF16 quiet NaN
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def out_bf16(m, n):
+    return torch.full((m, n), SENTINEL, dtype=torch.int16, device="cuda")
+
+
+def assert_ok(res, what):
+    assert res["ok"], f"{what}: {res}"
+
+
+# ----------------------------------------------------------- quantizers --
+
+def _edge_matrix(k=256):
+    """Rows rich in special cases for both quantizers."""
+    r = np.random.Generator(np.random.PCG64(123))
+    rows = []
+    rows.append(np.zeros(k, np.float32))
+    z = np.zeros(k, np.float32); z[1::2] = -0.0; rows.append(z)
+    rows.append((r.integers(-24, 25, k) * np.float32(0.25)).astype(np.float32))      # E2M1 ties
+    rows.append(np.exp2(r.uniform(-30, 30, k)).astype(np.float32) * np.sign(r.standard_normal(k)).astype(np.float32))
+    rows.append((r.standard_normal(k) * 1e-3).astype(np.float32))
+    t = np.zeros(k, np.float32); t[::16] = 1.0; t[1::16] = 0.25; t[2::16] = -0.75; rows.append(t)
+    big = r.standard_normal(k).astype(np.float32); big[5] = 3.0e38; rows.append(big)
+    tiny = np.full(k, 1e-40, np.float32); tiny[::3] = -1e-41; rows.append(tiny)
+    rows.append(r.standard_normal(k).astype(np.float32))
+    # E4M3 midpoints scaled into an MXFP8 block with exponent 0 (block max 448)
+    mids = ((F.E4M3_TABLE[:0x7E] + F.E4M3_TABLE[1:0x7F]) / 2).astype(np.float32)
+    mrow = np.resize(mids, k).astype(np.float32); mrow[::32] = 448.0; rows.append(mrow)
+    return np.stack(rows).astype(np.float32)
+
+
+def _check_nvfp4_quant(x, what, rows=None):
+    say("quantize_nvfp4", what, x.shape)
+    c, s, ts = L.bsgemm_quantize_nvfp4(dev(x))
+    torch.cuda.synchronize()
+    st = Q.nvfp4_tensor_scale(x)
+    assert ts.cpu().numpy()[0].tobytes() == np.float32(st).tobytes(), (what, ts.item(), st)
+    xs = x if rows is None else x[rows]
+    oc, os_, _ = Q.quantize_nvfp4(xs, tensor_scale=st)
+    gc, gs = c.cpu().numpy(), s.cpu().numpy()
+    if rows is not None:
+        gc, gs = gc[rows], gs[rows]
+    assert np.array_equal(gs, os_), f"{what}: scale bytes differ at {np.argwhere(gs != os_)[:5]}"
+    assert np.array_equal(gc, oc), f"{what}: code bytes differ at {np.argwhere(gc != oc)[:5]}"
+    return c, s, ts
+
+
+def _check_mxfp8_quant(x, what):
+    say("quantize_mxfp8", what, x.shape)
+    c, s = L.bsgemm_quantize_mxfp8(dev(x))
+    oc, os_ = Q.quantize_mxfp8(x)
+    gc, gs = c.cpu().numpy(), s.cpu().numpy()
+    assert np.array_equal(gs, os_), f"{what}: scale bytes differ at {np.argwhere(gs != os_)[:5]}"
+    assert np.array_equal(gc, oc), f"{what}: code bytes differ at {np.argwhere(gc != oc)[:5]}"
+    return c, s
+
+
+def test_quantize_nvfp4_small_config(gpu_lib):
+    a, b = synth.nvfp4_small_inputs()
+    _check_nvfp4_quant(a, "256x128 A")
+    _check_nvfp4_quant(b, "256x128 B")
+
+
+def test_quantize_nvfp4_edges(gpu_lib):
+    x = _edge_matrix()
+    _check_nvfp4_quant(x, "edge rows")
+    _check_nvfp4_quant(x[[0, 1]], "all-zero tensor")
+    _check_nvfp4_quant(x[:, :32], "k = 32")
+    _check_nvfp4_quant(x[[7]], "one row of FP32 subnormals")
+    _check_nvfp4_quant(_edge_matrix(96), "k = 96")
+    # chosen tensor scale 1.0 (amax 2688) exercises subnormal and saturated block scales
+    y = (np.exp2(np.random.Generator(np.random.PCG64(9)).uniform(-14, 9, (64, 256)))).astype(np.float32)
+    y[0, 0] = 2688.0
+    _check_nvfp4_quant(y, "wide block-scale range")
+
+
+def test_quantize_mxfp8_4k_config(gpu_lib):
+    a, b = synth.mxfp8_inputs()
+    _check_mxfp8_quant(a, "4096^2 A")
+    _check_mxfp8_quant(b, "4096^2 B")
+
+
+def test_quantize_mxfp8_edges(gpu_lib):
+    x = _edge_matrix()
+    _check_mxfp8_quant(x, "edge rows")
+    _check_mxfp8_quant(x[:, :32], "k = 32")
+    _check_mxfp8_quant(_edge_matrix(96), "k = 96")
+
+
+def test_quantize_empty(gpu_lib):
+    say("quantize empty")
+    x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
+    c, s, ts = L.bsgemm_quantize_nvfp4(x)
+    torch.cuda.synchronize()
+    assert ts.item() == 0.0
+    c8, s8 = L.bsgemm_quantize_mxfp8(x)
+    assert c8.numel() == 0
+
+
+# ---------------------------------------------------------------- GEMMs --
+
+def _quant(fmt, x):
+    return Q.quantize_nvfp4(x) if fmt == L.BSGEMM_NVFP4 else Q.quantize_mxfp8(x)
+
+
+def _ref(fmt, qa, qb):
+    return G.gemm_nvfp4(*qa, *qb) if fmt == L.BSGEMM_NVFP4 else G.gemm_mxfp8(*qa, *qb)
+
+
+def _gpu_gemm(fmt, qa, qb, k):
+    m, n = qa[0].shape[0], qb[0].shape[0]
+    c = out_bf16(m, n)
+    if fmt == L.BSGEMM_NVFP4:
+        ta, tb = dev(np.array([qa[2]], np.float32)), dev(np.array([qb[2]], np.float32))
+        L.bsgemm_run(fmt, dev(qa[0]), dev(qa[1]), ta, dev(qb[0]), dev(qb[1]), tb, k, c=c)
+    else:
+        L.bsgemm_run(fmt, dev(qa[0]), dev(qa[1]), None, dev(qb[0]), dev(qb[1]), None, k, c=c)
+    return u16(c)
+
+
+FMTS = {"nvfp4": L.BSGEMM_NVFP4, "mxfp8": L.BSGEMM_MXFP8}
+
+
+def test_gemm_nvfp4_small_config(gpu_lib):
+    a, b = synth.nvfp4_small_inputs()
+    qa, qb = Q.quantize_nvfp4(a), Q.quantize_nvfp4(b)
+    say("gemm nvfp4 256x256x128")
+    c = _gpu_gemm(L.BSGEMM_NVFP4, qa, qb, 128)
+    assert_ok(G.check(c, *G.gemm_nvfp4(*qa, *qb)), "nvfp4 256x256x128")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("m,n,k", [
+    (1, 1, 32), (7, 17, 64), (17, 255, 96), (256, 256, 128), (257, 300, 160),
+    (300, 257, 512), (64, 520, 1024), (513, 129, 288), (1, 700, 2048),
+])
+def test_gemm_shapes(gpu_lib, fmt, m, n, k):
+    f = FMTS[fmt]
+    r = np.random.Generator(np.random.PCG64(m * 7919 + n * 31 + k))
+    xa = r.standard_normal((m, k)).astype(np.float32)
+    xb = r.standard_normal((n, k)).astype(np.float32)
+    xa[:: max(1, m // 3)] *= np.float32(50.0)          # mixed block scales
+    qa, qb = _quant(f, xa), _quant(f, xb)
+    say("gemm", fmt, m, n, k)
+    c = _gpu_gemm(f, qa, qb, k)
+    assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+def test_gemm_zero_rows_and_k0(gpu_lib, fmt):
+    f = FMTS[fmt]
+    xa = synth.normal_f32((40, 128), 5)
+    xa[3] = 0.0                                          # an all-zero row
+    xb = synth.normal_f32((50, 128), 6)
+    qa, qb = _quant(f, xa), _quant(f, xb)
+    say("gemm zero row", fmt)
+    c = _gpu_gemm(f, qa, qb, 128)
+    assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} zero row")
+    assert np.all(F.decode_bf16(c[3]) == 0)
+    say("gemm k = 0", fmt)
+    e = np.zeros((40, 0), np.uint8)
+    qa0 = (e, e, np.float32(1)) if f == L.BSGEMM_NVFP4 else (e, e)
+    qb0 = (np.zeros((50, 0), np.uint8), np.zeros((50, 0), np.uint8), np.float32(1)) if f == L.BSGEMM_NVFP4 \
+        else (np.zeros((50, 0), np.uint8), np.zeros((50, 0), np.uint8))
+    c0 = _gpu_gemm(f, qa0, qb0, 0)
+    assert np.all(c0 == 0)
+
+
+def test_gemm_mxfp8_4k_config(gpu_lib):
+    a, b = synth.mxfp8_inputs()
+    qa, qb = Q.quantize_mxfp8(a), Q.quantize_mxfp8(b)
+    say("gemm mxfp8 4096^3")
+    c = _gpu_gemm(L.BSGEMM_MXFP8, qa, qb, 4096)
+    rows = np.random.Generator(np.random.PCG64(1)).choice(4096, 512, replace=False)
+    rows = np.sort(np.concatenate([rows, [0, 4095]]))
+    assert_ok(G.check(c[rows], *G.gemm_mxfp8(*qa, *qb, rows=rows)), "mxfp8 4096^3 (514 rows, all columns)")
+
+
+def test_gemm_deterministic(gpu_lib):
+    a, b = synth.nvfp4_small_inputs()
+    for f in (L.BSGEMM_NVFP4, L.BSGEMM_MXFP8):
+        qa, qb = _quant(f, np.tile(a, (3, 4))), _quant(f, np.tile(b, (2, 4)))
+        say("determinism", f)
+        c1 = _gpu_gemm(f, qa, qb, 512)
+        c2 = _gpu_gemm(f, qa, qb, 512)
+        assert np.array_equal(c1, c2)
+
+
+def _sample(n, count, seed, must=()):
+    idx = np.random.Generator(np.random.PCG64(seed)).choice(n, min(count, n), replace=False)
+    return np.unique(np.concatenate([idx, np.asarray(must, dtype=np.int64), [0, n - 1]]))
+
+
+def test_nvfp4_16k_config_sampled(gpu_lib):
+    """16384^3 NVFP4 with 1% outlier rows: GPU quantize + GEMM, checked on
+    (163 outlier + 256 random rows) x (163 outlier + 256 random columns)."""
+    a, b, ia, ib = synth.nvfp4_16k_inputs()
+    rows = _sample(16384, 256, 11, ia)
+    cols = _sample(16384, 256, 12, ib)
+    ca, sa, ta = _check_nvfp4_quant(a, "16k A (sampled rows)", rows)
+    cb, sb, tb = _check_nvfp4_quant(b, "16k B (sampled rows)", cols)
+    del a, b
+    say("gemm nvfp4 16384^3")
+    c = out_bf16(16384, 16384)
+    L.bsgemm_run(L.BSGEMM_NVFP4, ca, sa, ta, cb, sb, tb, 16384, c=c)
+    sub = c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    got = u16(sub)
+    qa = (ca.cpu().numpy()[rows], sa.cpu().numpy()[rows], np.float32(ta.item()))
+    qb = (cb.cpu().numpy()[cols], sb.cpu().numpy()[cols], np.float32(tb.item()))
+    assert_ok(G.check(got, *G.gemm_nvfp4(*qa, *qb)), "nvfp4 16384^3 sampled")
+    # nothing unwritten anywhere: the sentinel is a NaN
+    assert not torch.isnan(c.view(torch.bfloat16)).any().item()
+
+
+# -------------------------------------------------------------- grouped --
+
+def _grouped_case(counts, n, k, seed):
+    off = synth.offsets_from_counts(np.asarray(counts))
+    m = int(off[-1])
+    x = synth.normal_f32((m, k), seed)
+    qa = Q.quantize_nvfp4(x) if m else (np.zeros((0, k // 2), np.uint8), np.zeros((0, k // 16), np.uint8), np.float32(0))
+    w = synth.bf16_bits(synth.normal_f32((len(counts), n, k), seed + 1, std=0.02))
+    return qa, off, w
+
+
+def _gpu_grouped(qa, off, w, k):
+    m, n = qa[0].shape[0], w.shape[1]
+    c = out_bf16(m, n)
+    L.bsgemm_grouped_run(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)), dev(off),
+                         dev(w), k, c=c)
+    return u16(c)
+
+
+@pytest.mark.parametrize("counts,n,k", [
+    ([5], 64, 64),
+    ([0, 3, 0, 0, 300, 1, 0], 96, 128),
+    ([257, 0, 256, 255], 260, 96),
+    ([1] * 40, 33, 32),
+    ([600, 0, 0, 900], 512, 256),
+])
+def test_grouped_shapes(gpu_lib, counts, n, k):
+    qa, off, w = _grouped_case(counts, n, k, sum(counts) + n + k)
+    say("grouped", counts, n, k)
+    c = _gpu_grouped(qa, off, w, k)
+    assert_ok(G.check(c, *G.grouped_nvfp4_bf16(*qa, off, w)), f"grouped {counts} n={n} k={k}")
+
+
+def test_grouped_config_sampled(gpu_lib):
+    """32 groups, Dirichlet(0.5) counts over 16384 rows, K=7168, N=2048.
+    GPU quantize + grouped GEMM; sampled rows: first/last row of every
+    non-empty group plus 384 random rows, all 2048 columns."""
+    x, off, w = synth.grouped_inputs()
+    counts = np.diff(off.astype(np.int64))
+    must = [r for g in range(32) if counts[g] for r in (off[g], off[g + 1] - 1)]
+    rows = _sample(16384, 384, 21, must)
+    ca, sa, ta = _check_nvfp4_quant(x, "grouped A (sampled rows)", rows)
+    del x
+    say("grouped 32 x (2048 x 7168), m=16384")
+    c = out_bf16(16384, 2048)
+    L.bsgemm_grouped_run(ca, sa, ta, dev(off), dev(w), 7168, c=c)
+    got = u16(c)
+    qa = (ca.cpu().numpy(), sa.cpu().numpy(), np.float32(ta.item()))
+    assert_ok(G.check(got[rows], *G.grouped_nvfp4_bf16(*qa, off, w, rows=rows)), "grouped config sampled")
+    assert not np.any(got == SENTINEL)
+
+
+# ---------------------------------------------------------------- W4A16 --
+
+def _gpu_w4a16(x, qw, m):
+    c = out_bf16(m, qw[0].shape[0])
+    L.bsgemm_w4a16_run(dev(x), dev(qw[0]), dev(qw[1]), dev(np.array([qw[2]], np.float32)), c=c)
+    return u16(c)
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (1, 1, 32), (1, 33, 96), (1, 100, 4096), (1, 64, 8192 + 32), (2, 50, 64), (3, 16, 128),
+    (16, 130, 256), (17, 64, 512), (64, 96, 4096), (65, 40, 160), (100, 33, 96), (256, 64, 1024),
+])
+def test_w4a16_shapes(gpu_lib, m, n, k):
+    x = synth.bf16_bits(synth.normal_f32((m, k), m + n + k))
+    qw = Q.quantize_nvfp4(synth.normal_f32((n, k), m * n + k, std=0.02))
+    say("w4a16", m, n, k)
+    c = _gpu_w4a16(x, qw, m)
+    assert_ok(G.check(c, *G.w4a16(x, *qw)), f"w4a16 {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m", [1, 16, 64, 256])
+def test_w4a16_config_sampled(gpu_lib, m):
+    """W 14336 x 4096 quantized on the GPU; all m rows x 1024 sampled columns."""
+    x, wf = synth.w4a16_inputs(m)
+    cols = _sample(14336, 1024, 31 + m)
+    cw, sw, tw = _check_nvfp4_quant(wf, f"w4a16 W (sampled rows), m={m}", cols)
+    say("w4a16 config m =", m)
+    c = out_bf16(m, 14336)
+    L.bsgemm_w4a16_run(dev(x), cw, sw, tw, c=c)
+    got = u16(c)
+    qw = (cw.cpu().numpy()[cols], sw.cpu().numpy()[cols], np.float32(tw.item()))
+    assert_ok(G.check(got[:, cols], *G.w4a16(x, *qw)), f"w4a16 m={m} sampled")
+    assert not np.any(got == SENTINEL)
