@@ -166,6 +166,22 @@ __device__ __forceinline__ uint32_t buffer_load_u8(rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t buffer_load_u16(rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+__device__ __forceinline__ uint2 buffer_load_x2(rsrc_t r, int off) {
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  const u2 v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// An offset past every resource this library builds (all are < 2^31 bytes):
+// a buffer load there returns zero without touching memory.  Selecting it
+// instead of branching keeps loads unconditional, so the compiler never has
+// to wait for them inside the issuing block.
+constexpr int OOB = 0x7FFFFFF0;
+
 // -------------------------------------------------------------------- misc
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

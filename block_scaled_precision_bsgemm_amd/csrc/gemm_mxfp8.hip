@@ -40,7 +40,10 @@ struct Smem {
   uint32_t bs[2][BN];
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): any 16
+// consecutive rows reading one chunk then cover all 16 bank groups of
+// 16 bytes (two 128-byte rows per 256 bytes of banks).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // Map a linear tile index to (tile_m, tile_n): groups of GROUP_M tile rows
 // are walked column by column, so consecutive tiles share B columns and the
@@ -55,6 +58,7 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& tm,
   tn = in / gsize;
 }
 
+template <bool SCALE_DW>
 __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
@@ -71,7 +75,6 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
   //      (tid >> 3) + 32 i, i = 0..7, and the scale dword of row tid.
   const int lc = tid & 7, lr = tid >> 3;
   uint4 ra[8], rb[8];
-  uint32_t rsa, rsb;
   // Per-tile buffer resources: loads past the tile's last valid row return 0.
   const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
   const auto ra_rsrc = make_rsrc(A + (int64_t)m0 * K, rows_a * K);
@@ -80,27 +83,29 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
   const auto sb_rsrc = make_rsrc(Bs + (int64_t)n0 * KB, rows_b * KB);
   const int off0 = lr * K + lc * 16;
 
+  // Loads only issue here; the scale bytes are assembled in sstore, after the
+  // MFMAs of the current step, so nothing waits on them early.
+  uint32_t sa_raw[4], sb_raw[4];
   auto gload = [&](int kt) {
     const int kc = kt * BK + lc * 16;
-    const bool kin = kc < K;   // K % 32 == 0: a 16-byte chunk is wholly in or out
+    const int kofs = kc < K ? kt * BK : OOB;   // K % 32 == 0: chunks are wholly in or out
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int off = off0 + 32 * i * K + kt * BK;
-      ra[i] = kin ? buffer_load_x4(ra_rsrc, off) : make_uint4(0, 0, 0, 0);
-      rb[i] = kin ? buffer_load_x4(rb_rsrc, off) : make_uint4(0, 0, 0, 0);
+      const int off = kofs == OOB ? OOB : off0 + 32 * i * K + kofs;
+      ra[i] = buffer_load_x4(ra_rsrc, off);
+      rb[i] = buffer_load_x4(rb_rsrc, off);
     }
-    uint32_t sa = 0, sb = 0;
+    if (SCALE_DW) {            // K % 128 == 0: the step's 4 scale bytes are one dword
+      sa_raw[0] = buffer_load_u32(sa_rsrc, tid * KB + kt * 4);
+      sb_raw[0] = buffer_load_u32(sb_rsrc, tid * KB + kt * 4);
+    } else {                   // blocks past K read as 0 (their codes are 0 too)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kb = kt * 4 + j;
-      // Blocks past K hold zero codes; give them the unit scale 2^0.
-      const uint32_t ba = kb < KB ? buffer_load_u8(sa_rsrc, tid * KB + kb) : 127u;
-      const uint32_t bb = kb < KB ? buffer_load_u8(sb_rsrc, tid * KB + kb) : 127u;
-      sa |= ba << (8 * j);
-      sb |= bb << (8 * j);
+      for (int j = 0; j < 4; ++j) {
+        const int kb = kt * 4 + j;
+        sa_raw[j] = buffer_load_u8(sa_rsrc, kb < KB ? tid * KB + kb : OOB);
+        sb_raw[j] = buffer_load_u8(sb_rsrc, kb < KB ? tid * KB + kb : OOB);
+      }
     }
-    rsa = sa;
-    rsb = sb;
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -109,8 +114,13 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
       *reinterpret_cast<uint4*>(&sm.a[buf][swz(row, lc)]) = ra[i];
       *reinterpret_cast<uint4*>(&sm.b[buf][swz(row, lc)]) = rb[i];
     }
-    sm.as[buf][tid] = rsa;
-    sm.bs[buf][tid] = rsb;
+    if (SCALE_DW) {
+      sm.as[buf][tid] = sa_raw[0];
+      sm.bs[buf][tid] = sb_raw[0];
+    } else {
+      sm.as[buf][tid] = sa_raw[0] | (sa_raw[1] << 8) | (sa_raw[2] << 16) | (sa_raw[3] << 24);
+      sm.bs[buf][tid] = sb_raw[0] | (sb_raw[1] << 8) | (sb_raw[2] << 16) | (sb_raw[3] << 24);
+    }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -182,8 +192,12 @@ hipError_t launch_gemm_mxfp8(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
-  hipLaunchKernelGGL(mxfp8_gemm_kernel, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a, as, b,
-                     bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  if (k % 128 == 0)
+    hipLaunchKernelGGL(mxfp8_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL(mxfp8_gemm_kernel<false>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

@@ -59,30 +59,6 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& tm,
   tn = in / gsize;
 }
 
-// Eight scale bytes of one row for one K step: blocks [8 kt, 8 kt + 8) of a row
-// with `kb` blocks.  Blocks past the row's end read as 0.
-__device__ __forceinline__ uint2 load_scale8(rsrc_t r, int row_off, int kt, int kb, bool al4) {
-  uint2 v;
-  const int off = row_off + kt * 8;
-  if (al4) {
-    v.x = buffer_load_u32(r, off);
-    v.y = buffer_load_u32(r, off + 4);
-  } else {
-    v.x = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0) |
-          ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + 2, 0, 0) << 16);
-    v.y = __builtin_amdgcn_raw_buffer_load_b16(r, off + 4, 0, 0) |
-          ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + 6, 0, 0) << 16);
-  }
-  const int valid = kb - kt * 8;   // blocks of this step inside the row
-  if (valid < 8) {
-    const uint64_t keep = valid <= 0 ? 0ull : (~0ull >> (64 - 8 * valid));
-    const uint64_t w = (((uint64_t)v.y << 32) | v.x) & keep;
-    v.x = (uint32_t)w;
-    v.y = (uint32_t)(w >> 32);
-  }
-  return v;
-}
-
 struct Scale2 {
   float s;        // E4M3 scale as FP32 (its exponent drives the conversion)
   uint32_t m2;    // (1 + f) as an FP16 pair
@@ -95,6 +71,7 @@ __device__ __forceinline__ Scale2 decode_scale(uint32_t byte) {
   return d;
 }
 
+template <bool SCALE_QW>
 __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
@@ -107,7 +84,6 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
   const int KT = (K + BK - 1) / BK;
   const int KH = K / 2;          // code bytes per row
   const int KB = K / 16;         // scale bytes per row
-  const bool al4 = (KB & 3) == 0;
 
   const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
   const auto ca_rsrc = make_rsrc(A + (int64_t)m0 * KH, rows_a * KH);
@@ -119,18 +95,30 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
   // scale bytes of row tid
   const int lc = tid & 3, lr = tid >> 2;
   uint4 ra[4], rb[4];
-  uint2 rsa, rsb;
+  uint32_t sa_raw[4], sb_raw[4];
   const int off0 = lr * KH + lc * 16;
+  // Loads only issue here (no branches, no uses); scale words are assembled
+  // in sstore, after the MFMAs of the current step.
   auto gload = [&](int kt) {
-    const bool kin = kt * ROWB + lc * 16 < KH;
+    const int kofs = kt * ROWB + lc * 16 < KH ? kt * ROWB : OOB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int off = off0 + 64 * i * KH + kt * ROWB;
-      ra[i] = kin ? buffer_load_x4(ca_rsrc, off) : make_uint4(0, 0, 0, 0);
-      rb[i] = kin ? buffer_load_x4(cb_rsrc, off) : make_uint4(0, 0, 0, 0);
+      const int off = kofs == OOB ? OOB : off0 + 64 * i * KH + kofs;
+      ra[i] = buffer_load_x4(ca_rsrc, off);
+      rb[i] = buffer_load_x4(cb_rsrc, off);
     }
-    rsa = load_scale8(sa_rsrc, tid * KB, kt, KB, al4);
-    rsb = load_scale8(sb_rsrc, tid * KB, kt, KB, al4);
+    if (SCALE_QW) {            // K % 128 == 0: the step's 8 scale bytes are one qword
+      const uint2 va = buffer_load_x2(sa_rsrc, tid * KB + kt * 8);
+      const uint2 vb = buffer_load_x2(sb_rsrc, tid * KB + kt * 8);
+      sa_raw[0] = va.x; sa_raw[1] = va.y; sb_raw[0] = vb.x; sb_raw[1] = vb.y;
+    } else {                   // pairs of blocks; pairs past K read as 0
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kb = kt * 8 + 2 * j;
+        sa_raw[j] = buffer_load_u16(sa_rsrc, kb < KB ? tid * KB + kb : OOB);
+        sb_raw[j] = buffer_load_u16(sb_rsrc, kb < KB ? tid * KB + kb : OOB);
+      }
+    }
   };
   auto sstore = [&](int buf) {
 #pragma unroll
@@ -139,8 +127,13 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
       *reinterpret_cast<uint4*>(&sm.a[buf][swz(row, lc)]) = ra[i];
       *reinterpret_cast<uint4*>(&sm.b[buf][swz(row, lc)]) = rb[i];
     }
-    sm.as[buf][tid] = rsa;
-    sm.bs[buf][tid] = rsb;
+    if (SCALE_QW) {
+      sm.as[buf][tid] = make_uint2(sa_raw[0], sa_raw[1]);
+      sm.bs[buf][tid] = make_uint2(sb_raw[0], sb_raw[1]);
+    } else {
+      sm.as[buf][tid] = make_uint2(sa_raw[0] | (sa_raw[1] << 16), sa_raw[2] | (sa_raw[3] << 16));
+      sm.bs[buf][tid] = make_uint2(sb_raw[0] | (sb_raw[1] << 16), sb_raw[2] | (sb_raw[3] << 16));
+    }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -227,8 +220,12 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* bs, const float* bts, uint16_t* c,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
-  hipLaunchKernelGGL(nvfp4_gemm_kernel, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a, as, ats,
-                     b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  if (k % 128 == 0)
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

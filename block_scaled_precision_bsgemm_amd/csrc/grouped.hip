@@ -18,7 +18,7 @@
 //
 // Tile: 256 rows x 256 columns, 4 waves of 128 x 128, K step 64 elements:
 //   - A codes [256][32] bytes, A scales [256] dwords (4 E4M3 bytes);
-//   - W [256][64] BF16, 16-byte chunks swizzled by (row & 7).
+//   - W [256][64] BF16, 16-byte chunks swizzled by ((row >> 1) & 7).
 // K assignment (A and W agree): lane (r = l % 32, g = l / 32) takes K
 // elements [32g, 32g + 32) of the step.  Dword sp of that range feeds MFMA
 // sub-step sp at positions 8g..8g+7; its scale block is 2g + sp/2, and its W
@@ -41,7 +41,9 @@ struct Smem {
   int tile_info[4];
 };
 
-__device__ __forceinline__ int wswz(int row, int chunk) { return row * WROWB + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of W row r sits at c ^ ((r >> 1) & 7): 16 consecutive rows
+// reading one chunk cover all 16 bank groups.
+__device__ __forceinline__ int wswz(int row, int chunk) { return row * WROWB + ((chunk ^ ((row >> 1) & 7)) << 4); }
 
 // Find the group holding global m-tile `mt` (tiles of BM rows counted group by
 // group).  Run by wave 0.  Writes {group, first row, end row} to `info`, or
@@ -74,6 +76,7 @@ __device__ void find_tile(const int32_t* __restrict__ off, int G, int mt, int la
   if (lane == 0) info[0] = -1;
 }
 
+template <bool SCALE_DW>
 __global__ __launch_bounds__(NT, 1) void grouped_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
     const int32_t* __restrict__ off, const uint16_t* __restrict__ W, uint16_t* __restrict__ C,
@@ -92,7 +95,6 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
   const int n0 = nt * BN;
   const int KT = (K + BK - 1) / BK;
   const int KH = K / 2, KB = K / 16;
-  const bool al4 = (KB & 3) == 0;
 
   const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
   const auto ca_rsrc = make_rsrc(A + (int64_t)r0 * KH, rows_a * KH);
@@ -104,35 +106,29 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
   const int alc = tid & 1, alr = tid >> 1;
   const int wlc = tid & 7, wlr = tid >> 3;
   uint4 ra[2], rw[8];
-  uint32_t rsa;
+  uint32_t sa_raw[2];
+  // Loads only issue here (no branches, no uses); see sstore.
   auto gload = [&](int kt) {
-    const bool akin = kt * AROWB + alc * 16 < KH;
+    const int aofs = kt * AROWB + alc * 16 < KH ? kt * AROWB + alc * 16 : OOB;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      ra[i] = akin ? buffer_load_x4(ca_rsrc, (alr + 128 * i) * KH + kt * AROWB + alc * 16)
-                   : make_uint4(0, 0, 0, 0);
-    const int soff = tid * KB + kt * 4;
-    uint32_t s;
-    if (al4) {
-      s = buffer_load_u32(sa_rsrc, soff);
-    } else {
-      s = __builtin_amdgcn_raw_buffer_load_b16(sa_rsrc, soff, 0, 0) |
-          ((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(sa_rsrc, soff + 2, 0, 0) << 16);
+      ra[i] = buffer_load_x4(ca_rsrc, aofs == OOB ? OOB : (alr + 128 * i) * KH + aofs);
+    if (SCALE_DW) {            // K % 64 == 0: the step's 4 scale bytes are one dword
+      sa_raw[0] = buffer_load_u32(sa_rsrc, tid * KB + kt * 4);
+    } else {                   // two pairs of blocks; a pair past K reads as 0
+      sa_raw[0] = buffer_load_u16(sa_rsrc, tid * KB + kt * 4);
+      sa_raw[1] = buffer_load_u16(sa_rsrc, kt * 4 + 2 < KB ? tid * KB + kt * 4 + 2 : OOB);
     }
-    const int valid = KB - kt * 4;
-    if (valid < 4) s &= valid <= 0 ? 0u : (0xFFFFFFFFu >> (32 - 8 * valid));
-    rsa = s;
-    const bool wkin = kt * BK + wlc * 8 < K;
+    const int wofs = kt * BK + wlc * 8 < K ? (kt * BK + wlc * 8) * 2 : OOB;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      rw[i] = wkin ? buffer_load_x4(w_rsrc, ((wlr + 32 * i) * K + kt * BK + wlc * 8) * 2)
-                   : make_uint4(0, 0, 0, 0);
+      rw[i] = buffer_load_x4(w_rsrc, wofs == OOB ? OOB : (wlr + 32 * i) * K * 2 + wofs);
   };
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       *reinterpret_cast<uint4*>(&sm.a[buf][(alr + 128 * i) * AROWB + alc * 16]) = ra[i];
-    sm.as[buf][tid] = rsa;
+    sm.as[buf][tid] = SCALE_DW ? sa_raw[0] : (sa_raw[0] | (sa_raw[1] << 16));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       *reinterpret_cast<uint4*>(&sm.w[buf][wswz(wlr + 32 * i, wlc)]) = rw[i];
@@ -214,8 +210,14 @@ hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
                           hipStream_t stream) {
   const int tiles_n = (int)ceil_div(n, BN);
   const int64_t mtiles_max = m_total / BM + num_groups;   // >= sum_g ceil(c_g / BM)
-  hipLaunchKernelGGL(grouped_kernel, dim3((unsigned)(mtiles_max * tiles_n)), dim3(NT), 0, stream,
-                     a, as, ats, offsets, w, c, num_groups, (int)m_total, (int)n, (int)k, tiles_n);
+  if (k % 64 == 0)
+    hipLaunchKernelGGL(grouped_kernel<true>, dim3((unsigned)(mtiles_max * tiles_n)), dim3(NT), 0,
+                       stream, a, as, ats, offsets, w, c, num_groups, (int)m_total, (int)n, (int)k,
+                       tiles_n);
+  else
+    hipLaunchKernelGGL(grouped_kernel<false>, dim3((unsigned)(mtiles_max * tiles_n)), dim3(NT), 0,
+                       stream, a, as, ats, offsets, w, c, num_groups, (int)m_total, (int)n, (int)k,
+                       tiles_n);
   return hipGetLastError();
 }
 

@@ -138,22 +138,21 @@ __global__ __launch_bounds__(MM_THREADS, 1) void mfma_kernel(
 
   for (int st = s_begin; st < s_end; ++st) {
     const int kq = st * 128 + 32 * q;          // first K element of this lane
-    const bool kin = kq < K;
+    const bool kin = kq < K;                   // K % 32 == 0: 32 elements wholly in or out
     uint4 wc[NI];
     uint32_t ws[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int row = 16 * i + r;
-      wc[i] = kin ? buffer_load_x4(c_rsrc, row * KH + kq / 2) : make_uint4(0, 0, 0, 0);
-      ws[i] = kin ? __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, row * KB + kq / 16, 0, 0) : 0u;
+      wc[i] = buffer_load_x4(c_rsrc, kin ? row * KH + kq / 2 : OOB);
+      ws[i] = buffer_load_u16(s_rsrc, kin ? row * KB + kq / 16 : OOB);
     }
     uint4 xv[NJ][4];
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp)
-        xv[j][sp] = kin ? buffer_load_x4(x_rsrc, ((16 * j + r) * K + kq + 8 * sp) * 2)
-                        : make_uint4(0, 0, 0, 0);
+        xv[j][sp] = buffer_load_x4(x_rsrc, kin ? ((16 * j + r) * K + kq + 8 * sp) * 2 : OOB);
     float s[NI][2], mant[NI][2];
 #pragma unroll
     for (int i = 0; i < NI; ++i)
