@@ -11,8 +11,8 @@
 //   - Output tile 256 x 256; each wave owns 128 x 128 (4 x 4 MFMA tiles of
 //     32 x 32).
 //   - K step 128 bytes, double-buffered in LDS:
-//       A and B codes [256][128] bytes each, with 16-byte chunks XOR-swizzled
-//       by (row & 7), so 8 lanes reading 8 rows hit disjoint banks;
+//       A and B codes [256][128] bytes each, 16-byte chunks XOR-swizzled
+//       by ((row >> 1) & 7), conflict-free for the MFMA operand reads;
 //       A and B scales [256] dwords (4 E8M0 bytes of the step).
 //   - Operand register layout of the 32x32x64 FP8 MFMA, checked on the device
 //     against the oracle: lane (r = l % 32, g = l / 32) holds row r;
@@ -33,9 +33,12 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
 constexpr int GROUP_M = 8;   // tile rows per rasterisation group
 
+// Tiles are uint4 arrays: the compiler then knows every access is 16-byte
+// aligned and emits single ds_read_b128 / ds_write_b128 instructions.
+constexpr int RC = BK / 16;   // 16-byte chunks per row
 struct Smem {
-  uint8_t a[2][BM * BK];
-  uint8_t b[2][BN * BK];
+  uint4 a[2][BM * RC];
+  uint4 b[2][BN * RC];
   uint32_t as[2][BM];
   uint32_t bs[2][BN];
 };
@@ -43,7 +46,7 @@ struct Smem {
 // 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): any 16
 // consecutive rows reading one chunk then cover all 16 bank groups of
 // 16 bytes (two 128-byte rows per 256 bytes of banks).
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * RC + (chunk ^ ((row >> 1) & 7)); }
 
 // Map a linear tile index to (tile_m, tile_n): groups of GROUP_M tile rows
 // are walked column by column, so consecutive tiles share B columns and the
@@ -111,8 +114,8 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = lr + 32 * i;
-      *reinterpret_cast<uint4*>(&sm.a[buf][swz(row, lc)]) = ra[i];
-      *reinterpret_cast<uint4*>(&sm.b[buf][swz(row, lc)]) = rb[i];
+      sm.a[buf][swz(row, lc)] = ra[i];
+      sm.b[buf][swz(row, lc)] = rb[i];
     }
     if (SCALE_DW) {
       sm.as[buf][tid] = sa_raw[0];
@@ -146,8 +149,8 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + i * 32 + r;
-        const uint4 lo = *reinterpret_cast<const uint4*>(&sm.a[buf][swz(row, 4 * s + g)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&sm.a[buf][swz(row, 4 * s + 2 + g)]);
+        const uint4 lo = sm.a[buf][swz(row, 4 * s + g)];
+        const uint4 hi = sm.a[buf][swz(row, 4 * s + 2 + g)];
         af[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         sa[i] = (int)((sm.as[buf][row] >> (8 * (2 * s + g))) & 0xFFu);
@@ -155,8 +158,8 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = wn * 128 + j * 32 + r;
-        const uint4 lo = *reinterpret_cast<const uint4*>(&sm.b[buf][swz(row, 4 * s + g)]);
-        const uint4 hi = *reinterpret_cast<const uint4*>(&sm.b[buf][swz(row, 4 * s + 2 + g)]);
+        const uint4 lo = sm.b[buf][swz(row, 4 * s + g)];
+        const uint4 hi = sm.b[buf][swz(row, 4 * s + 2 + g)];
         bf[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                     (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         sb[j] = (int)((sm.bs[buf][row] >> (8 * (2 * s + g))) & 0xFFu);

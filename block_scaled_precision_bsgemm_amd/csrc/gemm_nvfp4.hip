@@ -38,16 +38,17 @@ constexpr int BM = 256, BN = 256, BK = 128, NT = 256;
 constexpr int ROWB = BK / 2;   // code bytes per row per step
 constexpr int GROUP_M = 8;
 
+// Tiles are uint4 arrays: the compiler then knows every access is 16-byte
+// aligned and emits single ds_read_b128 / ds_write_b128 instructions.
+constexpr int RC = ROWB / 16;   // 16-byte chunks per row
 struct Smem {
-  uint8_t a[2][BM * ROWB];
-  uint8_t b[2][BN * ROWB];
+  uint4 a[2][BM * RC];
+  uint4 b[2][BN * RC];
   uint2 as[2][BM];
   uint2 bs[2][BN];
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * ROWB + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
+__device__ __forceinline__ int swz(int row, int chunk) { return row * RC + (chunk ^ ((row >> 2) & 3)); }
 
 __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = GROUP_M * tiles_n;
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = lr + 64 * i;
-      *reinterpret_cast<uint4*>(&sm.a[buf][swz(row, lc)]) = ra[i];
-      *reinterpret_cast<uint4*>(&sm.b[buf][swz(row, lc)]) = rb[i];
+      sm.a[buf][swz(row, lc)] = ra[i];
+      sm.b[buf][swz(row, lc)] = rb[i];
     }
     if (SCALE_QW) {
       sm.as[buf][tid] = make_uint2(sa_raw[0], sa_raw[1]);
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + i * 32 + r;
-        ca[i] = *reinterpret_cast<const uint4*>(&sm.a[buf][swz(row, 2 * h + g)]);
+        ca[i] = sm.a[buf][swz(row, 2 * h + g)];
         const uint2 sc = sm.as[buf][row];
         const uint32_t w = h ? sc.y : sc.x;           // blocks 4h .. 4h+3
         da[i][0] = decode_scale((w >> (16 * g)) & 0xFFu);
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = wn * 128 + j * 32 + r;
-        cb[j] = *reinterpret_cast<const uint4*>(&sm.b[buf][swz(row, 2 * h + g)]);
+        cb[j] = sm.b[buf][swz(row, 2 * h + g)];
         const uint2 sc = sm.bs[buf][row];
         const uint32_t w = h ? sc.y : sc.x;
         db[j][0] = decode_scale((w >> (16 * g)) & 0xFFu);

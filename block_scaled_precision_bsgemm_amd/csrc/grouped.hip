@@ -17,7 +17,8 @@
 // W panel) run close together.  xcd_remap keeps neighbours on one XCD's L2.
 //
 // Tile: 256 rows x 256 columns, 4 waves of 128 x 128, K step 64 elements:
-//   - A codes [256][32] bytes, A scales [256] dwords (4 E4M3 bytes);
+//   - A codes [256][32] bytes (chunks swizzled by (row >> 3) & 1), A scales
+//     [256] dwords (4 E4M3 bytes);
 //   - W [256][64] BF16, 16-byte chunks swizzled by ((row >> 1) & 7).
 // K assignment (A and W agree): lane (r = l % 32, g = l / 32) takes K
 // elements [32g, 32g + 32) of the step.  Dword sp of that range feeds MFMA
@@ -34,16 +35,23 @@ constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
 constexpr int AROWB = BK / 2;        // A code bytes per row per step
 constexpr int WROWB = BK * 2;        // W bytes per row per step
 
+// Tiles are uint4 arrays: the compiler then knows every access is 16-byte
+// aligned and emits single ds_read_b128 / ds_write_b128 instructions.
+constexpr int ARC = AROWB / 16, WRC = WROWB / 16;   // 16-byte chunks per row
 struct Smem {
-  uint8_t a[2][BM * AROWB];
+  uint4 a[2][BM * ARC];
+  uint4 w[2][BN * WRC];
   uint32_t as[2][BM];
-  uint8_t w[2][BN * WROWB];
   int tile_info[4];
 };
 
+// 16-byte chunk c of A row r sits at c ^ ((r >> 3) & 1) (conflict-free for
+// 32 consecutive rows reading one chunk).
+__device__ __forceinline__ int aswz(int row, int chunk) { return row * ARC + (chunk ^ ((row >> 3) & 1)); }
+
 // 16-byte chunk c of W row r sits at c ^ ((r >> 1) & 7): 16 consecutive rows
 // reading one chunk cover all 16 bank groups.
-__device__ __forceinline__ int wswz(int row, int chunk) { return row * WROWB + ((chunk ^ ((row >> 1) & 7)) << 4); }
+__device__ __forceinline__ int wswz(int row, int chunk) { return row * WRC + (chunk ^ ((row >> 1) & 7)); }
 
 // Find the group holding global m-tile `mt` (tiles of BM rows counted group by
 // group).  Run by wave 0.  Writes {group, first row, end row} to `info`, or
@@ -127,11 +135,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
   auto sstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4*>(&sm.a[buf][(alr + 128 * i) * AROWB + alc * 16]) = ra[i];
+      sm.a[buf][aswz(alr + 128 * i, alc)] = ra[i];
     sm.as[buf][tid] = SCALE_DW ? sa_raw[0] : (sa_raw[0] | (sa_raw[1] << 16));
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint4*>(&sm.w[buf][wswz(wlr + 32 * i, wlc)]) = rw[i];
+      sm.w[buf][wswz(wlr + 32 * i, wlc)] = rw[i];
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -155,7 +163,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + r;
-      ca[i] = *reinterpret_cast<const uint4*>(&sm.a[buf][row * AROWB + g * 16]);
+      ca[i] = sm.a[buf][aswz(row, g)];
       const uint32_t sc = sm.as[buf][row];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = wn * 128 + j * 32 + r;
-        const uint4 q = *reinterpret_cast<const uint4*>(&sm.w[buf][wswz(row, 4 * g + sp)]);
+        const uint4 q = sm.w[buf][wswz(row, 4 * g + sp)];
         __builtin_memcpy(&bv[j], &q, 16);
       }
 #pragma unroll
