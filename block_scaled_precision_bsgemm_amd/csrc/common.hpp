@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace bsg {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -182,7 +184,66 @@ __device__ __forceinline__ uint2 buffer_load_x2(rsrc_t r, int off) {
 // to wait for them inside the issuing block.
 constexpr int OOB = 0x7FFFFFF0;
 
+// --------------------------------------------------------- direct-to-LDS loads
+
+// Buffer resource as an SGPR quad, for inline assembly.  Same layout as
+// make_rsrc: base address, stride 0, `bytes` records, raw (untyped) access.
+typedef int rsrc4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ rsrc4_t make_rsrc4(const void* base, int bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  rsrc4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct global->LDS loads (buffer_load ... lds): lane l's 16 (or 4) bytes
+// from `voff` within the resource land in LDS at lds_base + 16 l (4 l), where
+// lds_base is wave-uniform.  Offsets past the resource write zeros.
+//
+// They are issued from inline assembly on purpose.  The compiler cannot tell
+// which LDS bytes such a load writes, so for its own builtin it waits for all
+// outstanding loads before every later LDS read, which serialises a
+// multi-stage ring.  Hidden in assembly, the loads are invisible to its wait
+// insertion.  The kernel waits for them itself (vmcnt) before the barrier that
+// publishes a stage.  The compiler never holds a value in m0 in these
+// kernels; the assembly sets m0 itself.
+__device__ __forceinline__ void dma_x4(rsrc4_t rsrc, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1(rsrc4_t rsrc, uint32_t lds_base, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding and
+// all of its LDS reads have returned, then cross the workgroup barrier.  After
+// it, every wave's loads up to that point have landed in LDS, and no wave
+// still reads an LDS slot that the next direct loads may overwrite.  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
 // -------------------------------------------------------------------- misc
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -23,6 +23,8 @@
 //     is the one of block 2s+g.
 //   - Output lane layout: lane l holds column l % 32, rows
 //     8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -189,14 +191,218 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Ring kernel (K % 128 == 0): the operands stream HBM -> LDS by direct
+// loads through a 4-stage ring of 64-byte K steps, so three steps are in
+// flight while one is computed.  The pages' FP8 GEMM got its gains from the
+// same lever: ring depth.
+//
+// Codes, per stage and operand: [256][64] bytes, 16-byte chunk c of row r at
+// c ^ ((r >> 2) & 3) (conflict-free reads).  Each wave issues 8 code loads
+// per stage (4 A, 4 B; 1 KiB = 16 rows each).
+//
+// Scales are loaded in batches.  With one lane per row, a scale load touches
+// 64 cache lines for a few bytes each, and the address path costs about one
+// clock per line.  Per-stage 4-byte scale loads cost as much as all the code
+// loads.  So one load brings SB bytes per row: the scales of SB/2 K steps
+// (SB = 16 when K % 512 == 0, else 4).  That is one load per operand per wave
+// every SB/2 stages, into a ring of per-super-stage buffers.
+//
+// Per stage each wave runs 16 MFMAs (its 4 x 4 tiles, one K64 MFMA each).
+// The stage's fragments were read into registers during the second half of
+// the previous stage.  Halfway through the MFMAs the wave waits for the next
+// stage's loads, crosses the barrier and reads the next fragments, overlapping
+// the remaining MFMAs.  The K loop is unrolled by one super-stage, so every
+// step's load count and wait count are static.
+constexpr int RB_K = 64, RB_NS = 4, RB_ROW = RB_K / 16;   // 4 chunks per row
+constexpr int RB_CODE_LOADS = 8;                           // code loads per wave per stage
+
+// Scale buffers per super-stage: a buffer is rewritten only after at least
+// two barriers have passed since its last read (3 buffers when a
+// super-stage is only 2 stages long).
+template <int SB>
+constexpr int ring_scale_bufs() { return SB / 2 >= 4 ? 2 : 3; }
+
+template <int SB>
+struct RingSmem {
+  uint4 a[RB_NS][BM * RB_ROW];
+  uint4 b[RB_NS][BN * RB_ROW];
+  uint32_t as[ring_scale_bufs<SB>()][BM * SB / 4];   // [super-stage buffer][row][SB bytes]
+  uint32_t bs[ring_scale_bufs<SB>()][BN * SB / 4];
+};
+
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * RB_ROW + (chunk ^ ((row >> 2) & 3)); }
+
+struct Frags {
+  v8i a[4], b[4];
+  int sa[4], sb[4];
+};
+
+template <int SB>
+__global__ __launch_bounds__(NT, 1) void mxfp8_gemm_ring_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  constexpr int U = SB / 2;                       // stages per scale super-stage
+  __shared__ RingSmem<SB> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KT = K / RB_K;   // a positive multiple of U
+  const int KB = K / 32;
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+  const rsrc4_t ra = make_rsrc4(A + (int64_t)m0 * K, rows_a * K);
+  const rsrc4_t rb = make_rsrc4(B + (int64_t)n0 * K, rows_b * K);
+  const rsrc4_t rsa = make_rsrc4(As + (int64_t)m0 * KB, rows_a * KB);
+  const rsrc4_t rsb = make_rsrc4(Bs + (int64_t)n0 * KB, rows_b * KB);
+
+  // Code-load geometry: instruction u of this wave covers rows 16 (4 wave + u)
+  // .. +15; lane i fills LDS slot i & 3 of row 16 (4 wave + u) + (i >> 2) with
+  // the chunk that the swizzle puts there.
+  int code_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 16 * (4 * wave + u) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    code_off[u] = row * K + chunk * 16;
+  }
+  const int scale_off = (64 * wave + lane) * KB;
+
+  // Stage st: its codes, plus (when st starts a super-stage) the scales of the
+  // whole super-stage.  Stages past the last are issued at an out-of-range
+  // offset: zeros land in slots nobody reads, and every step keeps the same
+  // static wait count.
+  auto issue = [&](int st, auto WITH_SCALES) {
+    const int slot = st % RB_NS;
+    const bool live = st < KT;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int off = live ? code_off[u] + st * RB_K : OOB;
+      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
+      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + u)]), off);
+    }
+    if (decltype(WITH_SCALES)::value) {
+      const int sbuf = (st / U) % ring_scale_bufs<SB>();
+      const int soff = live ? scale_off + (st / U) * SB : OOB;
+      if (SB == 16) {
+        dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
+        dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave * 4]), soff);
+      } else {
+        dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+        dma_x1(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
+      }
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  // Fragments of stage st; `in` = st % U is static.  The stage's E8M0 bytes
+  // are 2 in and 2 in + 1 of the row's SB-byte scale entry; lane g takes
+  // byte 2 in + g.
+  auto read_frags = [&](int st, auto INC, Frags& f) {
+    constexpr int in = decltype(INC)::value;
+    constexpr int word = (2 * in) / 4, shift0 = 8 * ((2 * in) % 4);
+    const int slot = st % RB_NS, sbuf = (st / U) % ring_scale_bufs<SB>();
+    const int sh = shift0 + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r;
+      const uint4 lo = sm.a[slot][rswz(row, g)], hi = sm.a[slot][rswz(row, 2 + g)];
+      f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      f.sa[i] = (int)((sm.as[sbuf][row * (SB / 4) + word] >> sh) & 0xFFu);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + r;
+      const uint4 lo = sm.b[slot][rswz(row, g)], hi = sm.b[slot][rswz(row, 2 + g)];
+      f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      f.sb[j] = (int)((sm.bs[sbuf][row * (SB / 4) + word] >> sh) & 0xFFu);
+    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  auto mfma_rows = [&](const Frags& f, int i0) {
+#pragma unroll
+    for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
+                                                                    f.sa[i], 0, f.sb[j]);
+  };
+
+  // Loads issued for stage s: codes, plus 2 scale loads when s starts a
+  // super-stage.  Waiting for stage kt+1 leaves stages kt+2 and kt+3 in flight.
+  auto loads_of = [](int s_mod) { return RB_CODE_LOADS + (s_mod == 0 ? 2 : 0); };
+
+  // Step kt with kt % U == IN and CUR = kt & 1 (U is even, so IN fixes CUR).
+  Frags f[2];
+  auto step = [&](int kt, auto INC, auto LASTC) {
+    constexpr int IN = decltype(INC)::value;
+    constexpr int CUR = IN & 1;
+    constexpr bool LAST = decltype(LASTC)::value;
+    constexpr int ISSUE_MOD = (IN + RB_NS - 1) % U;   // stage kt+3 within its super-stage
+    constexpr int AFTER = loads_of((IN + 2) % U) + loads_of((IN + 3) % U);
+    if (!LAST) issue(kt + RB_NS - 1, std::integral_constant<bool, ISSUE_MOD == 0>{});
+    mfma_rows(f[CUR], 0);
+    if (!LAST) {
+      wait_vm_barrier<AFTER>();        // stage kt+1 landed; kt+2, kt+3 in flight
+      read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, f[CUR ^ 1]);
+    }
+    mfma_rows(f[CUR], 2);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // 3 LDS reads
+    }
+  };
+
+  // prologue: stages 0..2 (stage 0 carries the first super-stage's scales)
+  issue(0, std::true_type{});
+  issue(1, std::integral_constant<bool, (1 % U) == 0>{});
+  issue(2, std::integral_constant<bool, (2 % U) == 0>{});
+  wait_vm_barrier<loads_of(1 % U) + loads_of(2 % U)>();
+  read_frags(0, std::integral_constant<int, 0>{}, f[0]);
+  // Every step has the same shape, the last ones included: they issue
+  // out-of-range (zero, no traffic) loads for stages past KT and read the
+  // zero fragments of "stage KT", which are never used.  One copy of the
+  // U-step body therefore serves the whole loop.
+  for (int kt = 0; kt < KT; kt += U) {
+    static_for<0, U>([&](auto IC) {
+      constexpr int i = decltype(IC)::value;
+      step(kt + i, std::integral_constant<int, i>{}, std::false_type{});
+    });
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_mxfp8(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
-  if (k % 128 == 0)
-    hipLaunchKernelGGL(mxfp8_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+  if (k % 512 == 0 && k > 0)
+    hipLaunchKernelGGL(mxfp8_gemm_ring_kernel<16>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else if (k % 128 == 0 && k > 0)
+    hipLaunchKernelGGL(mxfp8_gemm_ring_kernel<4>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else
     hipLaunchKernelGGL(mxfp8_gemm_kernel<false>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
