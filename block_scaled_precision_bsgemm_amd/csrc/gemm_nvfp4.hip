@@ -214,6 +214,260 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
     }
 }
 
+
+// Decoded scales of one lane for one half step: for each of its two 16-element
+// blocks, the E4M3 value as FP32 (whose exponent drives the conversion) and
+// (1 + f) as an FP16 pair.  One packed FP8->FP32 conversion decodes both
+// scale bytes (OCP E4M3, exact for every code, subnormals included).
+struct Scales2 {
+  float s[2];
+  uint32_t m2[2];
+};
+
+__device__ __forceinline__ Scales2 decode_scale_pair(uint32_t word16) {
+  const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word16, 1.0f, false);
+  Scales2 d;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    d.s[b] = v[b];
+    // A zero scale needs no special case here: the conversion then scales by
+    // 2^-127, which rounds to zero in FP16.
+    const uint32_t m = ((__float_as_uint(v[b]) >> 13) & 0x3FFu) | 0x3C00u;
+    d.m2[b] = m | (m << 16);
+  }
+  return d;
+}
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
+  return sp == 0 ? q.x : sp == 1 ? q.y : sp == 2 ? q.z : q.w;
+}
+
+// ---------------------------------------------------------------------------
+// Ring kernel (K % 256 == 0).  The operands stream HBM -> LDS by direct loads
+// through a 3-stage ring of 128-element K steps; two steps are in flight
+// while one is computed (a step is ~4096 MFMA cycles, so this covers the
+// memory latency).
+//
+// Per stage and operand, codes are [256][64] bytes, 16-byte chunk c of row r
+// at c ^ ((r >> 2) & 3).  Each wave issues 8 code loads per stage (1 KiB =
+// 16 rows each).  Scales come in batches of 16 bytes per row (two stages of
+// eight 16-element blocks): one load per operand per wave every two stages,
+// with one lane per row.  There are 3 super-stage buffers, so a buffer is
+// rewritten only two barriers after its last read.
+//
+// A step is 8 sub-steps of 16 MFMAs (K16 each); sub-step t uses half t/4 of
+// the step's K range and dword t%4 of the lane's code chunk.  Software
+// pipeline inside a step:
+//   - the operands of sub-step t+1 are dequantised during sub-step t's MFMAs;
+//   - half 1's codes and scale words are read from LDS during sub-step 0 and
+//     decoded during sub-step 2;
+//   - between sub-steps 3 and 4 the wave waits for the next stage and crosses
+//     the barrier; the next stage's half-0 data is read during sub-step 4,
+//     decoded during sub-step 6, and dequantised for its sub-step 0 during
+//     sub-step 7.
+constexpr int NR_NS = 3, NR_ROW = ROWB / 16, NR_SBUF = 3;
+constexpr int NR_CODE_LOADS = 8;
+
+struct NRingSmem {
+  uint4 a[NR_NS][BM * NR_ROW];
+  uint4 b[NR_NS][BN * NR_ROW];
+  uint4 as[NR_SBUF][BM];          // 16 scale bytes per row: stage 2q then 2q+1
+  uint4 bs[NR_SBUF][BN];
+};
+
+// Codes and scale words of one half step for one lane: chunk 2h+g of its 4 A
+// and 4 B rows, and the 16-bit pair of E4M3 bytes of its two blocks.
+struct NHalf {
+  uint4 ca[4], cb[4];
+  uint32_t wa[4], wb[4];
+};
+struct NDec {
+  Scales2 a[4], b[4];
+};
+
+__global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
+    uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+  __shared__ NRingSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KT = K / BK;          // even and > 0 (K % 256 == 0)
+  const int KH = K / 2, KB = K / 16;
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+  const rsrc4_t ra = make_rsrc4(A + (int64_t)m0 * KH, rows_a * KH);
+  const rsrc4_t rb = make_rsrc4(B + (int64_t)n0 * KH, rows_b * KH);
+  const rsrc4_t rsa = make_rsrc4(As + (int64_t)m0 * KB, rows_a * KB);
+  const rsrc4_t rsb = make_rsrc4(Bs + (int64_t)n0 * KB, rows_b * KB);
+
+  int code_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 16 * (4 * wave + u) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    code_off[u] = row * KH + chunk * 16;
+  }
+  const int scale_off = (64 * wave + lane) * KB;
+
+  // Stage st (past-the-end stages load zeros from an out-of-range offset).
+  auto issue = [&](int st, auto WITH_SCALES) {
+    const int slot = st % NR_NS;
+    const bool live = st < KT;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int off = live ? code_off[u] + st * ROWB : OOB;
+      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
+      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + u)]), off);
+    }
+    if (decltype(WITH_SCALES)::value) {
+      const int sbuf = (st / 2) % NR_SBUF;
+      const int soff = live ? scale_off + (st / 2) * 16 : OOB;
+      dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+      dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  // Half h of stage st; `par` = st & 1 selects the stage's 8 bytes of the
+  // 16-byte super-stage entry (static).
+  auto read_half = [&](int st, auto PARC, auto HC, NHalf& x) {
+    constexpr int par = decltype(PARC)::value, h = decltype(HC)::value;
+    const int slot = st % NR_NS, sbuf = (st / 2) % NR_SBUF;
+    const uint32_t* sa32 = reinterpret_cast<const uint32_t*>(&sm.as[sbuf][0]);
+    const uint32_t* sb32 = reinterpret_cast<const uint32_t*>(&sm.bs[sbuf][0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r;
+      x.ca[i] = sm.a[slot][swz(row, 2 * h + g)];
+      x.wa[i] = sa32[row * 4 + par * 2 + h];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + r;
+      x.cb[j] = sm.b[slot][swz(row, 2 * h + g)];
+      x.wb[j] = sb32[row * 4 + par * 2 + h];
+    }
+  };
+  auto decode = [&](const NHalf& x, NDec& d) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d.a[i] = decode_scale_pair(x.wa[i] >> (16 * g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) d.b[j] = decode_scale_pair(x.wb[j] >> (16 * g));
+  };
+  auto dequant = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      av[i] = dequant8_f16(dword_of(x.ca[i], sp), d.a[i].s[sp >> 1], d.a[i].m2[sp >> 1]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      bv[j] = dequant8_f16(dword_of(x.cb[j], sp), d.b[j].s[sp >> 1], d.b[j].m2[sp >> 1]);
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  auto mfmas = [&](const v8h* av, const v8h* bv) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [] {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);   // 5 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+  };
+
+  NHalf x0, x1;     // current stage half 0 / half 1 (x0 is reused for the next stage)
+  NDec d0, d1;
+  v8h av[2][4], bv[2][4];
+
+  // Step kt with parity PAR = kt & 1 (static).  On entry x0/d0 hold stage
+  // kt's half 0 and av[0]/bv[0] its sub-step 0.
+  auto step = [&](int kt, auto PARC) {
+    constexpr int PAR = decltype(PARC)::value;
+    using H0 = std::integral_constant<int, 0>;
+    using H1 = std::integral_constant<int, 1>;
+    // stage kt+2 carries a scale super-stage when it is even, i.e. PAR == 0
+    issue(kt + 2, std::integral_constant<bool, PAR == 0>{});
+    // t = 0
+    mfmas(av[0], bv[0]);
+    dequant(x0, d0, 1, av[1], bv[1]);
+    read_half(kt, PARC, H1{}, x1);
+    interleave();
+    // t = 1
+    mfmas(av[1], bv[1]);
+    dequant(x0, d0, 2, av[0], bv[0]);
+    interleave();
+    // t = 2
+    mfmas(av[0], bv[0]);
+    dequant(x0, d0, 3, av[1], bv[1]);
+    decode(x1, d1);
+    interleave();
+    // t = 3
+    mfmas(av[1], bv[1]);
+    dequant(x1, d1, 0, av[0], bv[0]);
+    interleave();
+    // stage kt+1 landed (stage kt+2 stays in flight)
+    wait_vm_barrier<NR_CODE_LOADS + (PAR == 0 ? 2 : 0)>();
+    // t = 4
+    mfmas(av[0], bv[0]);
+    dequant(x1, d1, 1, av[1], bv[1]);
+    read_half(kt + 1, std::integral_constant<int, PAR ^ 1>{}, H0{}, x0);
+    interleave();
+    // t = 5
+    mfmas(av[1], bv[1]);
+    dequant(x1, d1, 2, av[0], bv[0]);
+    interleave();
+    // t = 6
+    mfmas(av[0], bv[0]);
+    dequant(x1, d1, 3, av[1], bv[1]);
+    decode(x0, d0);
+    interleave();
+    // t = 7
+    mfmas(av[1], bv[1]);
+    dequant(x0, d0, 0, av[0], bv[0]);
+    interleave();
+  };
+
+  // prologue: stages 0 (with the first scale super-stage) and 1
+  issue(0, std::true_type{});
+  issue(1, std::false_type{});
+  wait_vm_barrier<NR_CODE_LOADS>();
+  read_half(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, x0);
+  decode(x0, d0);
+  dequant(x0, d0, 0, av[0], bv[0]);
+  // Uniform body to the end: the last step issues zero loads past KT and
+  // prepares "stage KT" (zeros), which is never used.
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    step(kt + 1, std::integral_constant<int, 1>{});
+  }
+
+  const float alpha = __fmul_rn(*Ats, *Bts);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (row < M && col < N)
+          C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+      }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
@@ -221,7 +475,10 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* bs, const float* bts, uint16_t* c,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
-  if (k % 128 == 0)
+  if (k % 256 == 0 && k > 0)
+    hipLaunchKernelGGL(nvfp4_gemm_ring_kernel, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else if (k % 128 == 0)
     hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else
