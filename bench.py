@@ -258,13 +258,14 @@ def main():
 
 def cpu_baseline(ca, sa, ta, cb, sb, tb, K):
     """The CPU oracle's NVFP4 GEMM (float64 decode + BLAS matmul for C and
-    sum |ab|) on A[0:2048] x B[0:8192] of the benchmark's operands, full K."""
+    sum |ab|) on A[0:8192] x B[0:16384] of the benchmark's operands, full K:
+    about 10-20 s of host work, half the output of one step."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     from oracle import gemm as G
 
-    ms_, ns_ = 2048, 8192
+    ms_, ns_ = 8192, 16384
     qa = (ca[:ms_].cpu().numpy(), sa[:ms_].cpu().numpy(), np.float32(ta.item()))
     qb = (cb[:ns_].cpu().numpy(), sb[:ns_].cpu().numpy(), np.float32(tb.item()))
     t0 = time.perf_counter()
