@@ -166,6 +166,7 @@ int bsgemm_quantize_nvfp4(int64_t rows, int64_t k, const float* x, uint8_t* code
     if (int s = check_k(fn, k)) return s;
     REQUIRE_ALIGNED(x);
     REQUIRE_ALIGNED(codes);
+    REQUIRE_ALIGNED(scales);
     if (int s = check_limits(fn, rows, 0, 0)) return s;
     int num_cus = 0;
     if (int s = check_device(fn, &num_cus)) return s;
@@ -188,6 +189,7 @@ int bsgemm_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* code
     if (int s = check_k(fn, k)) return s;
     REQUIRE_ALIGNED(x);
     REQUIRE_ALIGNED(codes);
+    REQUIRE_ALIGNED(scales);
     if (int s = check_limits(fn, rows, 0, 0)) return s;
     int num_cus = 0;
     if (int s = check_device(fn, &num_cus)) return s;
@@ -221,7 +223,9 @@ int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k, const uint8_t* a,
     }
     if (int s = check_k(fn, k)) return s;
     REQUIRE_ALIGNED(a);
+    REQUIRE_ALIGNED(a_scales);
     REQUIRE_ALIGNED(b);
+    REQUIRE_ALIGNED(b_scales);
     REQUIRE_ALIGNED(c_bf16);
     if (int s = check_limits(fn, m, n, k)) return s;
     int num_cus = 0;
@@ -254,6 +258,7 @@ int bsgemm_grouped_run(int num_groups, int64_t m_total, int64_t n, int64_t k, co
     if (group_offsets == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
     if (int s = check_k(fn, k)) return s;
     REQUIRE_ALIGNED(a);
+    REQUIRE_ALIGNED(a_scales);
     REQUIRE_ALIGNED(w_bf16);
     REQUIRE_ALIGNED(c_bf16);
     if (int s = check_limits(fn, m_total, n, k)) return s;
@@ -284,6 +289,7 @@ int bsgemm_w4a16_run(int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16, co
     if (int s = check_k(fn, k)) return s;
     REQUIRE_ALIGNED(x_bf16);
     REQUIRE_ALIGNED(w);
+    REQUIRE_ALIGNED(w_scales);
     REQUIRE_ALIGNED(c_bf16);
     if (int s = check_limits(fn, m, n, k)) return s;
     int num_cus = 0;

@@ -1,18 +1,17 @@
 // Small-M weight-only 4-bit GEMM: BF16 activations X[M][K] x NVFP4 weights
-// W[N][K], BF16 output.
+// W[N][K], BF16 output C[M][N].
 //
 // Source: "Add sm121 (GB10) tier to the 4-bit GEMM dispatch heuristic"
 // (bitsandbytes PR #2030), sections "Methodology" and "The SIMT / MMA layer".
 // That PR measures a fused dequant+GEMM against dequantise-then-linear, and a
 // SIMT (vector ALU) kernel against a matrix-core kernel at small M.  Here:
-//   - m == 1: gemv_kernel.  Vector ALU only.  Each 16-element block's dot
-//     product is taken on the unscaled E2M1 values (exact in BF16, via fdot2);
-//     the block's full E4M3 scale is applied once, in FP32.
-//   - m >= 2: mfma_kernel.  W fragments go straight from HBM into registers,
-//     are dequantised exactly to BF16 and meet X on the 16x16x32 BF16 MFMA.
-//     The 4 waves of a workgroup split K; partial tiles are summed through LDS.
-// Either way, every weight byte is read from HBM once per M tile; X is small
-// and stays in L2.
+//   - m == 1: gemv_kernel, vector ALU only;
+//   - m >= 2: skinny_kernel, BF16 MFMA.
+// Both read every weight byte from HBM once per 64 rows of X and keep X in
+// L2.  At these sizes the kernels are bound by the weight stream, so both
+// are built to keep as much of it in flight as the hardware allows.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -21,13 +20,18 @@ namespace bsg {
 namespace {
 
 typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------ m == 1
+//
+// Wave = GV_ROWS weight rows.  In each 4096-element chunk of K, lane l owns K
+// [32 l, 32 l + 32) and [2048 + 32 l, 2048 + 32 l + 32): one 16-byte code
+// load per row and half, so every load instruction reads 1 KB of one row.
+// All loads of a chunk are issued before any arithmetic.  Each 16-element
+// block's dot product is taken on the unscaled E2M1 values (exact in BF16,
+// via fdot2); the block's full E4M3 scale is applied once, in FP32.
 
-constexpr int GV_THREADS = 256;
-constexpr int GV_ROWS_PER_WAVE = 4;
-constexpr int GV_ROWS = (GV_THREADS / 64) * GV_ROWS_PER_WAVE;   // rows per workgroup
-constexpr int GV_CHUNK = 64 * 64;                               // K elements per wave pass
+constexpr int GV_ROWS = 4, GV_WAVES = 4;
 
 template <int J>
 __device__ __forceinline__ float dot_e2m1_pair(uint32_t codes, uint32_t xpair, float acc) {
@@ -51,164 +55,315 @@ __device__ __forceinline__ float block_dot(uint32_t c0, uint32_t c1, const uint4
   return p;
 }
 
-// Lane l of a wave handles K elements [kc + 64 l, kc + 64 l + 64) of every
-// chunk kc, as two halves of 32 (K % 32 == 0, so a half is wholly in or out).
-__global__ __launch_bounds__(GV_THREADS) void gemv_kernel(
-    const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
-    const float* __restrict__ Wts, uint16_t* __restrict__ C, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nbase = blockIdx.x * GV_ROWS + wave * GV_ROWS_PER_WAVE;
-  const int KH = K / 2, KB = K / 16;
-  const int rows = max(0, min(N - nbase, GV_ROWS_PER_WAVE));
-  const auto c_rsrc = make_rsrc(Wc + (int64_t)nbase * KH, rows * KH);
-  const auto s_rsrc = make_rsrc(Ws + (int64_t)nbase * KB, rows * KB);
-  const auto x_rsrc = make_rsrc(X, K * 2);
-  float acc[GV_ROWS_PER_WAVE] = {};
-  for (int kc = 0; kc < K; kc += GV_CHUNK) {
-    const int k0 = kc + 64 * lane;
+// Sum R per-lane partial sums over the 64 lanes with a halving butterfly:
+// each step sends half of the remaining values to the partner lane, so the
+// R rows cost R - 1 + (6 - log2 R) shuffles instead of 6 R.  Afterwards lane
+// l holds the total of row rows_lane<R>(l).
+template <int R>
+__device__ __forceinline__ float reduce_rows(float (&v)[R], int lane) {
+  static_assert(R >= 1 && R <= 64 && (R & (R - 1)) == 0, "R must be a power of two");
+  int cnt = R;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kh = k0 + 32 * h;
-      if (kh >= K) break;
-      uint4 x[4];
+  for (int s = 32; s >= 1; s >>= 1) {
+    if (cnt > 1) {
+      const bool hi = (lane & s) != 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) x[q] = buffer_load_x4(x_rsrc, (kh + 8 * q) * 2);
-      uint4 cw[GV_ROWS_PER_WAVE];
-      uint32_t sw[GV_ROWS_PER_WAVE];
-#pragma unroll
-      for (int rr = 0; rr < GV_ROWS_PER_WAVE; ++rr) {
-        // 16 code bytes (32 elements) and 2 scale bytes per row
-        const uint4 v = buffer_load_x4(c_rsrc, rr * KH + kh / 2);
-        cw[rr] = v;
-        sw[rr] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, rr * KB + kh / 16, 0, 0);
+      for (int i = 0; i < R / 2; ++i) {
+        if (i < cnt / 2) {
+          const float send = hi ? v[i] : v[i + cnt / 2];
+          const float keep = hi ? v[i + cnt / 2] : v[i];
+          v[i] = keep + __shfl_xor(send, s);
+        }
       }
-#pragma unroll
-      for (int rr = 0; rr < GV_ROWS_PER_WAVE; ++rr) {
-        const float s0 = e4m3_scale_value(sw[rr] & 0xFFu);
-        const float s1 = e4m3_scale_value((sw[rr] >> 8) & 0xFFu);
-        acc[rr] = fmaf(block_dot(cw[rr].x, cw[rr].y, x[0], x[1]), s0, acc[rr]);
-        acc[rr] = fmaf(block_dot(cw[rr].z, cw[rr].w, x[2], x[3]), s1, acc[rr]);
-      }
+      cnt /= 2;
+    } else {
+      v[0] += __shfl_xor(v[0], s);
     }
   }
-  const float ts = *Wts;
-#pragma unroll
-  for (int rr = 0; rr < GV_ROWS_PER_WAVE; ++rr) {
-    float v = acc[rr];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    if (lane == rr && rr < rows) C[nbase + rr] = (uint16_t)f32_to_bf16_rne(v * ts);
+  return v[0];
+}
+template <int R>
+__device__ __forceinline__ int rows_lane(int lane) {
+  int r = 0, half = R / 2, s = 32;
+  for (int i = 0; (1 << i) < R; ++i) {
+    if (lane & s) r += half;
+    half >>= 1;
+    s >>= 1;
   }
+  return r;
+}
+
+__global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
+    const float* __restrict__ Wts, uint16_t* __restrict__ C, int N, int K) {
+  constexpr int R = GV_ROWS;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * GV_WAVES + wave) * R;
+  const int KH = K / 2, KB = K / 16;
+  const int rows = max(0, min(N - n0, R));
+  const auto c_rsrc = make_rsrc(Wc + (int64_t)n0 * KH, rows * KH);
+  const auto s_rsrc = make_rsrc(Ws + (int64_t)n0 * KB, rows * KB);
+  const auto x_rsrc = make_rsrc(X, K * 2);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int kc = 0; kc < K; kc += 4096) {
+    // K % 32 == 0, so each lane's 32-element group is wholly in or out of K
+    const int g0 = kc + 32 * lane, g1 = kc + 2048 + 32 * lane;
+    const bool in0 = g0 < K, in1 = g1 < K;
+    uint4 x0[4], x1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x0[q] = buffer_load_x4(x_rsrc, in0 ? (g0 + 8 * q) * 2 : OOB);
+      x1[q] = buffer_load_x4(x_rsrc, in1 ? (g1 + 8 * q) * 2 : OOB);
+    }
+    uint4 c0[R], c1[R];
+    uint32_t s0[R], s1[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      c0[r] = buffer_load_x4(c_rsrc, in0 ? r * KH + g0 / 2 : OOB);
+      s0[r] = buffer_load_u16(s_rsrc, in0 ? r * KB + g0 / 16 : OOB);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      c1[r] = buffer_load_x4(c_rsrc, in1 ? r * KH + g1 / 2 : OOB);
+      s1[r] = buffer_load_u16(s_rsrc, in1 ? r * KB + g1 / 16 : OOB);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float a = acc[r];
+      a = fmaf(block_dot(c0[r].x, c0[r].y, x0[0], x0[1]), e4m3_scale_value(s0[r] & 0xFFu), a);
+      a = fmaf(block_dot(c0[r].z, c0[r].w, x0[2], x0[3]), e4m3_scale_value(s0[r] >> 8), a);
+      a = fmaf(block_dot(c1[r].x, c1[r].y, x1[0], x1[1]), e4m3_scale_value(s1[r] & 0xFFu), a);
+      a = fmaf(block_dot(c1[r].z, c1[r].w, x1[2], x1[3]), e4m3_scale_value(s1[r] >> 8), a);
+      acc[r] = a;
+    }
+  }
+  const float tot = reduce_rows<R>(acc, lane);
+  const int r = rows_lane<R>(lane);
+  if ((lane & (64 / R - 1)) == 0 && r < rows) C[n0 + r] = (uint16_t)f32_to_bf16_rne(tot * *Wts);
 }
 
 // ------------------------------------------------------------------ m >= 2
+//
+// Workgroup = SK_CONS consumer waves + SK_PROD producer waves.  It owns W rows
+// [n0, n0 + nb) (nb <= 64: four 16-row MFMA tiles; rows past nb are masked)
+// and X rows [m0, m0 + MT), over all of K.
+//
+// K is cut into 128-element blocks; stage s holds KS consecutive blocks.
+// Consumer c = (tile group g = c % TP, K split h = c / TP) owns the NT = 4/TP
+// W tiles of group g and, in stage s, block KS s + h.  It loads its W codes
+// straight from HBM into registers, RING stages ahead, dequantises them exactly
+// to BF16 and runs 16x16x32 BF16 MFMAs against X fragments from LDS.
+// The producers direct-load each stage's X blocks (and, when K % 256 == 0,
+// the stage's scales) into an NSLOT-deep LDS ring, NSLOT - 1 stages ahead.
+// Producers and consumers are separate waves so that the deep weight stream
+// and the shallow X stream each have their own in-order load counter.
+// One workgroup barrier per stage publishes a slot and retires the oldest.
+// At the end the K splits are summed through LDS.
+//
+// K inside a block: lane (r, q) of a W tile holds the codes of K
+// [32 q, 32 q + 32) (one 16-byte load); its dword sp feeds MFMA sub-step sp at
+// K positions 8 q .. 8 q + 7.  X fragments use the same assignment, so each
+// MFMA sums a consistent set of 32 K positions.
 
-constexpr int MM_THREADS = 256;
-constexpr int MM_NB = 32;   // weight rows (output columns) per workgroup
+constexpr int SK_CONS = 8, SK_PROD = 2, SK_THREADS = 64 * (SK_CONS + SK_PROD);
 
-typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+template <int MT, int KS>
+struct SkStage {
+  uint4 x[KS][MT * 16];    // [block][row m: 16 chunks of 16 B; chunk c at c ^ (m & 15)]
+  uint4 s[64 * KS / 2];    // W scales of the stage: row r at bytes [8 KS r, 8 KS r + 8 KS)
+};
 
-// K assignment (W and X agree): in each 128-element step, lane (r = l % 16,
-// q = l / 16) takes elements [32q, 32q + 32).  Dword sp of those 32 feeds MFMA
-// sub-step sp at positions 8q..8q+7, with scale block 2q + sp/2.
-template <int MT>
-__global__ __launch_bounds__(MM_THREADS, 1) void mfma_kernel(
+// Exact BF16 pair from two E2M1 codes (byte J of `codes`) and an E4M3 scale
+// s = 2^E (1 + f): the conversion applies 2^E, one FP32 multiply each applies
+// (1 + f) (both exact), and a byte permute packs the high halves.
+template <int J>
+__device__ __forceinline__ uint32_t dequant_pair_bf16(uint32_t codes, float s, float mant) {
+  const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, s, J);
+  return __builtin_amdgcn_perm(__float_as_uint(p[1] * mant), __float_as_uint(p[0] * mant), 0x07060302u);
+}
+
+template <int MT, int KS, int NSLOT, bool SDMA, int P>
+__device__ __forceinline__ void sk_produce(SkStage<MT, KS>* st, const uint16_t* X, const uint8_t* Ws, int m0,
+                                           int n0, int rows_x, int rows_w, int K, int S, int lane) {
+  constexpr int XD = KS * MT / 4;             // X loads per stage (1 KB each)
+  constexpr int SD = SDMA ? KS / 2 : 0;       // scale loads per stage (1 KB each)
+  constexpr int CNT = (XD + SK_PROD - 1 - P) / SK_PROD + (SD + SK_PROD - 1 - P) / SK_PROD;
+  static_assert(CNT * (NSLOT - 2) < 64, "outstanding loads exceed the vmcnt range");
+  const int KB = K / 16;
+  const auto x_rsrc = make_rsrc4(X + (int64_t)m0 * K, rows_x * K * 2);
+  const auto s_rsrc = make_rsrc4(Ws + (int64_t)n0 * KB, rows_w * KB);
+  auto issue = [&](int s) {
+    SkStage<MT, KS>& t = st[s % NSLOT];
+    const int kst = s * 128 * KS;
+#pragma unroll
+    for (int i = P; i < XD; i += SK_PROD) {
+      // 4 rows of block j: lane -> (row m, LDS chunk lane & 15)
+      const int j = i / (MT / 4), m = 4 * (i % (MT / 4)) + (lane >> 4);
+      const int c = (lane & 15) ^ (m & 15);
+      const int k = kst + 128 * j + 8 * c;
+      dma_x4(x_rsrc, lds_addr(&t.x[j][4 * (i % (MT / 4)) * 16]), k < K ? (m * K + k) * 2 : OOB);
+    }
+#pragma unroll
+    for (int i = P; i < SD; i += SK_PROD) {
+      const int e = 64 * i + lane;                      // 16-byte piece: row e / (KS/2)
+      const int r = e / (KS / 2), b = kst / 16 + 16 * (e % (KS / 2));
+      dma_x4(s_rsrc, lds_addr(&t.s[64 * i]), b < KB ? r * KB + b : OOB);
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < NSLOT - 1; ++p) issue(p);
+  for (int s = 0; s < S; ++s) {
+    wait_vm_barrier<CNT * (NSLOT - 2)>();   // stage s has landed: publish it
+    issue(s + NSLOT - 1);                   // into the slot retired by that barrier
+  }
+  // the consumers' two final barriers: stage reads done, partial sums written
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
+}
+
+template <int MT, int TP, int NSLOT, int RING, bool SDMA>
+__global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
-    const float* __restrict__ Wts, uint16_t* __restrict__ C, int M, int N, int K) {
-  constexpr int NI = MM_NB / 16, NJ = MT / 16;
-  __shared__ v4f red[3][NI * NJ][64];
+    const float* __restrict__ Wts, uint16_t* __restrict__ C, int M, int N, int K, int nb, int m_tiles) {
+  constexpr int NJ = MT / 16, KS = SK_CONS / TP, NT = 4 / TP;
+  static_assert(KS % 2 == 0 && NT * TP == 4, "consumer split");
+  __shared__ SkStage<MT, KS> st[NSLOT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * MM_NB, m0 = blockIdx.y * MT;
+  // consecutive workgroups (the m tiles of one W slab) share an XCD's L2
+  const int lin = xcd_remap(blockIdx.x, gridDim.x);
+  const int n0 = (lin / m_tiles) * nb, m0 = (lin % m_tiles) * MT;
   const int KH = K / 2, KB = K / 16;
-  const int rows_w = min(N - n0, MM_NB), rows_x = min(M - m0, MT);
+  const int rows_w = max(0, min(nb, N - n0)), rows_x = max(0, min(MT, M - m0));
+  const int S = (K + 128 * KS - 1) / (128 * KS);
+
+  if (wave >= SK_CONS) {
+    if (wave == SK_CONS) sk_produce<MT, KS, NSLOT, SDMA, 0>(st, X, Ws, m0, n0, rows_x, rows_w, K, S, lane);
+    else sk_produce<MT, KS, NSLOT, SDMA, 1>(st, X, Ws, m0, n0, rows_x, rows_w, K, S, lane);
+    return;
+  }
+
+  // ------------------------------------------------------------ consumers
+  const int g = wave % TP, h = wave / TP;
+  const int r = lane & 15, q = lane >> 4;
   const auto c_rsrc = make_rsrc(Wc + (int64_t)n0 * KH, rows_w * KH);
   const auto s_rsrc = make_rsrc(Ws + (int64_t)n0 * KB, rows_w * KB);
-  const auto x_rsrc = make_rsrc(X + (int64_t)m0 * K, rows_x * K * 2);
-  // this wave's K range: a quarter of the 128-element steps
-  const int steps = (K + 127) / 128;
-  const int per = (steps + 3) / 4;
-  const int s_begin = wave * per, s_end = min(steps, s_begin + per);
-
-  v4f acc[NI][NJ];
+  auto wrow = [&](int il) { return 16 * (g * NT + il) + r; };
+  auto wload = [&](int s, int il) -> uint4 {
+    const int t = KS * s + h, k = 128 * t + 32 * q;
+    return buffer_load_x4(c_rsrc, (s < S && k < K) ? wrow(il) * KH + 64 * t + 16 * q : OOB);
+  };
+  auto sload = [&](int s, int il) -> uint32_t {   // scales of blocks 8t + 2q, 8t + 2q + 1
+    const int t = KS * s + h, k = 128 * t + 32 * q;
+    return SDMA ? 0u : buffer_load_u16(s_rsrc, (s < S && k < K) ? wrow(il) * KB + 8 * t + 2 * q : OOB);
+  };
+  uint4 wr[RING][NT];
+  uint32_t sr[RING][NT];
+  static_for<0, RING>([&](auto B) {
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = v4f{};
-
-  for (int st = s_begin; st < s_end; ++st) {
-    const int kq = st * 128 + 32 * q;          // first K element of this lane
-    const bool kin = kq < K;                   // K % 32 == 0: 32 elements wholly in or out
-    uint4 wc[NI];
-    uint32_t ws[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = 16 * i + r;
-      wc[i] = buffer_load_x4(c_rsrc, kin ? row * KH + kq / 2 : OOB);
-      ws[i] = buffer_load_u16(s_rsrc, kin ? row * KB + kq / 16 : OOB);
+    for (int il = 0; il < NT; ++il) {
+      wr[B][il] = wload(B, il);
+      sr[B][il] = sload(B, il);
     }
-    uint4 xv[NJ][4];
+  });
+  v4f acc[NT][NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+  for (int il = 0; il < NT; ++il)
 #pragma unroll
-      for (int sp = 0; sp < 4; ++sp)
-        xv[j][sp] = buffer_load_x4(x_rsrc, kin ? ((16 * j + r) * K + kq + 8 * sp) * 2 : OOB);
-    float s[NI][2], mant[NI][2];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        s[i][b] = e4m3_scale_value((ws[i] >> (8 * b)) & 0xFFu);
-        mant[i][b] = scale_mantissa_f32(s[i][b]);
-      }
-#pragma unroll
-    for (int sp = 0; sp < 4; ++sp) {
-      v8bf_t wv[NI];
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const uint32_t d = sp == 0 ? wc[i].x : sp == 1 ? wc[i].y : sp == 2 ? wc[i].z : wc[i].w;
-        const v8bf w8 = dequant8_bf16(d, s[i][sp >> 1], mant[i][sp >> 1]);
-        __builtin_memcpy(&wv[i], &w8, 16);
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        v8bf_t x8;
-        __builtin_memcpy(&x8, &xv[j][sp], 16);
-#pragma unroll
-        for (int i = 0; i < NI; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[i], x8, acc[i][j], 0, 0, 0);
-      }
-    }
-  }
+    for (int j = 0; j < NJ; ++j) acc[il][j] = v4f{};
 
-  // sum the four waves' partial tiles
-  if (wave > 0) {
+  for (int s0 = 0; s0 < S; s0 += RING) {
+    static_for<0, RING>([&](auto B) {
+      const int s = s0 + B;
+      if (s < S) {
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage s published
+        const SkStage<MT, KS>& t = st[s % NSLOT];
+        float sc[NT][2], mn[NT][2];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+        for (int il = 0; il < NT; ++il) {
+          uint32_t w16;
+          if (SDMA)
+            w16 = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(t.s) +
+                                                     wrow(il) * 8 * KS + 8 * h + 2 * q);
+          else
+            w16 = sr[B][il];
+          sc[il][0] = e4m3_scale_value(w16 & 0xFFu);
+          sc[il][1] = e4m3_scale_value(w16 >> 8);
+          mn[il][0] = scale_mantissa_f32(sc[il][0]);
+          mn[il][1] = scale_mantissa_f32(sc[il][1]);
+        }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) red[wave - 1][i * NJ + j][lane] = acc[i][j];
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const float ts = *Wts;
+        for (int sp = 0; sp < 4; ++sp) {
+          v8bf_t wv[NT];
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+          for (int il = 0; il < NT; ++il) {
+            const uint32_t d = sp == 0 ? wr[B][il].x : sp == 1 ? wr[B][il].y : sp == 2 ? wr[B][il].z : wr[B][il].w;
+            const float sv = sc[il][sp >> 1], mv = mn[il][sp >> 1];
+            const uint32_t w4[4] = {dequant_pair_bf16<0>(d, sv, mv), dequant_pair_bf16<1>(d, sv, mv),
+                                    dequant_pair_bf16<2>(d, sv, mv), dequant_pair_bf16<3>(d, sv, mv)};
+            __builtin_memcpy(&wv[il], w4, 16);
+          }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        v4f v = acc[i][j];
+          for (int j = 0; j < NJ; ++j) {
+            const uint4 xv = t.x[h][(16 * j + r) * 16 + ((4 * q + sp) ^ r)];
+            v8bf_t x8;
+            __builtin_memcpy(&x8, &xv, 16);
 #pragma unroll
-        for (int w = 0; w < 3; ++w) v += red[w][i * NJ + j][lane];
-        // D[n][m] lane layout: column m = 16 j + r, rows n = 16 i + 4 q + e
-        const int m = m0 + 16 * j + r;
-        if (m < M) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int n = n0 + 16 * i + 4 * q + e;
-            if (n < N) C[(int64_t)m * N + n] = (uint16_t)f32_to_bf16_rne(v[e] * ts);
+            for (int il = 0; il < NT; ++il)
+              acc[il][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[il], x8, acc[il][j], 0, 0, 0);
           }
         }
+        // refill this ring slot with the block RING stages ahead
+#pragma unroll
+        for (int il = 0; il < NT; ++il) {
+          wr[B][il] = wload(s + RING, il);
+          sr[B][il] = sload(s + RING, il);
+        }
       }
+    });
   }
+
+  // ---- sum the K splits through LDS; consumer i (< 4) finishes W tile i
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  v4f* red = reinterpret_cast<v4f*>(&st[0]);   // [consumer][il][j][lane]
+  static_assert(SK_CONS * NT * NJ * 64 * sizeof(v4f) <= sizeof(st), "reduction space");
+#pragma unroll
+  for (int il = 0; il < NT; ++il)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) red[((wave * NT + il) * NJ + j) * 64 + lane] = acc[il][j];
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (wave >= 4) return;
+  const float ts = *Wts;
+  const int i = wave, gi = i / NT, il = i % NT;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    v4f v = v4f{};
+#pragma unroll
+    for (int hh = 0; hh < KS; ++hh) v += red[(((hh * TP + gi) * NT + il) * NJ + j) * 64 + lane];
+    // D[n][m] fragment: column m = 16 j + r, rows n = 16 i + 4 q + e
+    const int m = m0 + 16 * j + r;
+    const int nl = 16 * i + 4 * q;
+    if (m < M) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (nl + e < rows_w) C[(int64_t)m * N + n0 + nl + e] = (uint16_t)f32_to_bf16_rne(v[e] * ts);
+    }
+  }
+}
+
+template <int MT, int TP, int NSLOT, int RING>
+void launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w, const uint8_t* ws,
+                   const float* wts, uint16_t* c, hipStream_t stream) {
+  // W rows per workgroup: about one workgroup per CU for the W slab, 16..64
+  const int nb = (int)std::min<int64_t>(64, std::max<int64_t>(16, ceil_div(n, 256)));
+  const int n_tiles = (int)ceil_div(n, nb), m_tiles = (int)ceil_div(m, MT);
+  const dim3 grid((unsigned)(n_tiles * m_tiles));
+  if (k % 256 == 0)
+    hipLaunchKernelGGL((skinny_kernel<MT, TP, NSLOT, RING, true>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
+                       wts, c, (int)m, (int)n, (int)k, nb, m_tiles);
+  else
+    hipLaunchKernelGGL((skinny_kernel<MT, TP, NSLOT, RING, false>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
+                       wts, c, (int)m, (int)n, (int)k, nb, m_tiles);
 }
 
 }  // namespace
@@ -216,14 +371,14 @@ __global__ __launch_bounds__(MM_THREADS, 1) void mfma_kernel(
 hipError_t launch_w4a16(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream) {
   if (m == 1) {
-    hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)ceil_div(n, GV_ROWS)), dim3(GV_THREADS), 0,
+    hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)ceil_div(n, GV_ROWS * GV_WAVES)), dim3(64 * GV_WAVES), 0,
                        stream, x, w, ws, wts, c, (int)n, (int)k);
   } else if (m <= 16) {
-    hipLaunchKernelGGL(mfma_kernel<16>, dim3((unsigned)ceil_div(n, MM_NB), (unsigned)ceil_div(m, 16)),
-                       dim3(MM_THREADS), 0, stream, x, w, ws, wts, c, (int)m, (int)n, (int)k);
+    launch_skinny<16, 2, 8, 1>(m, n, k, x, w, ws, wts, c, stream);
+  } else if (m <= 32) {
+    launch_skinny<32, 2, 4, 1>(m, n, k, x, w, ws, wts, c, stream);
   } else {
-    hipLaunchKernelGGL(mfma_kernel<64>, dim3((unsigned)ceil_div(n, MM_NB), (unsigned)ceil_div(m, 64)),
-                       dim3(MM_THREADS), 0, stream, x, w, ws, wts, c, (int)m, (int)n, (int)k);
+    launch_skinny<64, 4, 4, 2>(m, n, k, x, w, ws, wts, c, stream);
   }
   return hipGetLastError();
 }

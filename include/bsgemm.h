@@ -37,8 +37,9 @@
  *     noted.  The caller allocates and owns every buffer.  The library never
  *     allocates, frees or keeps a pointer after the call returns.
  *   - Buffers are dense and row-major; pitches are implied by the sizes.  Code
- *     buffers, x, w_bf16, x_bf16 and c_bf16 must be 16-byte aligned.  Scale
- *     buffers and scalar slots need only their natural alignment.
+ *     buffers, scale buffers, x, w_bf16, x_bf16 and c_bf16 must be 16-byte
+ *     aligned (the kernels fetch scales in 4- and 16-byte pieces).  Scalar
+ *     slots (tensor scales, group offsets) need only their natural alignment.
  *   - Work is queued on `stream` (a hipStream_t; NULL = the null stream).  The
  *     call returns without waiting.  Keep the buffers alive until the stream
  *     has finished.
@@ -99,7 +100,7 @@ enum bsgemm_format {
  * Arguments:
  *   x            device float[rows][k], 16-byte aligned
  *   codes        device uint8[rows][k/2], 16-byte aligned (written)
- *   scales       device uint8[rows][k/16] (written)
+ *   scales       device uint8[rows][k/16], 16-byte aligned (written)
  *   tensor_scale device float[1] (written).  Used as the amax slot during the
  *                call: it holds amax bits until the call's last kernel has run.
  * Sizes: rows >= 0, k >= 0, k % 32 == 0.
@@ -127,7 +128,7 @@ int bsgemm_quantize_nvfp4(int64_t rows, int64_t k, const float* x, uint8_t* code
  * Arguments:
  *   x      device float[rows][k], 16-byte aligned
  *   codes  device uint8[rows][k], 16-byte aligned (written)
- *   scales device uint8[rows][k/32] (written)
+ *   scales device uint8[rows][k/32], 16-byte aligned (written)
  * Sizes: rows >= 0, k >= 0, k % 32 == 0.
  */
 int bsgemm_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* codes,

@@ -60,6 +60,9 @@ def test_run_validation(so):
     assert run(so, fmt=L.BSGEMM_MXFP8) == L.BSGEMM_ERR_UNSUPPORTED      # tensor scales given
     assert run(so, a=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, c=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert run(so, sa=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert b"a_scales is not 16-byte aligned" in so.bsgemm_last_error()
+    assert run(so, sb=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, k=1 << 22) == L.BSGEMM_ERR_RESOURCE
     # an empty operand may be NULL; the error then comes from the next check
     assert run(so, m=0, a=None, sa=None, c=None, k=48) == L.BSGEMM_ERR_UNSUPPORTED
@@ -71,10 +74,12 @@ def test_quantize_validation(so):
     assert q4(4, 64, P, P, P, None, None) == L.BSGEMM_ERR_INVALID_ARG
     assert q4(4, 40, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert q4(4, 64, MIS, P, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert q4(4, 64, P, P, MIS, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert q8(-1, 64, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
     assert q8(4, 64, P, None, P, None) == L.BSGEMM_ERR_INVALID_ARG
     assert q8(4, 16, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert q8(4, 64, P, MIS, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert q8(4, 64, P, P, MIS, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
 
 
 def test_grouped_and_w4a16_validation(so):
@@ -84,11 +89,13 @@ def test_grouped_and_w4a16_validation(so):
     assert g(2, 64, 64, 64, P, P, None, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
     assert g(2, 64, 64, 33, P, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert g(2, 64, 64, 64, P, P, P, P, MIS, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert g(2, 64, 64, 64, P, MIS, P, P, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
     w = so.bsgemm_w4a16_run
     assert w(1, 64, 64, None, P, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
     assert w(1, 64, 64, P, P, P, None, P, None) == L.BSGEMM_ERR_INVALID_ARG
     assert w(1, 64, 80, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert w(1, 64, 64, MIS, P, P, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert w(1, 64, 64, P, P, MIS, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
 
 
 def test_last_error_is_per_thread(so):

@@ -315,6 +315,7 @@ def _gpu_w4a16(x, qw, m):
 @pytest.mark.parametrize("m,n,k", [
     (1, 1, 32), (1, 33, 96), (1, 100, 4096), (1, 64, 8192 + 32), (2, 50, 64), (3, 16, 128),
     (16, 130, 256), (17, 64, 512), (64, 96, 4096), (65, 40, 160), (100, 33, 96), (256, 64, 1024),
+    (5, 300, 1024), (16, 48, 8192 + 96), (32, 40, 4096 + 256), (33, 70, 2048 + 512),
 ])
 def test_w4a16_shapes(gpu_lib, m, n, k):
     x = synth.bf16_bits(synth.normal_f32((m, k), m + n + k))
