@@ -234,6 +234,24 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
+// ------------------------------------------------------------- tile order
+
+// Output-tile order for large GEMM grids (tiles_m and tiles_n multiples of
+// 16).  Workgroups are dispatched round-robin over the 8 XCDs, and one wave
+// of 256 workgroups (one per CU, 32 per XCD) runs at a time.  Each such wave
+// covers one 16 x 16 block of output tiles (a "super-tile"): XCD x takes the
+// 4 x 8 sub-block at tile rows 4 (x % 4) and tile columns 8 (x / 4), so its
+// L2 serves 4 A panels and 8 B panels per K step.  Super-tiles are walked
+// along a row, so their 16 A panels stay in the infinity cache while the B
+// panels stream through it.
+__device__ __forceinline__ void supertile_order(int bid, int tiles_n, int& tm, int& tn) {
+  const int x = bid & 7, i = bid >> 3;
+  const int st = i >> 5, w = i & 31;
+  const int per_row = tiles_n >> 4;
+  tm = (st / per_row) * 16 + 4 * (x & 3) + (w & 3);
+  tn = (st % per_row) * 16 + 8 * (x >> 2) + (w >> 2);
+}
+
 // -------------------------------------------------------------------- misc
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).

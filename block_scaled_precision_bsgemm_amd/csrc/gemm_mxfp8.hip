@@ -248,7 +248,10 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_ring_kernel(
   __shared__ RingSmem<SB> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tm, tn;
-  raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
+    supertile_order(blockIdx.x, tiles_n, tm, tn);
+  else
+    raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = K / RB_K;   // a positive multiple of U
   const int KB = K / 32;
@@ -299,26 +302,31 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_ring_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   // Fragments of stage st; `in` = st % U is static.  The stage's E8M0 bytes
-  // are 2 in and 2 in + 1 of the row's SB-byte scale entry; lane g takes
-  // byte 2 in + g.
+  // are 2 in and 2 in + 1 of the row's SB-byte scale entry; lane g takes byte
+  // 2 in + g.  Both sit in dword in / 2; shifting it right by 8 g puts lane
+  // g's byte at position 2 (in % 2) for both lane halves, and the MFMA's
+  // scale byte select (op_sel) picks it there: no per-byte extraction.  The
+  // scale dwords are read first, so the first MFMA never waits on a drained
+  // LDS queue.
   auto read_frags = [&](int st, auto INC, Frags& f) {
     constexpr int in = decltype(INC)::value;
-    constexpr int word = (2 * in) / 4, shift0 = 8 * ((2 * in) % 4);
+    constexpr int word = in / 2;
     const int slot = st % RB_NS, sbuf = (st / U) % ring_scale_bufs<SB>();
-    const int sh = shift0 + 8 * g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.sa[i] = (int)(sm.as[sbuf][(wm * 128 + i * 32 + r) * (SB / 4) + word] >> (8 * g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.sb[j] = (int)(sm.bs[sbuf][(wn * 128 + j * 32 + r) * (SB / 4) + word] >> (8 * g));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + r;
       const uint4 lo = sm.a[slot][rswz(row, g)], hi = sm.a[slot][rswz(row, 2 + g)];
       f.a[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      f.sa[i] = (int)((sm.as[sbuf][row * (SB / 4) + word] >> sh) & 0xFFu);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wn * 128 + j * 32 + r;
       const uint4 lo = sm.b[slot][rswz(row, g)], hi = sm.b[slot][rswz(row, 2 + g)];
       f.b[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      f.sb[j] = (int)((sm.bs[sbuf][row * (SB / 4) + word] >> sh) & 0xFFu);
     }
   };
 
@@ -327,13 +335,15 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_ring_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
-  auto mfma_rows = [&](const Frags& f, int i0) {
+  // OPSEL: byte of the (shifted) scale dwords that holds this stage's scale
+  auto mfma_rows = [&](const Frags& f, int i0, auto OPSEL) {
+    constexpr int sel = decltype(OPSEL)::value;
 #pragma unroll
     for (int i = i0; i < i0 + 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0,
-                                                                    f.sa[i], 0, f.sb[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, sel,
+                                                                    f.sa[i], sel, f.sb[j]);
   };
 
   // Loads issued for stage s: codes, plus 2 scale loads when s starts a
@@ -348,13 +358,17 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_ring_kernel(
     constexpr bool LAST = decltype(LASTC)::value;
     constexpr int ISSUE_MOD = (IN + RB_NS - 1) % U;   // stage kt+3 within its super-stage
     constexpr int AFTER = loads_of((IN + 2) % U) + loads_of((IN + 3) % U);
+    constexpr auto SEL = std::integral_constant<int, 2 * (IN % 2)>{};
     if (!LAST) issue(kt + RB_NS - 1, std::integral_constant<bool, ISSUE_MOD == 0>{});
-    mfma_rows(f[CUR], 0);
+    // keep the loads at the head of the step: the compiler would otherwise
+    // sink them below the first MFMAs and shorten the ring's lead
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(f[CUR], 0, SEL);
     if (!LAST) {
       wait_vm_barrier<AFTER>();        // stage kt+1 landed; kt+2, kt+3 in flight
       read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, f[CUR ^ 1]);
     }
-    mfma_rows(f[CUR], 2);
+    mfma_rows(f[CUR], 2, SEL);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
@@ -379,17 +393,30 @@ __global__ __launch_bounds__(NT, 1) void mxfp8_gemm_ring_kernel(
     });
   }
 
+  // Epilogue.  Tiles wholly inside C (all but the ragged edge) store without
+  // per-element bounds checks; each store writes two 64-byte row segments.
+  uint16_t* cw = C + (int64_t)(m0 + wm * 128 + g * 4) * N + n0 + wn * 128 + r;
+  if (m0 + BM <= M && n0 + BN <= N) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + r;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+        for (int v = 0; v < 16; ++v)
+          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+        }
       }
-    }
+  }
 }
 
 }  // namespace

@@ -292,7 +292,10 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   __shared__ NRingSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tm, tn;
-  raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
+    supertile_order(blockIdx.x, tiles_n, tm, tn);
+  else
+    raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int KT = K / BK;          // even and > 0 (K % 256 == 0)
   const int KH = K / 2, KB = K / 16;
