@@ -129,11 +129,13 @@ __device__ __forceinline__ v8h dequant8_f16(uint32_t codes, float s, uint32_t ma
 // Eight E2M1 codes times an E4M3 scale, as exact BF16 values.  The BF16
 // products have at most 6 significant bits, so they are exact.  The
 // conversion gives v * 2^E as FP32; one FP32 multiply by (1 + f) completes the
-// scale; the high halves of the exact FP32 results are the BF16 patterns.
+// scale; the high halves of the exact FP32 results are the BF16 patterns,
+// packed by one byte permute.  `mant` is scale_mantissa_f32(s): 0 for a zero
+// scale, which the conversion alone would leave as 2^-127 (not zero).
 template <int J>
 __device__ __forceinline__ uint32_t dequant2_bf16(uint32_t codes, float s, float mant) {
   const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, s, J);
-  return (__float_as_uint(p[0] * mant) >> 16) | (__float_as_uint(p[1] * mant) & 0xFFFF0000u);
+  return __builtin_amdgcn_perm(__float_as_uint(p[1] * mant), __float_as_uint(p[0] * mant), 0x07060302u);
 }
 
 __device__ __forceinline__ v8bf dequant8_bf16(uint32_t codes, float s, float mant) {

@@ -210,6 +210,264 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Ring kernel (K % 64 == 0).  The same tiles and K assignment as above (tile
+// order n-major, see below), but
+// the operands stream HBM -> LDS by direct loads through a 3-stage ring of
+// 64-element K steps (two steps in flight while one is computed), and the
+// BF16 dequantisation of A runs one MFMA sub-step ahead, under the previous
+// sub-step's MFMAs.  One barrier per step.
+//
+// Per stage: A codes [256][32] bytes (chunk swizzle (r >> 3) & 1, 2 loads per
+// wave), W [256][128] bytes (chunk swizzle (r >> 1) & 7, 8 loads per wave).
+// A scales come SB bytes per row at a time (SB = 16, four steps, when
+// K % 256 == 0; else 4): one load per wave per SB/4 steps, into a ring of 3
+// buffers, so a buffer is rewritten only after a barrier has passed since
+// its last read.
+constexpr int GR_NS = 3, GR_SBUF = 3;
+constexpr int GR_LOADS = 2 + 8;   // code loads per wave per stage
+
+template <int SB>
+struct GRingSmem {
+  uint4 a[GR_NS][BM * ARC];
+  uint4 w[GR_NS][BN * WRC];
+  uint32_t as[GR_SBUF][BM * SB / 4];
+  int tile_info[4];
+};
+
+template <int SB>
+__global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
+    const int32_t* __restrict__ off, const uint16_t* __restrict__ W, uint16_t* __restrict__ C,
+    int G, int M, int N, int K, int tiles_n) {
+  constexpr int U = SB / 4;                  // steps per scale load
+  __shared__ GRingSmem<SB> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // n-tile-major order: consecutive tiles (kept on one XCD by xcd_remap) are
+  // the m-tiles of one W column panel, so each group's W panel is fetched
+  // from HBM about once and re-read from L2; A (small) is shared through the
+  // infinity cache across panels.
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int mtiles = gridDim.x / tiles_n;
+  const int nt = t / mtiles, mt = t - nt * mtiles;
+  if (wave == 0) find_tile(off, G, mt, lane, sm.tile_info);
+  __syncthreads();
+  const int grp = sm.tile_info[0];
+  if (grp < 0) return;                      // uniform over the workgroup
+  // Offsets are a documented precondition; clamping keeps even malformed
+  // ones inside the A and C buffers.
+  const int r0 = min(max(sm.tile_info[1], 0), M), r1 = min(max(sm.tile_info[2], r0), M);
+  const int n0 = nt * BN;
+  const int KT = K / BK;                    // a positive multiple of U
+  const int KH = K / 2, KB = K / 16;
+  const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
+  const rsrc4_t ra = make_rsrc4(A + (int64_t)r0 * KH, rows_a * KH);
+  const rsrc4_t rsa = make_rsrc4(As + (int64_t)r0 * KB, rows_a * KB);
+  const rsrc4_t rw = make_rsrc4(W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+
+  // Load geometry.  A instruction u covers rows 32 (2 wave + u) .. +31 (two
+  // lanes per row); W instruction u covers rows 8 (8 wave + u) .. +7 (eight
+  // lanes per row).  Each lane fetches the global chunk that the swizzle puts
+  // in its LDS slot.
+  int a_off[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 32 * (2 * wave + u) + (lane >> 1);
+    a_off[u] = row * KH + (((lane & 1) ^ ((row >> 3) & 1)) * 16);
+  }
+  int w_off[2];   // even and odd u differ in the swizzle; rows step by 16 per pair
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 8 * (8 * wave + u) + (lane >> 3);
+    w_off[u] = row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
+  }
+  const int s_off = (64 * wave + lane) * KB;
+
+  auto issue = [&](int st, auto WITH_SCALES) {
+    const int slot = st % GR_NS;
+    const bool live = st < KT;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      dma_x4(ra, lds_addr(&sm.a[slot][64 * (2 * wave + u)]), live ? a_off[u] + st * AROWB : OOB);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      dma_x4(rw, lds_addr(&sm.w[slot][64 * (8 * wave + u)]),
+             live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
+    if (decltype(WITH_SCALES)::value) {
+      const int sbuf = (st / U) % GR_SBUF;
+      const int soff = live ? s_off + (st / U) * SB : OOB;
+      if (SB == 16) dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
+      else dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+    }
+  };
+
+  // Wave w computes rows [64 w, 64 w + 64) x all 256 columns: 2 x 8 MFMA
+  // tiles.  Each A row is then dequantised by exactly one wave (the BF16
+  // expansion is the kernel's VALU cost); the W fragments, which need no
+  // arithmetic, are read from LDS by all four waves.
+  const int r = lane & 31, g = lane >> 5;
+
+  struct AFrag {
+    uint4 c[2];
+    float s[2][2], m[2][2];
+  };
+  // A codes and decoded scales of stage st for this lane's 2 row fragments.
+  // The step's 4 scale bytes are dword `in` of the row's SB-byte entry; lane
+  // g takes bytes 2g and 2g + 1 (its two 16-element blocks).
+  auto read_a = [&](int st, auto INC, AFrag& f) {
+    constexpr int in = decltype(INC)::value;
+    const int slot = st % GR_NS, sbuf = (st / U) % GR_SBUF;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wave * 64 + i * 32 + r;
+      f.c[i] = sm.a[slot][aswz(row, g)];
+      const uint32_t word = sm.as[sbuf][row * (SB / 4) + in] >> (16 * g);
+      const v2f sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);   // exact E4M3
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        f.s[i][b] = sv[b];
+        f.m[i][b] = scale_mantissa_f32(sv[b]);
+      }
+    }
+  };
+  auto read_w = [&](int st, int sp, v8bf* bv) {
+    const int slot = st % GR_NS;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint4 q = sm.w[slot][wswz(j * 32 + r, 4 * g + sp)];
+      __builtin_memcpy(&bv[j], &q, 16);
+    }
+  };
+  auto dequant = [&](const AFrag& f, int sp, v8bf* av) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t d = sp == 0 ? f.c[i].x : sp == 1 ? f.c[i].y : sp == 2 ? f.c[i].z : f.c[i].w;
+      av[i] = dequant8_bf16(d, f.s[i][sp >> 1], f.m[i][sp >> 1]);
+    }
+  };
+
+  v16f acc[2][8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = v16f{};
+  auto mfmas = [&](const v8bf* av, const v8bf* bv) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+  };
+  auto interleave = [] {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // 4 VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+    }
+  };
+  auto loads_of = [](int s_mod) { return GR_LOADS + (s_mod == 0 ? 1 : 0); };
+
+  AFrag fa[2];
+  v8bf av[2][2], bv[2][8];
+  // Step kt, kt % U == IN (static); fa[CUR] holds stage kt's A data, and
+  // av[0] / bv[0] its sub-step 0 operands.
+  auto step = [&](int kt, auto INC) {
+    constexpr int IN = decltype(INC)::value;
+    constexpr int CUR = IN & 1;
+    constexpr int AFTER = loads_of((IN + 2) % U);   // stage kt+2 stays in flight
+    issue(kt + 2, std::integral_constant<bool, ((IN + 2) % U) == 0>{});
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(av[0], bv[0]);
+    read_w(kt, 1, bv[1]);
+    dequant(fa[CUR], 1, av[1]);
+    interleave();
+    mfmas(av[1], bv[1]);
+    read_w(kt, 2, bv[0]);
+    dequant(fa[CUR], 2, av[0]);
+    interleave();
+    mfmas(av[0], bv[0]);
+    read_w(kt, 3, bv[1]);
+    dequant(fa[CUR], 3, av[1]);
+    interleave();
+    wait_vm_barrier<AFTER>();         // stage kt+1 landed
+    read_a(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, fa[CUR ^ 1]);
+    mfmas(av[1], bv[1]);
+    read_w(kt + 1, 0, bv[0]);
+    dequant(fa[CUR ^ 1], 0, av[0]);
+    interleave();
+  };
+
+  issue(0, std::true_type{});
+  issue(1, std::integral_constant<bool, (1 % U) == 0>{});
+  wait_vm_barrier<loads_of(1 % U)>();
+  read_a(0, std::integral_constant<int, 0>{}, fa[0]);
+  read_w(0, 0, bv[0]);
+  dequant(fa[0], 0, av[0]);
+  // U is 1 or 4; the body below covers 2 steps when U == 1 so that the fa
+  // double buffer index stays static.
+  if constexpr (U == 1) {
+    for (int kt = 0; kt < KT; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      // second step of the pair: same code with the buffers swapped
+      constexpr int IN = 1;
+      issue(kt + 3, std::true_type{});
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(av[0], bv[0]);
+      read_w(kt + 1, 1, bv[1]);
+      dequant(fa[1], 1, av[1]);
+      interleave();
+      mfmas(av[1], bv[1]);
+      read_w(kt + 1, 2, bv[0]);
+      dequant(fa[1], 2, av[0]);
+      interleave();
+      mfmas(av[0], bv[0]);
+      read_w(kt + 1, 3, bv[1]);
+      dequant(fa[1], 3, av[1]);
+      interleave();
+      wait_vm_barrier<loads_of(0)>();
+      read_a(kt + 2, std::integral_constant<int, 0>{}, fa[0]);
+      mfmas(av[1], bv[1]);
+      read_w(kt + 2, 0, bv[0]);
+      dequant(fa[0], 0, av[0]);
+      interleave();
+      (void)IN;
+    }
+  } else {
+    for (int kt = 0; kt < KT; kt += U) {
+      static_for<0, U>([&](auto IC) { step(kt + decltype(IC)::value, IC); });
+    }
+  }
+
+  // Epilogue: C rows r0..r1 of this group, scaled by the tensor scale.
+  const float alpha = *Ats;
+  if (r0 + BM <= r1 && n0 + BN <= N) {
+    uint16_t* cw = C + (int64_t)(r0 + wave * 64 + g * 4) * N + n0 + r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] =
+              (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int col = n0 + j * 32 + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = r0 + wave * 64 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          if (row < r1 && col < N)
+            C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+        }
+      }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
@@ -218,14 +476,16 @@ hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
                           hipStream_t stream) {
   const int tiles_n = (int)ceil_div(n, BN);
   const int64_t mtiles_max = m_total / BM + num_groups;   // >= sum_g ceil(c_g / BM)
-  if (k % 64 == 0)
-    hipLaunchKernelGGL(grouped_kernel<true>, dim3((unsigned)(mtiles_max * tiles_n)), dim3(NT), 0,
-                       stream, a, as, ats, offsets, w, c, num_groups, (int)m_total, (int)n, (int)k,
-                       tiles_n);
+  const dim3 grid((unsigned)(mtiles_max * tiles_n));
+  if (k % 256 == 0 && k > 0)
+    hipLaunchKernelGGL(grouped_ring_kernel<16>, grid, dim3(NT), 0, stream, a, as, ats, offsets, w, c,
+                       num_groups, (int)m_total, (int)n, (int)k, tiles_n);
+  else if (k % 64 == 0 && k > 0)
+    hipLaunchKernelGGL(grouped_ring_kernel<4>, grid, dim3(NT), 0, stream, a, as, ats, offsets, w, c,
+                       num_groups, (int)m_total, (int)n, (int)k, tiles_n);
   else
-    hipLaunchKernelGGL(grouped_kernel<false>, dim3((unsigned)(mtiles_max * tiles_n)), dim3(NT), 0,
-                       stream, a, as, ats, offsets, w, c, num_groups, (int)m_total, (int)n, (int)k,
-                       tiles_n);
+    hipLaunchKernelGGL(grouped_kernel<false>, grid, dim3(NT), 0, stream, a, as, ats, offsets, w, c,
+                       num_groups, (int)m_total, (int)n, (int)k, tiles_n);
   return hipGetLastError();
 }
 

@@ -154,7 +154,8 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 // Consumer c = (tile group g = c % TP, K split h = c / TP) owns the NT = 4/TP
 // W tiles of group g and, in stage s, block KS s + h.  It loads its W codes
 // straight from HBM into registers, RING stages ahead, dequantises them exactly
-// to BF16 and runs 16x16x32 BF16 MFMAs against X fragments from LDS.
+// to BF16 (dequant2_bf16) and runs 16x16x32 BF16 MFMAs against X fragments
+// from LDS.
 // The producers direct-load each stage's X blocks (and, when K % 256 == 0,
 // the stage's scales) into an NSLOT-deep LDS ring, NSLOT - 1 stages ahead.
 // Producers and consumers are separate waves so that the deep weight stream
@@ -174,15 +175,6 @@ struct SkStage {
   uint4 x[KS][MT * 16];    // [block][row m: 16 chunks of 16 B; chunk c at c ^ (m & 15)]
   uint4 s[64 * KS / 2];    // W scales of the stage: row r at bytes [8 KS r, 8 KS r + 8 KS)
 };
-
-// Exact BF16 pair from two E2M1 codes (byte J of `codes`) and an E4M3 scale
-// s = 2^E (1 + f): the conversion applies 2^E, one FP32 multiply each applies
-// (1 + f) (both exact), and a byte permute packs the high halves.
-template <int J>
-__device__ __forceinline__ uint32_t dequant_pair_bf16(uint32_t codes, float s, float mant) {
-  const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, s, J);
-  return __builtin_amdgcn_perm(__float_as_uint(p[1] * mant), __float_as_uint(p[0] * mant), 0x07060302u);
-}
 
 template <int MT, int KS, int NSLOT, bool SDMA, int P>
 __device__ __forceinline__ void sk_produce(SkStage<MT, KS>* st, const uint16_t* X, const uint8_t* Ws, int m0,
@@ -299,8 +291,8 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
           for (int il = 0; il < NT; ++il) {
             const uint32_t d = sp == 0 ? wr[B][il].x : sp == 1 ? wr[B][il].y : sp == 2 ? wr[B][il].z : wr[B][il].w;
             const float sv = sc[il][sp >> 1], mv = mn[il][sp >> 1];
-            const uint32_t w4[4] = {dequant_pair_bf16<0>(d, sv, mv), dequant_pair_bf16<1>(d, sv, mv),
-                                    dequant_pair_bf16<2>(d, sv, mv), dequant_pair_bf16<3>(d, sv, mv)};
+            const uint32_t w4[4] = {dequant2_bf16<0>(d, sv, mv), dequant2_bf16<1>(d, sv, mv),
+                                    dequant2_bf16<2>(d, sv, mv), dequant2_bf16<3>(d, sv, mv)};
             __builtin_memcpy(&wv[il], w4, 16);
           }
 #pragma unroll

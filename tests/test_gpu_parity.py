@@ -277,6 +277,8 @@ def _gpu_grouped(qa, off, w, k):
     ([257, 0, 256, 255], 260, 96),
     ([1] * 40, 33, 32),
     ([600, 0, 0, 900], 512, 256),
+    ([77, 256], 260, 320),                 # odd number of 64-element K steps
+    ([512, 256, 0, 300], 512, 1280),       # whole 256-row tiles; 16-byte scale batches
 ])
 def test_grouped_shapes(gpu_lib, counts, n, k):
     qa, off, w = _grouped_case(counts, n, k, sum(counts) + n + k)
