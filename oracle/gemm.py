@@ -72,6 +72,23 @@ def gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, rows=None):
     return c * st, t * st
 
 
+def dequant_mxfp4(codes, scales) -> np.ndarray:
+    """x_hat = e2m1(code) * 2**(scale - 127), exactly, float64 [R, K]."""
+    c = unpack_nibbles(codes)
+    R, K = c.shape
+    s = decode_e8m0(scales)
+    assert s.shape == (R, K // 32)
+    return decode_e2m1(c) * np.repeat(s, 32, axis=1)
+
+
+def gemm_mxfp4(a_codes, a_scales, b_codes, b_scales, rows=None):
+    """MXFP4 x MXFP4: returns (C_ref, T)."""
+    a_codes, a_scales = np.asarray(a_codes), np.asarray(a_scales)
+    if rows is not None:
+        a_codes, a_scales = a_codes[rows], a_scales[rows]
+    return _matmul_and_mag(dequant_mxfp4(a_codes, a_scales), dequant_mxfp4(b_codes, b_scales))
+
+
 def gemm_mxfp8(a_codes, a_scales, b_codes, b_scales, rows=None):
     """MXFP8 x MXFP8: returns (C_ref, T)."""
     a_codes, a_scales = np.asarray(a_codes), np.asarray(a_scales)

@@ -1,4 +1,4 @@
-"""NVFP4 and MXFP8 quantizers (vectorised numpy).
+"""NVFP4, MXFP8 and MXFP4 quantizers (vectorised numpy).
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__``).
 
@@ -30,6 +30,7 @@ from .formats import (decode_e4m3, encode_e2m1_mag, encode_e4m3_mag,
 F32 = np.float32
 NVFP4_BLOCK = 16
 MXFP8_BLOCK = 32
+MXFP4_BLOCK = 32
 E2M1_MAX = F32(6.0)
 E4M3_MAX = F32(448.0)
 
@@ -77,24 +78,36 @@ def quantize_nvfp4(x, tensor_scale=None):
     return pack_nibbles(codes), scale_codes.astype(np.uint8), F32(s_t)
 
 
-def mxfp8_block_exponent(bamax) -> np.ndarray:
-    """e = min{ e in Z : 448 * 2**e >= bamax }, clamped to [-127, 127].
+def mx_block_exponent(bamax, top) -> np.ndarray:
+    """e = min{ e in Z : top * 2**e >= bamax }, clamped to [-127, 127], where
+    `top` is the element format's largest value (448 for E4M3, 6 for E2M1).
 
-    This is the exact value of ceil(log2(bamax / 448)).  The search starts from
-    the binary exponent of bamax (448 = 0.875 * 2**9, so the answer is E-9 or
-    E-8 where bamax = f * 2**E, f in [0.5, 1)) and is then checked against the
-    definition in exact float64 arithmetic.  bamax == 0 gives -127.
+    This is the exact value of ceil(log2(bamax / top)).  The search starts
+    below the answer (from the binary exponents of bamax and top) and walks up
+    to the least e meeting the definition, checked in exact float64
+    arithmetic.  bamax == 0 gives -127.
     """
     b = np.asarray(bamax, dtype=np.float64)
     _, E = np.frexp(b)
-    e = E.astype(np.int64) - 10
+    _, Et = np.frexp(top)
+    e = E.astype(np.int64) - int(Et) - 1
     for _ in range(3):  # walk up to the least e meeting the definition
-        e = np.where(448.0 * np.ldexp(1.0, e) >= b, e, e + 1)
-    ok = 448.0 * np.ldexp(1.0, e) >= b
-    minimal = ~(448.0 * np.ldexp(1.0, e - 1) >= b)
+        e = np.where(top * np.ldexp(1.0, e) >= b, e, e + 1)
+    ok = top * np.ldexp(1.0, e) >= b
+    minimal = ~(top * np.ldexp(1.0, e - 1) >= b)
     assert np.all(ok & (minimal | (b == 0)))
     e = np.where(b == 0, -127, e)
     return np.clip(e, -127, 127)
+
+
+def mxfp8_block_exponent(bamax) -> np.ndarray:
+    """e = min{ e in Z : 448 * 2**e >= bamax }, clamped to [-127, 127]."""
+    return mx_block_exponent(bamax, 448.0)
+
+
+def mxfp4_block_exponent(bamax) -> np.ndarray:
+    """e = min{ e in Z : 6 * 2**e >= bamax }, clamped to [-127, 127]."""
+    return mx_block_exponent(bamax, 6.0)
 
 
 def quantize_mxfp8(x):
@@ -118,3 +131,28 @@ def quantize_mxfp8(x):
     q = blocks * np.ldexp(1.0, -e)[:, :, None]
     codes = (signbit_u8(blocks) << 7) | encode_e4m3_mag(np.abs(q))
     return codes.reshape(R, K).astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def quantize_mxfp4(x):
+    """MXFP4-quantize X[R, K] (K % 32 == 0).
+
+    Returns (codes uint8 [R, K/2], scales uint8 [R, K/32]):
+
+    1. per 32-element block: bamax = max |x|; e = ceil(log2(bamax / 6))
+       computed exactly (``mxfp4_block_exponent``); scale code = e + 127
+       (E8M0).  This is the MXFP8 rule with E2M1's largest value, 6, in place
+       of 448, so no element saturates.
+    2. q = x * 2**-e (exact: a power-of-two scaling of an FP32 value, done in
+       float64); code = signbit(x) << 3 | E2M1_RNE(|q|).
+    3. byte j of a row holds element 2j in the low nibble, 2j+1 in the high.
+    """
+    x = np.ascontiguousarray(x, dtype=F32)
+    assert x.ndim == 2 and x.shape[1] % MXFP4_BLOCK == 0
+    assert np.all(np.isfinite(x)), "inputs must be finite"
+    R, K = x.shape
+    blocks = x.reshape(R, K // MXFP4_BLOCK, MXFP4_BLOCK).astype(np.float64)
+    bamax = np.max(np.abs(blocks), axis=2) if x.size else np.zeros((R, 0))
+    e = mxfp4_block_exponent(bamax)
+    q = blocks * np.ldexp(1.0, -e)[:, :, None]
+    codes = (signbit_u8(blocks) << 3) | encode_e2m1_mag(np.abs(q))
+    return pack_nibbles(codes.reshape(R, K).astype(np.uint8)), (e + 127).astype(np.uint8)

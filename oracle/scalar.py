@@ -137,3 +137,26 @@ def quantize_mxfp8_scalar(rows):
         codes.append(rc)
         scales.append(rs)
     return codes, scales
+
+
+def quantize_mxfp4_scalar(rows):
+    """rows: list of lists of FP32-valued floats, len % 32 == 0.
+    Returns (element codes, scale codes) as lists of lists of ints; element
+    codes are unpacked 4-bit values (sign << 3 | E2M1 magnitude)."""
+    codes, scales = [], []
+    for r in rows:
+        rc, rs = [], []
+        for b0 in range(0, len(r), 32):
+            blk = [f32(v) for v in r[b0:b0 + 32]]
+            signs = [_signbit(v) for v in r[b0:b0 + 32]]
+            bamax = max(abs(v) for v in blk)
+            e = -127
+            while bamax != 0 and 6 * TWO ** e < bamax:  # least e with 6 * 2**e >= bamax
+                e += 1
+            e = min(e, 127)
+            rs.append(e + 127)
+            for v, sg in zip(blk, signs):
+                rc.append((sg << 3) | e2m1_encode_mag(abs(v * TWO ** -e)))
+        codes.append(rc)
+        scales.append(rs)
+    return codes, scales

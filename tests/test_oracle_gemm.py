@@ -34,6 +34,13 @@ def _exact_mxfp8(codes, scales):
              for k in range(K)] for r in range(R)]
 
 
+def _exact_mxfp4(codes, scales):
+    un = F.unpack_nibbles(codes)
+    R, K = un.shape
+    return [[S.e2m1_frac(int(un[r, k])) * Fraction(2) ** (int(scales[r, k // 32]) - 127)
+             for k in range(K)] for r in range(R)]
+
+
 def _exact_gemm(a, b):
     return [[sum((x * y for x, y in zip(ra, rb)), Fraction(0)) for rb in b] for ra in a]
 
@@ -95,6 +102,53 @@ def test_nvfp4_one_hot_rows_select_scaled_b():
     scales = np.full((2, K // 16), 0x38, np.uint8)       # 1.0
     c, _ = G.gemm_nvfp4(F.pack_nibbles(codes), scales, np.float32(1.0), *b)
     assert np.array_equal(c[0], bd[:, 17]) and np.array_equal(c[1], -2.0 * bd[:, 50])
+
+
+def test_mxfp4_gemm_equals_exact_bruteforce():
+    xa = synth.normal_f32((4, 96), 43)
+    xb = synth.normal_f32((4, 96), 44)
+    xa[2] *= np.float32(1e3)
+    xb[:, 32:64] *= np.float32(1e-2)
+    a, b = Q.quantize_mxfp4(xa), Q.quantize_mxfp4(xb)
+    c, t = G.gemm_mxfp4(*a, *b)
+    ea, eb = _exact_mxfp4(*a), _exact_mxfp4(*b)
+    ce, te = _exact_gemm(ea, eb), _exact_mag(ea, eb)
+    for i in range(4):
+        for j in range(4):
+            assert abs(Fraction(float(c[i, j])) - ce[i][j]) <= Fraction(1e-12) * te[i][j]
+            assert abs(Fraction(float(t[i, j])) - te[i][j]) <= Fraction(1e-12) * te[i][j]
+
+
+def test_mxfp4_constant_codes_and_one_hot_closed_forms():
+    K = 128
+    # constant codes: every A element 1.5 (code 3) at scale 2**2, every B element -0.5 (code 9) at 2**-3
+    a = (F.pack_nibbles(np.full((2, K), 3, np.uint8)), np.full((2, K // 32), 129, np.uint8))
+    b = (F.pack_nibbles(np.full((3, K), 9, np.uint8)), np.full((3, K // 32), 124, np.uint8))
+    c, t = G.gemm_mxfp4(*a, *b)
+    assert np.all(c == K * 1.5 * 4 * -0.5 / 8) and np.all(t == -c)
+    # one-hot A rows pick one dequantised element of each B row
+    xb = synth.normal_f32((5, K), 45)
+    b = Q.quantize_mxfp4(xb)
+    bd = G.dequant_mxfp4(*b)
+    codes = np.zeros((2, K), np.uint8)
+    codes[0, 70] = 2                                      # +1.0
+    codes[1, 5] = 8 | 4                                   # -2.0
+    a = (F.pack_nibbles(codes), np.full((2, K // 32), 127, np.uint8))
+    c, _ = G.gemm_mxfp4(*a, *b)
+    assert np.array_equal(c[0], bd[:, 70]) and np.array_equal(c[1], -2.0 * bd[:, 5])
+
+
+def test_planted_mxfp4_scale_index_fails_the_bruteforce_pin(monkeypatch):
+    xa, xb = synth.normal_f32((4, 96), 46), synth.normal_f32((4, 96), 47)
+    xa[:, 32:64] *= np.float32(50.0)
+    a, b = Q.quantize_mxfp4(xa), Q.quantize_mxfp4(xb)
+    ea, eb = _exact_mxfp4(*a), _exact_mxfp4(*b)
+    ce, te = _exact_gemm(ea, eb), _exact_mag(ea, eb)
+    orig = G.dequant_mxfp4
+    monkeypatch.setattr(G, "dequant_mxfp4", lambda codes, scales: orig(codes, np.roll(scales, 1, axis=1)))
+    c, _ = G.gemm_mxfp4(*a, *b)
+    worst = max(abs(Fraction(float(c[i, j])) - ce[i][j]) / te[i][j] for i in range(4) for j in range(4))
+    assert worst > Fraction(1e-6)
 
 
 def test_mxfp8_block_permutation_invariance():

@@ -1,4 +1,4 @@
-"""Pins for the oracle's NVFP4 and MXFP8 quantizers (CPU only).
+"""Pins for the oracle's NVFP4, MXFP8 and MXFP4 quantizers (CPU only).
 
 The quantizers are pinned by properties that the recipe and the formats fix
 (what the tensor-absmax element and each block maximum must encode to, error
@@ -13,7 +13,7 @@ from block_scaled_precision_bsgemm_amd import synth
 from oracle import formats as F
 from oracle import quantize as Q
 from oracle import scalar as S
-from oracle.gemm import dequant_mxfp8, dequant_nvfp4
+from oracle.gemm import dequant_mxfp4, dequant_mxfp8, dequant_nvfp4
 
 
 def _nvfp4_data(seed, rows=64, k=256):
@@ -214,3 +214,92 @@ def test_nvfp4_random_blocks_vector_equals_scalar_many():
     assert np.array_equal(F.unpack_nibbles(codes), np.array(sc, dtype=np.uint8))
     assert np.array_equal(scales, np.array(ss, dtype=np.uint8))
     assert (scales < 8).any() and (scales == 0x7E).any()
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def test_mxfp4_scale_minimal_and_block_max_in_range():
+    x = synth.normal_f32((64, 512), 61)
+    x[3] *= np.float32(1e-30)
+    x[4] *= np.float32(1e30)
+    codes, scales = Q.quantize_mxfp4(x)
+    assert codes.shape == (64, 256) and scales.shape == (64, 16)
+    bamax = np.abs(x.astype(np.float64)).reshape(64, -1, 32).max(2)
+    e = scales.astype(np.int64) - 127
+    assert np.all(6.0 * np.ldexp(1.0, e) >= bamax)
+    assert np.all(6.0 * np.ldexp(1.0, e - 1) < bamax)
+    xh = dequant_mxfp4(codes, scales).reshape(64, -1, 32)
+    qmax = np.abs(xh).max(2) / np.ldexp(1.0, e)
+    # bamax / 2**e lies in (3, 6]; RNE onto the E2M1 grid gives 3, 4 or 6
+    assert np.all(np.isin(qmax, [3.0, 4.0, 6.0]))
+
+
+def test_mxfp4_elementwise_rounding_to_nearest():
+    x = synth.normal_f32((16, 256), 62)
+    codes, scales = Q.quantize_mxfp4(x)
+    e = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    q = x.astype(np.float64) * np.ldexp(1.0, -e)
+    xh = dequant_mxfp4(codes, scales) * np.ldexp(1.0, -e)
+    grid = F.E2M1_TABLE[:8]
+    # the chosen value is a grid point at the least distance from q
+    dist = np.abs(np.abs(q)[..., None] - grid).min(-1)
+    assert np.all(np.abs(np.abs(xh) - np.abs(q)) == dist)
+    assert np.all((np.sign(xh) == np.sign(q)) | (xh == 0))
+
+
+def test_mxfp4_zero_tiny_and_tie_blocks():
+    x = np.zeros((1, 128), np.float32)
+    x[0, 1] = -0.0
+    x[0, 32] = np.float32(1e-39)                         # float32 subnormal
+    x[0, 64:68] = [4.0, 0.25, 0.75, 5.0]                 # block max 5: 2**-e = 1
+    x[0, 96:100] = [7.0, -5.0, 2.5, 1.25]                # block max 7: 2**-e = 0.5 -> 3.5, 2.5, 1.25, 0.625
+    codes, scales = Q.quantize_mxfp4(x)
+    un = F.unpack_nibbles(codes)[0]
+    assert scales[0, 0] == 0 and un[1] == 8 and un[:32].sum() == 8   # -0.0 keeps its sign bit
+    assert scales[0, 1] == 0                             # clamped at 2**-127
+    assert scales[0, 2] == 127                           # 6 * 2**0 >= 5 > 6 * 2**-1
+    # 4 -> 4; ties: 0.25 -> 0, 0.75 -> 1.0, 5 -> 4 (even codes 0, 2, 6)
+    assert un[64] == 6 and un[65] == 0 and un[66] == 2 and un[67] == 6
+    assert scales[0, 3] == 128                           # 6 * 2 >= 7 > 6
+    assert un[96] == 6 and un[97] == 8 | 4 and un[98] == 2 and un[99] == 1   # 3.5->4, 2.5->2, 1.25->1, 0.625->0.5
+
+
+def test_mxfp4_roundtrip_and_idempotence():
+    rng = np.random.Generator(np.random.PCG64(18))
+    rows, k = 16, 256
+    codes = rng.integers(0, 16, size=(rows, k)).astype(np.uint8)
+    cb = codes.reshape(rows, -1, 32)
+    pos = rng.integers(0, 32, size=(rows, k // 32))
+    mags = cb & 0x7
+    np.put_along_axis(mags, pos[..., None], 7, 2)       # every block holds a +-6
+    cb = (cb & 0x8) | mags
+    codes = cb.reshape(rows, k)
+    scales = rng.integers(100, 150, size=(rows, k // 32)).astype(np.uint8)
+    packed = F.pack_nibbles(codes)
+    x = dequant_mxfp4(packed, scales)
+    c2, s2 = Q.quantize_mxfp4(x.astype(np.float32))
+    assert np.array_equal(s2, scales) and np.array_equal(c2, packed)
+    y = synth.normal_f32((8, 128), 14)
+    c, s = Q.quantize_mxfp4(y)
+    d1 = dequant_mxfp4(c, s)
+    c3, s3 = Q.quantize_mxfp4(d1.astype(np.float32))
+    assert np.array_equal(dequant_mxfp4(c3, s3), d1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_mxfp4_vector_equals_scalar(seed):
+    x = _tricky_rows(seed + 20, 8, 64)
+    codes, scales = Q.quantize_mxfp4(x)
+    sc, ss = S.quantize_mxfp4_scalar(x.tolist())
+    assert np.array_equal(F.unpack_nibbles(codes), np.array(sc, dtype=np.uint8))
+    assert np.array_equal(scales, np.array(ss, dtype=np.uint8))
+
+
+def test_mxfp4_random_blocks_vector_equals_scalar_many():
+    """~10^4 blocks spanning 2^-40 .. 2^40 in magnitude."""
+    r = np.random.Generator(np.random.PCG64(78))
+    x = (r.standard_normal((40, 32 * 8)) * np.exp2(r.uniform(-40, 40, (40, 8)).repeat(32, 1))).astype(np.float32)
+    codes, scales = Q.quantize_mxfp4(x)
+    sc, ss = S.quantize_mxfp4_scalar(x.tolist())
+    assert np.array_equal(F.unpack_nibbles(codes), np.array(sc, dtype=np.uint8))
+    assert np.array_equal(scales, np.array(ss, dtype=np.uint8))
