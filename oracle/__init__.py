@@ -9,14 +9,14 @@ What it computes, in plain slow code, decoding every code exactly to float64:
 
 * ``formats``  -- the element and scale formats (E2M1, E4M3, E8M0, BF16):
   exact decoders and round-to-nearest-even, saturating encoders.
-* ``quantize`` -- the NVFP4 and MXFP8 quantizers (vectorised numpy, FP32
-  arithmetic emulated with numpy float32).
+* ``quantize`` -- the NVFP4, MXFP8 and MXFP4 quantizers (vectorised numpy,
+  FP32 arithmetic emulated with numpy float32).
 * ``scalar``   -- a second, independent scalar quantizer in pure Python with
   ``fractions.Fraction`` and its own FP32 rounding, used only to cross-check
   ``quantize``.
 * ``gemm``     -- the block-scaled GEMM references (NVFP4 x NVFP4, MXFP8 x MXFP8,
-  grouped NVFP4 x BF16, NVFP4-weight x BF16-activation), the magnitude sum
-  T[m,n] = sum_k |a_k b_k| and the per-element acceptance test.
+  MXFP4 x MXFP4, grouped NVFP4 x BF16, NVFP4-weight x BF16-activation), the
+  magnitude sum T[m,n] = sum_k |a_k b_k| and the per-element acceptance test.
 
 Sources.  The pages this library follows name the formats but define none of
 their arithmetic:
@@ -37,7 +37,8 @@ The bit layouts follow the OCP Microscaling Formats (MX) v1.0 specification
 (E2M1, E4M3 "FN", E8M0) and NVIDIA's published NVFP4 description (E2M1 values,
 one E4M3 scale per 16 elements, one FP32 per-tensor scale).  The quantizer
 recipes (tensor scale = absmax / (6 * 448), block scale = (block absmax / 6) /
-tensor scale, MXFP8 block exponent = ceil(log2(block absmax / 448))) are the
+tensor scale, MXFP8 block exponent = ceil(log2(block absmax / 448)), MXFP4
+block exponent = ceil(log2(block absmax / 6))) are the
 problem statement of this library; every reading taken where that statement is
 silent is listed in the docstring that takes it.
 """
