@@ -15,9 +15,10 @@ The same JSON line carries:
     fraction of the FP4 peak too.
   - ``cpu_baseline``: the CPU oracle's GEMM timed on a bounded sample.
   - ``rows``: the other parts of the hot path, each timed with HIP events:
-    the MXFP8 GEMM at 16384^3 and 4096^3, the ragged grouped NVFP4 x BF16
+    the MXFP8 GEMM at 16384^3 and 4096^3, the MXFP4 GEMM at 16384^3 (on
+    the MXFP8 row's N(0, 1) inputs), the ragged grouped NVFP4 x BF16
     GEMM, the W4A16 GEMM at M = 1, 16, 64, 256 with weights rotated through
-    16 copies (cold cache), the two quantizers at 16384^2, and the
+    16 copies (cold cache), the three quantizers at 16384^2, and the
     256 x 256 x 128 NVFP4 GEMM latency.
 
 ``--only headline`` runs just the headline GEMM (for profiler runs).  It adds
@@ -180,7 +181,18 @@ def main():
     c8b, s8b = L.bsgemm_quantize_mxfp8(dmb)
     ms = time_events(lambda i: L.bsgemm_quantize_mxfp8(dma, c8a, s8a), 5, 2)
     rows["quantize_mxfp8_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (4 + 1.03125) / (ms * 1e-3) / 1e9, 1)}
+    # MXFP4 from the same N(0, 1) 16k inputs
+    c4a, s4a = L.bsgemm_quantize_mxfp4(dma)
+    c4b, s4b = L.bsgemm_quantize_mxfp4(dmb)
+    ms = time_events(lambda i: L.bsgemm_quantize_mxfp4(dma, c4a, s4a), 5, 2)
+    rows["quantize_mxfp4_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (4 + 0.53125) / (ms * 1e-3) / 1e9, 1)}
     del dma, dmb
+    c16 = torch.empty((M, N), dtype=torch.int16, device=dev)
+    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP4, c4a, s4a, None, c4b, s4b, None, K, c=c16),
+                     max(3, args.steps // 2), 2)
+    tf = flops / (ms * 1e-3) / 1e12
+    rows["mxfp4_gemm_16384"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp4_peak": round(tf / PEAK["fp4"], 4)}
+    del c4a, s4a, c4b, s4b, c16
 
     # --------------------------------------------------- MXFP8 16k^3 and 4k^3
     c16 = torch.empty((M, N), dtype=torch.int16, device=dev)

@@ -136,7 +136,7 @@ int check_limits(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k) {
 
 extern "C" {
 
-int bsgemm_version(void) { return 100; }   // 0.1.0
+int bsgemm_version(void) { return 200; }   // 0.2.0: MXFP4
 
 const char* bsgemm_status_string(int status) {
   switch (status) {
@@ -201,6 +201,30 @@ int bsgemm_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* code
   }
 }
 
+int bsgemm_quantize_mxfp4(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                          uint8_t* scales, void* stream) {
+  static const char* fn = "bsgemm_quantize_mxfp4";
+  try {
+    if (rows < 0 || k < 0) return fail(BSGEMM_ERR_INVALID_ARG, "%s: negative size", fn);
+    const int64_t n = rows * k;
+    REQUIRE_PTR(x, n);
+    REQUIRE_PTR(codes, n);
+    REQUIRE_PTR(scales, n);
+    if (int s = check_k(fn, k)) return s;
+    REQUIRE_ALIGNED(x);
+    REQUIRE_ALIGNED(codes);
+    REQUIRE_ALIGNED(scales);
+    if (int s = check_limits(fn, rows, 0, 0)) return s;
+    int num_cus = 0;
+    if (int s = check_device(fn, &num_cus)) return s;
+    if (n == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish_launch(fn, bsg::launch_quantize_mxfp4(rows, k, x, codes, scales, st, num_cus), st);
+  } catch (...) {
+    return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
+  }
+}
+
 int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k, const uint8_t* a,
                const uint8_t* a_scales, const float* a_tscale, const uint8_t* b,
                const uint8_t* b_scales, const float* b_tscale, uint16_t* c_bf16, void* stream) {
@@ -215,9 +239,10 @@ int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k, const uint8_t* a,
     if (fmt == BSGEMM_NVFP4) {
       if (a_tscale == nullptr || b_tscale == nullptr)
         return fail(BSGEMM_ERR_INVALID_ARG, "%s: NVFP4 needs a_tscale and b_tscale", fn);
-    } else if (fmt == BSGEMM_MXFP8) {
+    } else if (fmt == BSGEMM_MXFP8 || fmt == BSGEMM_MXFP4) {
       if (a_tscale != nullptr || b_tscale != nullptr)
-        return fail(BSGEMM_ERR_UNSUPPORTED, "%s: MXFP8 takes no tensor scales (pass NULL)", fn);
+        return fail(BSGEMM_ERR_UNSUPPORTED, "%s: %s takes no tensor scales (pass NULL)", fn,
+                    fmt == BSGEMM_MXFP8 ? "MXFP8" : "MXFP4");
     } else {
       return fail(BSGEMM_ERR_UNSUPPORTED, "%s: unknown format %d", fn, fmt);
     }
@@ -233,9 +258,9 @@ int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k, const uint8_t* a,
     if (m == 0 || n == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e =
-        fmt == BSGEMM_NVFP4
-            ? bsg::launch_gemm_nvfp4(m, n, k, a, a_scales, a_tscale, b, b_scales, b_tscale, c_bf16, st)
-            : bsg::launch_gemm_mxfp8(m, n, k, a, a_scales, b, b_scales, c_bf16, st);
+        fmt == BSGEMM_NVFP4   ? bsg::launch_gemm_nvfp4(m, n, k, a, a_scales, a_tscale, b, b_scales, b_tscale, c_bf16, st)
+        : fmt == BSGEMM_MXFP8 ? bsg::launch_gemm_mxfp8(m, n, k, a, a_scales, b, b_scales, c_bf16, st)
+                              : bsg::launch_gemm_mxfp4(m, n, k, a, a_scales, b, b_scales, c_bf16, st);
     return finish_launch(fn, e, st);
   } catch (...) {
     return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);

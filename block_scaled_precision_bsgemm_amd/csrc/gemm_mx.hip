@@ -1,0 +1,528 @@
+// MX-format GEMMs (MXFP8 x MXFP8 and MXFP4 x MXFP4) on the gfx950 scaled MFMA
+// (v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// Both block formats (E4M3 or E2M1 values, one E8M0 scale per 32 K-elements)
+// are ones this MFMA consumes natively.  Each lane supplies one E8M0 byte for
+// its row and its 32-element K block, so no dequantisation happens anywhere.
+// Prior art: "Together AI Ports ThunderKittens GEMM Kernels to NVIDIA Vera
+// Rubin NVL72", section "Building the GEMM".  That page stages FP8 E4M3
+// operands through a multi-stage shared-memory ring and sweeps its depth.
+//
+// Both kernels are templated on the element format.  Everything is counted in
+// bytes of a code row: one byte holds one E4M3 element or two E2M1 elements,
+// so a 16-byte chunk is 16 (FP8) or 32 (FP4) K-elements.
+//
+// Layout of one workgroup (256 threads, 4 waves):
+//   - Output tile 256 x 256; each wave owns 128 x 128 (4 x 4 MFMA tiles of
+//     32 x 32).
+//   - Operand register layout of the 32x32x64 MFMA, checked on the device
+//     against the oracle: lane (r = l % 32, g = l / 32) holds row r, and its
+//     scale byte applies to the MFMA's 32-element K block g.
+//       FP8: dwords 0-3 = K [16g, 16g+16) of block 0, dwords 4-7 = K
+//            [32+16g, 32+16g+16) of block 1 (two 16-byte chunks);
+//       FP4: dwords 0-3 = K [32g, 32g+32), element 2j in the low nibble of
+//            byte j (one 16-byte chunk, block g whole).
+//     So an FP8 MFMA over code bytes [64s, 64s+64) takes chunks 4s+g and
+//     4s+2+g, and an FP4 MFMA over bytes [32s, 32s+32) takes chunk 2s+g.
+//     Either way the lane's scale is that of block 2s+g.
+//   - Output lane layout: lane l holds column l % 32, rows
+//     8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+#include <type_traits>
+
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace bsg {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 128, NT = 256;   // BK: code bytes per row per step
+constexpr int GROUP_M = 8;   // tile rows per rasterisation group
+
+// K-elements per code byte.
+template <bool FP4>
+constexpr int per_byte() { return FP4 ? 2 : 1; }
+
+// Tiles are uint4 arrays: the compiler then knows every access is 16-byte
+// aligned and emits single ds_read_b128 / ds_write_b128 instructions.
+constexpr int RC = BK / 16;   // 16-byte chunks per row
+template <bool FP4>
+struct Smem {
+  static constexpr int SW = per_byte<FP4>();   // scale dwords per row per step
+  uint4 a[2][BM * RC];
+  uint4 b[2][BN * RC];
+  uint32_t as[2][BM * SW];
+  uint32_t bs[2][BN * SW];
+};
+
+// 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7): any 16
+// consecutive rows reading one chunk then cover all 16 bank groups of
+// 16 bytes (two 128-byte rows per 256 bytes of banks).
+__device__ __forceinline__ int swz(int row, int chunk) { return row * RC + (chunk ^ ((row >> 1) & 7)); }
+
+// Map a linear tile index to (tile_m, tile_n): groups of GROUP_M tile rows
+// are walked column by column, so consecutive tiles share B columns and the
+// group's A rows.
+__device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = GROUP_M * tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in = t - group * per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+// Operand of one MFMA from a lane's fragment registers (lo = the first
+// 16-byte chunk, hi = the second): FP8 takes both, FP4 one.  The compiler
+// narrows an FP4 operand to its 4 used registers.
+__device__ __forceinline__ v8i frag8(const uint4& lo, const uint4& hi) {
+  return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+__device__ __forceinline__ v8i frag4(const uint4& c) {
+  return v8i{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+}
+
+// FP4 is the E2M1 source format (4) of the MFMA's cbsz/blgp fields, FP8 the
+// E4M3 one (0).
+template <bool FP4>
+constexpr int mfma_fmt() { return FP4 ? 4 : 0; }
+
+// General kernel (any K % 32 == 0): operands go HBM -> registers -> LDS,
+// double-buffered, 128 code bytes per row per step; scales come byte by byte
+// so blocks past K read as 0.
+template <bool FP4>
+__global__ __launch_bounds__(NT, 1) void mx_gemm_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  constexpr int SPS = 4 * per_byte<FP4>();   // scale bytes per row per step
+  constexpr int SW = SPS / 4;                // ... in dwords
+  __shared__ Smem<FP4> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KP = K / per_byte<FP4>();   // code bytes per row
+  const int KT = (KP + BK - 1) / BK;
+  const int KB = K / 32;
+
+  // ---- global -> register staging: thread owns chunk (tid & 7) of rows
+  //      (tid >> 3) + 32 i, i = 0..7, and the SPS scale bytes of row tid.
+  const int lc = tid & 7, lr = tid >> 3;
+  uint4 ra[8], rb[8];
+  // Per-tile buffer resources: loads past the tile's last valid row return 0.
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+  const auto ra_rsrc = make_rsrc(A + (int64_t)m0 * KP, rows_a * KP);
+  const auto rb_rsrc = make_rsrc(B + (int64_t)n0 * KP, rows_b * KP);
+  const auto sa_rsrc = make_rsrc(As + (int64_t)m0 * KB, rows_a * KB);
+  const auto sb_rsrc = make_rsrc(Bs + (int64_t)n0 * KB, rows_b * KB);
+  const int off0 = lr * KP + lc * 16;
+
+  // Loads only issue here; the scale bytes are assembled in sstore, after the
+  // MFMAs of the current step, so nothing waits on them early.
+  uint32_t sa_raw[SPS], sb_raw[SPS];
+  auto gload = [&](int kt) {
+    const int kc = kt * BK + lc * 16;
+    const int kofs = kc < KP ? kt * BK : OOB;   // KP % 16 == 0: chunks are wholly in or out
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int off = kofs == OOB ? OOB : off0 + 32 * i * KP + kofs;
+      ra[i] = buffer_load_x4(ra_rsrc, off);
+      rb[i] = buffer_load_x4(rb_rsrc, off);
+    }
+    // one offset register; bytes of blocks past K are zeroed in sstore
+    const int sbase = tid * KB + kt * SPS;
+#pragma unroll
+    for (int j = 0; j < SPS; ++j) {
+      sa_raw[j] = buffer_load_u8(sa_rsrc, sbase + j);
+      sb_raw[j] = buffer_load_u8(sb_rsrc, sbase + j);
+    }
+  };
+  // Scale bytes of blocks past K (read from the next row, or as 0 past the
+  // tile) become 0, like their codes: 2^-127 * 0 contributes nothing.
+  auto sstore = [&](int buf, int kt) {
+#pragma unroll
+    for (int j = 0; j < SPS; ++j) {
+      if (kt * SPS + j >= KB) { sa_raw[j] = 0u; sb_raw[j] = 0u; }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int row = lr + 32 * i;
+      sm.a[buf][swz(row, lc)] = ra[i];
+      sm.b[buf][swz(row, lc)] = rb[i];
+    }
+#pragma unroll
+    for (int w = 0; w < SW; ++w) {
+      const uint32_t* x = sa_raw + 4 * w;
+      const uint32_t* y = sb_raw + 4 * w;
+      sm.as[buf][tid * SW + w] = x[0] | (x[1] << 8) | (x[2] << 16) | (x[3] << 24);
+      sm.bs[buf][tid * SW + w] = y[0] | (y[1] << 8) | (y[2] << 16) | (y[3] << 24);
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+
+  if (KT > 0) {
+    gload(0);
+    sstore(0, 0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < KT) gload(kt + 1);
+    // sub-step s: one MFMA per tile over 64 K-elements, scale byte 2s + g
+#pragma unroll
+    for (int s = 0; s < SPS / 2; ++s) {
+      v8i af[4], bf[4];
+      int sa[4], sb[4];
+      const int sbyte = 2 * s + g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + r;
+        af[i] = FP4 ? frag4(sm.a[buf][swz(row, 2 * s + g)])
+                    : frag8(sm.a[buf][swz(row, 4 * s + g)], sm.a[buf][swz(row, 4 * s + 2 + g)]);
+        sa[i] = (int)((sm.as[buf][row * SW + sbyte / 4] >> (8 * (sbyte % 4))) & 0xFFu);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = wn * 128 + j * 32 + r;
+        bf[j] = FP4 ? frag4(sm.b[buf][swz(row, 2 * s + g)])
+                    : frag8(sm.b[buf][swz(row, 4 * s + g)], sm.b[buf][swz(row, 4 * s + 2 + g)]);
+        sb[j] = (int)((sm.bs[buf][row * SW + sbyte / 4] >> (8 * (sbyte % 4))) & 0xFFu);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[i], bf[j], acc[i][j], mfma_fmt<FP4>(), mfma_fmt<FP4>(), 0, sa[i], 0, sb[j]);
+    }
+    if (kt + 1 < KT) sstore(buf ^ 1, kt + 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: FP32 -> BF16 (RNE), masked stores
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = n0 + wn * 128 + j * 32 + r;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+      }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Ring kernel (K % 128 == 0): the operands stream HBM -> LDS by direct
+// loads through a 4-stage ring of 64-code-byte K steps (64 K-elements of FP8,
+// 128 of FP4), so three steps are in flight while one is computed.  The
+// pages' FP8 GEMM got its gains from the same lever: ring depth.
+//
+// Codes, per stage and operand: [256][64] bytes, 16-byte chunk c of row r at
+// c ^ ((r >> 2) & 3) (conflict-free reads).  Each wave issues 8 code loads
+// per stage (4 A, 4 B; 1 KiB = 16 rows each).
+//
+// Scales are loaded in batches.  With one lane per row, a scale load touches
+// 64 cache lines for a few bytes each, and the address path costs about one
+// clock per line.  Per-stage 4-byte scale loads cost as much as all the code
+// loads.  So one load brings SB bytes per row: the scales of U K steps (SB =
+// 16 when K % 512 == 0, else 4; a stage takes 2 scale bytes per row for FP8,
+// 4 for FP4).  That is one load per operand per wave every U stages, into a
+// ring of per-super-stage buffers.
+//
+// Per stage each wave runs 16 MFMA issues' worth of work: its 4 x 4 tiles,
+// one K64 FP8 MFMA or two K64 FP4 MFMAs each (an FP4 MFMA takes half the
+// cycles of an FP8 one, so a stage costs the same matrix-core time in both
+// formats).  The stage's fragments were read into registers during the second
+// half of the previous stage.  Halfway through the MFMAs the wave waits for
+// the next stage's loads, crosses the barrier and reads the next fragments,
+// overlapping the remaining MFMAs.  The K loop is unrolled by one
+// super-stage, so every step's load count and wait count are static.
+constexpr int RB_K = 64, RB_NS = 4, RB_ROW = RB_K / 16;   // code bytes per stage row; 4 chunks per row
+constexpr int RB_CODE_LOADS = 8;                           // code loads per wave per stage
+
+// Scale buffers per super-stage of U stages.  Stage st + 3 is issued at the
+// head of step st; the buffer it overwrites must have had its last read
+// (made in the step before the stage it serves, after that step's barrier)
+// before a barrier that precedes step st.
+template <int U>
+constexpr int ring_scale_bufs() { return U >= 4 ? 2 : (U >= 2 ? 3 : 4); }
+
+template <int SB, bool FP4>
+struct RingSmem {
+  static constexpr int U = SB / (2 * per_byte<FP4>());
+  uint4 a[RB_NS][BM * RB_ROW];
+  uint4 b[RB_NS][BN * RB_ROW];
+  uint32_t as[ring_scale_bufs<U>()][BM * SB / 4];   // [super-stage buffer][row][SB bytes]
+  uint32_t bs[ring_scale_bufs<U>()][BN * SB / 4];
+};
+
+__device__ __forceinline__ int rswz(int row, int chunk) { return row * RB_ROW + (chunk ^ ((row >> 2) & 3)); }
+
+// One stage's fragments, from chunks g and 2 + g of the lane's rows: one
+// 8-dword MFMA operand per tile (FP8), or two 4-dword ones (FP4, lo and hi).
+template <bool FP4> struct Frags;
+template <> struct Frags<false> {
+  v8i a[4], b[4];
+  int sa[4], sb[4];
+};
+template <> struct Frags<true> {
+  uint4 alo[4], ahi[4], blo[4], bhi[4];
+  int sa[4], sb[4];
+};
+
+template <int SB, bool FP4>
+__global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  using Sm = RingSmem<SB, FP4>;
+  constexpr int U = Sm::U;                        // stages per scale super-stage
+  constexpr int NSB = ring_scale_bufs<U>();
+  __shared__ Sm sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tm, tn;
+  if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
+    supertile_order(blockIdx.x, tiles_n, tm, tn);
+  else
+    raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KP = K / per_byte<FP4>();   // code bytes per row
+  const int KT = KP / RB_K;             // a positive multiple of U
+  const int KB = K / 32;
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+  const rsrc4_t ra = make_rsrc4(A + (int64_t)m0 * KP, rows_a * KP);
+  const rsrc4_t rb = make_rsrc4(B + (int64_t)n0 * KP, rows_b * KP);
+  const rsrc4_t rsa = make_rsrc4(As + (int64_t)m0 * KB, rows_a * KB);
+  const rsrc4_t rsb = make_rsrc4(Bs + (int64_t)n0 * KB, rows_b * KB);
+
+  // Code-load geometry: instruction u of this wave covers rows 16 (4 wave + u)
+  // .. +15; lane i fills LDS slot i & 3 of row 16 (4 wave + u) + (i >> 2) with
+  // the chunk that the swizzle puts there.
+  int code_off[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int row = 16 * (4 * wave + u) + (lane >> 2);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
+    code_off[u] = row * KP + chunk * 16;
+  }
+  const int scale_off = (64 * wave + lane) * KB;
+
+  // Stage st: its codes, plus (when st starts a super-stage) the scales of the
+  // whole super-stage.  Stages past the last are issued at an out-of-range
+  // offset: zeros land in slots nobody reads, and every step keeps the same
+  // static wait count.
+  auto issue = [&](int st, auto WITH_SCALES) {
+    const int slot = st % RB_NS;
+    const bool live = st < KT;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int off = live ? code_off[u] + st * RB_K : OOB;
+      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
+      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + u)]), off);
+    }
+    if (decltype(WITH_SCALES)::value) {
+      const int sbuf = (st / U) % NSB;
+      const int soff = live ? scale_off + (st / U) * SB : OOB;
+      if (SB == 16) {
+        dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
+        dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave * 4]), soff);
+      } else {
+        dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+        dma_x1(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
+      }
+    }
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  // Fragments of stage st; `in` = st % U is static.  FP8: the stage's E8M0
+  // bytes are 2 in and 2 in + 1 of the row's SB-byte scale entry and lane g
+  // takes byte 2 in + g; both sit in dword in / 2.  FP4: the stage's bytes
+  // are dword in, and lane g takes byte 2 s + g for MFMA s = 0, 1.  Shifting
+  // the dword right by 8 g puts lane g's byte at the same position for both
+  // lane halves (2 (in % 2) for FP8, 2 s for FP4), and the MFMA's scale byte
+  // select (op_sel) picks it there: no per-byte extraction.  The scale dwords
+  // are read first, so the first MFMA never waits on a drained LDS queue.
+  auto read_frags = [&](int st, auto INC, Frags<FP4>& f) {
+    constexpr int in = decltype(INC)::value;
+    constexpr int word = FP4 ? in : in / 2;
+    const int slot = st % RB_NS, sbuf = (st / U) % NSB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.sa[i] = (int)(sm.as[sbuf][(wm * 128 + i * 32 + r) * (SB / 4) + word] >> (8 * g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.sb[j] = (int)(sm.bs[sbuf][(wn * 128 + j * 32 + r) * (SB / 4) + word] >> (8 * g));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r;
+      const uint4 lo = sm.a[slot][rswz(row, g)], hi = sm.a[slot][rswz(row, 2 + g)];
+      if constexpr (FP4) {
+        f.alo[i] = lo;
+        f.ahi[i] = hi;
+      } else {
+        f.a[i] = frag8(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + r;
+      const uint4 lo = sm.b[slot][rswz(row, g)], hi = sm.b[slot][rswz(row, 2 + g)];
+      if constexpr (FP4) {
+        f.blo[j] = lo;
+        f.bhi[j] = hi;
+      } else {
+        f.b[j] = frag8(lo, hi);
+      }
+    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  // MFMAs of tile rows i0, i0 + 1.  OPSEL: byte of the (shifted) scale dwords
+  // that holds this stage's FP8 scale.  FP4 runs its two K64 halves in turn
+  // (all 8 tiles of the first, then the second), so the two MFMAs into one
+  // accumulator are 7 issues apart.
+  auto mfma_rows = [&](const Frags<FP4>& f, int i0, auto OPSEL) {
+    constexpr int fmt = mfma_fmt<FP4>();
+    if constexpr (FP4) {
+      static_for<0, 2>([&](auto SC) {
+        constexpr int s = decltype(SC)::value;
+#pragma unroll
+        for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j], fmt, fmt,
+                2 * s, f.sa[i], 2 * s, f.sb[j]);
+      });
+    } else {
+      constexpr int sel = decltype(OPSEL)::value;
+#pragma unroll
+      for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], fmt, fmt, sel,
+                                                                      f.sa[i], sel, f.sb[j]);
+    }
+  };
+
+  // Loads issued for stage s: codes, plus 2 scale loads when s starts a
+  // super-stage.  Waiting for stage kt+1 leaves stages kt+2 and kt+3 in flight.
+  auto loads_of = [](int s_mod) { return RB_CODE_LOADS + (s_mod == 0 ? 2 : 0); };
+
+  // Step kt with kt % U == IN; fragments alternate between f[0] and f[1] with
+  // the step's parity, which IN fixes when U is even (U == 1 unrolls by 2).
+  Frags<FP4> f[2];
+  auto step = [&](int kt, auto INC, auto CURC) {
+    constexpr int IN = decltype(INC)::value;
+    constexpr int CUR = decltype(CURC)::value;
+    constexpr int ISSUE_MOD = (IN + RB_NS - 1) % U;   // stage kt+3 within its super-stage
+    constexpr int AFTER = loads_of((IN + 2) % U) + loads_of((IN + 3) % U);
+    constexpr auto SEL = std::integral_constant<int, 2 * (IN % 2)>{};
+    issue(kt + RB_NS - 1, std::integral_constant<bool, ISSUE_MOD == 0>{});
+    // keep the loads at the head of the step: the compiler would otherwise
+    // sink them below the first MFMAs and shorten the ring's lead
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_rows(f[CUR], 0, SEL);
+    wait_vm_barrier<AFTER>();        // stage kt+1 landed; kt+2, kt+3 in flight
+    read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, f[CUR ^ 1]);
+    mfma_rows(f[CUR], 2, SEL);
+    // 8 MFMAs (FP8) or 16 (FP4) interleaved with the 24 LDS reads
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, per_byte<FP4>(), 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                  // 3 LDS reads
+    }
+  };
+
+  // prologue: stages 0..2 (stage 0 carries the first super-stage's scales)
+  issue(0, std::true_type{});
+  issue(1, std::integral_constant<bool, (1 % U) == 0>{});
+  issue(2, std::integral_constant<bool, (2 % U) == 0>{});
+  wait_vm_barrier<loads_of(1 % U) + loads_of(2 % U)>();
+  read_frags(0, std::integral_constant<int, 0>{}, f[0]);
+  // Every step has the same shape, the last ones included: they issue
+  // out-of-range (zero, no traffic) loads for stages past KT and read the
+  // zero fragments of "stage KT", which are never used.  One copy of the
+  // loop body (U steps, or 2 when U == 1) therefore serves the whole loop;
+  // with U == 1 and KT odd the second step of the last pass is skipped.
+  constexpr int UNROLL = U == 1 ? 2 : U;
+  for (int kt = 0; kt < KT; kt += UNROLL) {
+    static_for<0, UNROLL>([&](auto IC) {
+      constexpr int i = decltype(IC)::value;
+      if (U == 1 && i == 1 && kt + 1 == KT) return;
+      step(kt + i, std::integral_constant<int, i % U>{}, std::integral_constant<int, i & 1>{});
+    });
+  }
+
+  // Epilogue.  Tiles wholly inside C (all but the ragged edge) store without
+  // per-element bounds checks; each store writes two 64-byte row segments.
+  uint16_t* cw = C + (int64_t)(m0 + wm * 128 + g * 4) * N + n0 + wn * 128 + r;
+  if (m0 + BM <= M && n0 + BN <= N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 128 + j * 32 + r;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+        }
+      }
+  }
+}
+
+template <bool FP4>
+hipError_t launch_mx(int64_t m, int64_t n, int64_t k, const uint8_t* a, const uint8_t* as,
+                     const uint8_t* b, const uint8_t* bs, uint16_t* c, hipStream_t stream) {
+  const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
+  if (k % 512 == 0 && k > 0)
+    hipLaunchKernelGGL((mx_gemm_ring_kernel<16, FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else if (k % 128 == 0 && k > 0)
+    hipLaunchKernelGGL((mx_gemm_ring_kernel<4, FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((mx_gemm_kernel<FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a, as, b,
+                       bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_mxfp8(int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                             const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
+                             hipStream_t stream) {
+  return launch_mx<false>(m, n, k, a, as, b, bs, c, stream);
+}
+
+hipError_t launch_gemm_mxfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                             const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
+                             hipStream_t stream) {
+  return launch_mx<true>(m, n, k, a, as, b, bs, c, stream);
+}
+
+}  // namespace bsg

@@ -10,11 +10,16 @@ namespace bsg {
 
 hipError_t launch_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* codes,
                                  uint8_t* scales, hipStream_t stream, int num_cus);
+hipError_t launch_quantize_mxfp4(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t stream, int num_cus);
 hipError_t launch_quantize_nvfp4(int64_t rows, int64_t k, const float* x, uint8_t* codes,
                                  uint8_t* scales, float* tensor_scale, hipStream_t stream,
                                  int num_cus);
 
 hipError_t launch_gemm_mxfp8(int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                             const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
+                             hipStream_t stream);
+hipError_t launch_gemm_mxfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
                              hipStream_t stream);
 hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,

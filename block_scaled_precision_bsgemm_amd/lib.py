@@ -24,12 +24,14 @@ BSGEMM_ERR_RESOURCE = 5
 BSGEMM_ERR_LAUNCH = 6
 BSGEMM_NVFP4 = 1
 BSGEMM_MXFP8 = 2
+BSGEMM_MXFP4 = 3
 
 # Symbols declared in include/bsgemm.h with their ctypes signatures.
 _i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
 SIGNATURES = {
     "bsgemm_quantize_nvfp4": (_int, [_i64, _i64, _p, _p, _p, _p, _p]),
     "bsgemm_quantize_mxfp8": (_int, [_i64, _i64, _p, _p, _p, _p]),
+    "bsgemm_quantize_mxfp4": (_int, [_i64, _i64, _p, _p, _p, _p]),
     "bsgemm_run": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
     "bsgemm_grouped_run": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
     "bsgemm_w4a16_run": (_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
@@ -101,6 +103,15 @@ def bsgemm_quantize_mxfp8(x, codes=None, scales=None, stream=None):
     codes = _empty((rows, k), torch.uint8, x) if codes is None else codes
     scales = _empty((rows, k // 32), torch.uint8, x) if scales is None else scales
     _check(load().bsgemm_quantize_mxfp8(rows, k, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes, scales
+
+
+def bsgemm_quantize_mxfp4(x, codes=None, scales=None, stream=None):
+    """x: float32 [rows, k] -> (codes uint8 [rows, k/2], scales uint8 [rows, k/32])."""
+    rows, k = x.shape
+    codes = _empty((rows, k // 2), torch.uint8, x) if codes is None else codes
+    scales = _empty((rows, k // 32), torch.uint8, x) if scales is None else scales
+    _check(load().bsgemm_quantize_mxfp4(rows, k, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream)))
     return codes, scales
 
 

@@ -12,6 +12,9 @@ distributions are the library's stated synthetic recipe):
   (the 256 x 256 x 128 case of "Triton #11171 ...", section "The missing case
   was defined by shape, layout, and execution mode together").
 * ``mxfp8_4k``      -- MXFP8 x MXFP8, M=N=K=4096, ~ N(0, 1).
+* ``mxfp4``         -- MXFP4 x MXFP4, M=N=K=4096 or 16384, ~ N(0, 1) with 1% of
+  the rows of A and of B multiplied by 100 (the 16k-square recipe of
+  ``nvfp4_16k``, own seeds).
 * ``nvfp4_16k``     -- NVFP4 x NVFP4, M=N=K=16384 ("Together AI Ports
   ThunderKittens GEMM Kernels to NVIDIA Vera Rubin NVL72", section "Building
   the GEMM": 16k square GEMMs), ~ N(0, 1) with 1% of the rows of A and of B
@@ -37,6 +40,7 @@ SEEDS = {
     "nvfp4_16k.A.rows": 3011, "nvfp4_16k.B.rows": 3012,
     "grouped.counts": 4000, "grouped.A": 4001, "grouped.W": 4002,
     "w4a16.X": 5001, "w4a16.W": 5002,
+    "mxfp4.A": 6001, "mxfp4.B": 6002, "mxfp4.A.rows": 6011, "mxfp4.B.rows": 6012,
 }
 
 SHAPES = {
@@ -44,6 +48,8 @@ SHAPES = {
     "mxfp8_4k": dict(M=4096, N=4096, K=4096),
     "mxfp8_16k": dict(M=16384, N=16384, K=16384),
     "nvfp4_16k": dict(M=16384, N=16384, K=16384),
+    "mxfp4_4k": dict(M=4096, N=4096, K=4096),
+    "mxfp4_16k": dict(M=16384, N=16384, K=16384),
     "grouped": dict(G=32, M=16384, N=2048, K=7168, alpha=0.5),
     "w4a16": dict(Ms=(1, 16, 64, 256), N=14336, K=4096),
 }
@@ -106,6 +112,13 @@ def mxfp8_inputs(M=4096, N=4096, K=4096):
 def nvfp4_16k_inputs(M=16384, N=16384, K=16384):
     a, ia = with_outlier_rows(normal_f32((M, K), SEEDS["nvfp4_16k.A"]), SEEDS["nvfp4_16k.A.rows"])
     b, ib = with_outlier_rows(normal_f32((N, K), SEEDS["nvfp4_16k.B"]), SEEDS["nvfp4_16k.B.rows"])
+    return a, b, ia, ib
+
+
+def mxfp4_inputs(M=16384, N=16384, K=16384):
+    """A [M, K], B [N, K] ~ N(0, 1) with 1% outlier rows (x100) in each."""
+    a, ia = with_outlier_rows(normal_f32((M, K), SEEDS["mxfp4.A"]), SEEDS["mxfp4.A.rows"])
+    b, ib = with_outlier_rows(normal_f32((N, K), SEEDS["mxfp4.B"]), SEEDS["mxfp4.B.rows"])
     return a, b, ia, ib
 
 

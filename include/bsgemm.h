@@ -30,6 +30,10 @@
  *     codes  uint8 [R][K]     E4M3 (FN) values
  *     scales uint8 [R][K/32]  E8M0 scale of each 32-element block along K
  *     value  = e4m3(code) * 2^(scale - 127)
+ *   MXFP4 operand [R][K], K % 32 == 0:
+ *     codes  uint8 [R][K/2]   E2M1 values; element 2j in the low nibble of byte j
+ *     scales uint8 [R][K/32]  E8M0 scale of each 32-element block along K
+ *     value  = e2m1(code) * 2^(scale - 127)
  *   BF16 operands and outputs are uint16 bit patterns, row-major.
  *
  * Conventions common to every call:
@@ -73,7 +77,8 @@ enum bsgemm_status {
 
 enum bsgemm_format {
   BSGEMM_NVFP4 = 1,
-  BSGEMM_MXFP8 = 2
+  BSGEMM_MXFP8 = 2,
+  BSGEMM_MXFP4 = 3
 };
 
 /*
@@ -135,18 +140,49 @@ int bsgemm_quantize_mxfp8(int64_t rows, int64_t k, const float* x, uint8_t* code
                           uint8_t* scales, void* stream);
 
 /*
+ * MXFP4 quantizer: x[rows][k] (FP32) -> codes uint8[rows][k/2], scales uint8[rows][k/32].
+ *
+ *   For each 32-element block along k:
+ *     bamax = max |x|;
+ *     e     = ceil(log2(bamax / 6)), computed exactly as
+ *             min{e : 6 * 2^e >= bamax}, clamped to [-127, 127]
+ *             (bamax == 0 gives -127);
+ *     scale = e + 127 (E8M0);
+ *     code  = signbit(x) << 3 | E2M1_RNE(|x * 2^-e|)  (never saturates:
+ *             |x * 2^-e| <= 6 by the choice of e).
+ *   Element 2j of a row goes to the low nibble of byte j.
+ * This is the MXFP8 rule with E2M1's largest value (6) in place of E4M3's
+ * (448).  The output is bit-exact.  Format family named on the pages:
+ * "MXFP" ("Triton #11171 ...", section "The broader related matrix protected
+ * neighboring policy"); the 4-bit E2M1 element is the one of NVFP4 ("Together
+ * AI Ports ThunderKittens ...", section "Building the GEMM").
+ *
+ * Arguments:
+ *   x      device float[rows][k], 16-byte aligned
+ *   codes  device uint8[rows][k/2], 16-byte aligned (written)
+ *   scales device uint8[rows][k/32], 16-byte aligned (written)
+ * Sizes: rows >= 0, k >= 0, k % 32 == 0.
+ */
+int bsgemm_quantize_mxfp4(int64_t rows, int64_t k, const float* x, uint8_t* codes,
+                          uint8_t* scales, void* stream);
+
+/*
  * Dense block-scaled GEMM with both operands in format `fmt`:
  *   C[m][n] = bf16_RNE( sum_k deq(A)[m][k] * deq(B)[n][k] )
  * with FP32 accumulation.  For NVFP4 the sum runs over
  * (e2m1 * e4m3)_A * (e2m1 * e4m3)_B and is then multiplied by
- * (*a_tscale) * (*b_tscale).
+ * (*a_tscale) * (*b_tscale).  MXFP8 and MXFP4 apply their E8M0 block scales
+ * inside the matrix-core product.
  * Source: "Together AI Ports ThunderKittens GEMM Kernels to NVIDIA Vera Rubin
- * NVL72", section "Building the GEMM" (NVFP4 and FP8 E4M3 GEMMs, 16k square).
+ * NVL72", section "Building the GEMM" (NVFP4 and FP8 E4M3 GEMMs, 16k square);
+ * MXFP4 is the MX member with the E2M1 element ("Triton #11171 ...", section
+ * "The broader related matrix protected neighboring policy").
  *
  * Arguments:
- *   fmt                 BSGEMM_NVFP4 or BSGEMM_MXFP8
+ *   fmt                 BSGEMM_NVFP4, BSGEMM_MXFP8 or BSGEMM_MXFP4
  *   a, a_scales         operand A [m][k] in the layout of `fmt`
- *   a_tscale, b_tscale  device float[1] for NVFP4; must be NULL for MXFP8
+ *   a_tscale, b_tscale  device float[1] for NVFP4; must be NULL for the MX
+ *                       formats
  *   b, b_scales         operand B [n][k], in the same format
  *   c_bf16              device uint16[m][n] (written)
  * Sizes: m, n, k >= 0, k % 32 == 0.

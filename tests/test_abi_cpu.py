@@ -42,7 +42,7 @@ def test_status_strings_and_version(so):
                        (5, b"BSGEMM_ERR_RESOURCE"), (6, b"BSGEMM_ERR_LAUNCH")]:
         assert so.bsgemm_status_string(code) == name
     assert so.bsgemm_status_string(99) == b"unknown status"
-    assert so.bsgemm_version() == 100
+    assert so.bsgemm_version() == 200
 
 
 def run(so, fmt=L.BSGEMM_NVFP4, m=64, n=64, k=64, a=P, sa=P, ta=P, b=P, sb=P, tb=P, c=P):
@@ -58,6 +58,10 @@ def test_run_validation(so):
     assert run(so, k=48) == L.BSGEMM_ERR_UNSUPPORTED
     assert run(so, fmt=7) == L.BSGEMM_ERR_UNSUPPORTED
     assert run(so, fmt=L.BSGEMM_MXFP8) == L.BSGEMM_ERR_UNSUPPORTED      # tensor scales given
+    assert run(so, fmt=L.BSGEMM_MXFP4) == L.BSGEMM_ERR_UNSUPPORTED
+    assert b"MXFP4 takes no tensor scales" in so.bsgemm_last_error()
+    assert run(so, fmt=L.BSGEMM_MXFP4, ta=None, tb=None, k=80) == L.BSGEMM_ERR_UNSUPPORTED
+    assert run(so, fmt=L.BSGEMM_MXFP4, ta=None, tb=None, sb=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, a=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, c=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, sa=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
@@ -69,7 +73,14 @@ def test_run_validation(so):
 
 
 def test_quantize_validation(so):
-    q4, q8 = so.bsgemm_quantize_nvfp4, so.bsgemm_quantize_mxfp8
+    q4, q8, m4 = so.bsgemm_quantize_nvfp4, so.bsgemm_quantize_mxfp8, so.bsgemm_quantize_mxfp4
+    assert m4(-1, 64, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert m4(4, 64, None, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert m4(4, 64, P, P, None, None) == L.BSGEMM_ERR_INVALID_ARG
+    assert m4(4, 48, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert m4(4, 64, MIS, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert m4(4, 64, P, MIS, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert m4(4, 64, P, P, MIS, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert q4(4, 64, None, P, P, P, None) == L.BSGEMM_ERR_INVALID_ARG
     assert q4(4, 64, P, P, P, None, None) == L.BSGEMM_ERR_INVALID_ARG
     assert q4(4, 40, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
@@ -117,6 +128,8 @@ def test_no_device_is_reported_not_launched(so):
         pytest.skip("a GPU is visible; this case checks the no-device path")
     assert run(so) == L.BSGEMM_ERR_DEVICE
     assert so.bsgemm_quantize_mxfp8(4, 64, P, P, P, None) == L.BSGEMM_ERR_DEVICE
+    assert so.bsgemm_quantize_mxfp4(4, 64, P, P, P, None) == L.BSGEMM_ERR_DEVICE
+    assert run(so, fmt=L.BSGEMM_MXFP4, ta=None, tb=None) == L.BSGEMM_ERR_DEVICE
 
 
 def test_binding_raises_on_error():

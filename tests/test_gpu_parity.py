@@ -95,6 +95,30 @@ def _check_mxfp8_quant(x, what):
     return c, s
 
 
+def _check_mxfp4_quant(x, what, rows=None):
+    say("quantize_mxfp4", what, x.shape)
+    c, s = L.bsgemm_quantize_mxfp4(dev(x))
+    xs = x if rows is None else x[rows]
+    oc, os_ = Q.quantize_mxfp4(xs)
+    gc, gs = c.cpu().numpy(), s.cpu().numpy()
+    if rows is not None:
+        gc, gs = gc[rows], gs[rows]
+    assert np.array_equal(gs, os_), f"{what}: scale bytes differ at {np.argwhere(gs != os_)[:5]}"
+    assert np.array_equal(gc, oc), f"{what}: code bytes differ at {np.argwhere(gc != oc)[:5]}"
+    return c, s
+
+
+def _mxfp4_tie_rows(k=256):
+    """Blocks whose maximum is 6 (exponent 0) filled with every E2M1 midpoint
+    (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5) and its neighbours, both signs, and
+    the same blocks scaled by 2^-3 and 2^20 (exact, so the ties stay ties)."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    vals = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(7))])
+    row = np.resize(np.concatenate([vals, -vals]), k).astype(np.float32)
+    row[::32] = 6.0
+    return np.stack([row, row * np.float32(0.125), row * np.float32(2.0 ** 20)])
+
+
 def test_quantize_nvfp4_small_config(gpu_lib):
     a, b = synth.nvfp4_small_inputs()
     _check_nvfp4_quant(a, "256x128 A")
@@ -127,6 +151,26 @@ def test_quantize_mxfp8_edges(gpu_lib):
     _check_mxfp8_quant(_edge_matrix(96), "k = 96")
 
 
+def test_quantize_mxfp4_4k_config(gpu_lib):
+    a, b, _, _ = synth.mxfp4_inputs(4096, 4096, 4096)
+    _check_mxfp4_quant(a, "4096^2 A")
+    _check_mxfp4_quant(b, "4096^2 B")
+
+
+def test_quantize_mxfp4_edges(gpu_lib):
+    x = _edge_matrix()
+    _check_mxfp4_quant(x, "edge rows")
+    _check_mxfp4_quant(x[:, :32], "k = 32")
+    _check_mxfp4_quant(_edge_matrix(96), "k = 96")
+    _check_mxfp4_quant(_mxfp4_tie_rows(), "E2M1 ties")
+    # block maxima at FLT_MAX and just above 6 * 2^125 (largest exponents)
+    y = np.random.Generator(np.random.PCG64(21)).standard_normal((4, 64)).astype(np.float32)
+    y[0, 0] = np.finfo(np.float32).max
+    y[1, 3] = np.float32(6 * 2.0 ** 125)
+    y[2, 40] = np.nextafter(np.float32(6 * 2.0 ** 125), np.float32(np.inf))
+    _check_mxfp4_quant(y, "largest block exponents")
+
+
 def test_quantize_empty(gpu_lib):
     say("quantize empty")
     x = torch.zeros((0, 64), dtype=torch.float32, device="cuda")
@@ -135,16 +179,20 @@ def test_quantize_empty(gpu_lib):
     assert ts.item() == 0.0
     c8, s8 = L.bsgemm_quantize_mxfp8(x)
     assert c8.numel() == 0
+    c4, s4 = L.bsgemm_quantize_mxfp4(x)
+    assert c4.numel() == 0
 
 
 # ---------------------------------------------------------------- GEMMs --
 
 def _quant(fmt, x):
-    return Q.quantize_nvfp4(x) if fmt == L.BSGEMM_NVFP4 else Q.quantize_mxfp8(x)
+    return {L.BSGEMM_NVFP4: Q.quantize_nvfp4, L.BSGEMM_MXFP8: Q.quantize_mxfp8,
+            L.BSGEMM_MXFP4: Q.quantize_mxfp4}[fmt](x)
 
 
-def _ref(fmt, qa, qb):
-    return G.gemm_nvfp4(*qa, *qb) if fmt == L.BSGEMM_NVFP4 else G.gemm_mxfp8(*qa, *qb)
+def _ref(fmt, qa, qb, rows=None):
+    return {L.BSGEMM_NVFP4: G.gemm_nvfp4, L.BSGEMM_MXFP8: G.gemm_mxfp8,
+            L.BSGEMM_MXFP4: G.gemm_mxfp4}[fmt](*qa, *qb, rows=rows)
 
 
 def _gpu_gemm(fmt, qa, qb, k):
@@ -158,7 +206,7 @@ def _gpu_gemm(fmt, qa, qb, k):
     return u16(c)
 
 
-FMTS = {"nvfp4": L.BSGEMM_NVFP4, "mxfp8": L.BSGEMM_MXFP8}
+FMTS = {"nvfp4": L.BSGEMM_NVFP4, "mxfp8": L.BSGEMM_MXFP8, "mxfp4": L.BSGEMM_MXFP4}
 
 
 def test_gemm_nvfp4_small_config(gpu_lib):
@@ -169,10 +217,11 @@ def test_gemm_nvfp4_small_config(gpu_lib):
     assert_ok(G.check(c, *G.gemm_nvfp4(*qa, *qb)), "nvfp4 256x256x128")
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("m,n,k", [
     (1, 1, 32), (7, 17, 64), (17, 255, 96), (256, 256, 128), (257, 300, 160),
     (300, 257, 512), (64, 520, 1024), (513, 129, 288), (1, 700, 2048),
+    (260, 513, 384), (512, 512, 640),
 ])
 def test_gemm_shapes(gpu_lib, fmt, m, n, k):
     f = FMTS[fmt]
@@ -186,7 +235,7 @@ def test_gemm_shapes(gpu_lib, fmt, m, n, k):
     assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 def test_gemm_zero_rows_and_k0(gpu_lib, fmt):
     f = FMTS[fmt]
     xa = synth.normal_f32((40, 128), 5)
@@ -216,9 +265,39 @@ def test_gemm_mxfp8_4k_config(gpu_lib):
     assert_ok(G.check(c[rows], *G.gemm_mxfp8(*qa, *qb, rows=rows)), "mxfp8 4096^3 (514 rows, all columns)")
 
 
+def test_gemm_mxfp4_4k_config(gpu_lib):
+    a, b, ia, _ = synth.mxfp4_inputs(4096, 4096, 4096)
+    qa, qb = Q.quantize_mxfp4(a), Q.quantize_mxfp4(b)
+    say("gemm mxfp4 4096^3")
+    c = _gpu_gemm(L.BSGEMM_MXFP4, qa, qb, 4096)
+    rows = _sample(4096, 512, 2, ia)
+    assert_ok(G.check(c[rows], *G.gemm_mxfp4(*qa, *qb, rows=rows)), "mxfp4 4096^3 (sampled rows, all columns)")
+
+
+def test_mxfp4_16k_config_sampled(gpu_lib):
+    """16384^3 MXFP4 with 1% outlier rows: GPU quantize + GEMM (the launch
+    configuration the benchmark times), checked on (163 outlier + 256 random
+    rows) x (163 outlier + 256 random columns)."""
+    a, b, ia, ib = synth.mxfp4_inputs()
+    rows = _sample(16384, 256, 13, ia)
+    cols = _sample(16384, 256, 14, ib)
+    ca, sa = _check_mxfp4_quant(a, "16k A (sampled rows)", rows)
+    cb, sb = _check_mxfp4_quant(b, "16k B (sampled rows)", cols)
+    del a, b
+    say("gemm mxfp4 16384^3")
+    c = out_bf16(16384, 16384)
+    L.bsgemm_run(L.BSGEMM_MXFP4, ca, sa, None, cb, sb, None, 16384, c=c)
+    sub = c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()]
+    got = u16(sub)
+    qa = (ca.cpu().numpy()[rows], sa.cpu().numpy()[rows])
+    qb = (cb.cpu().numpy()[cols], sb.cpu().numpy()[cols])
+    assert_ok(G.check(got, *G.gemm_mxfp4(*qa, *qb)), "mxfp4 16384^3 sampled")
+    assert not torch.isnan(c.view(torch.bfloat16)).any().item()
+
+
 def test_gemm_deterministic(gpu_lib):
     a, b = synth.nvfp4_small_inputs()
-    for f in (L.BSGEMM_NVFP4, L.BSGEMM_MXFP8):
+    for f in (L.BSGEMM_NVFP4, L.BSGEMM_MXFP8, L.BSGEMM_MXFP4):
         qa, qb = _quant(f, np.tile(a, (3, 4))), _quant(f, np.tile(b, (2, 4)))
         say("determinism", f)
         c1 = _gpu_gemm(f, qa, qb, 512)
@@ -422,3 +501,28 @@ def test_gemm_mxfp8_wide_range_encoder_output(gpu_lib, k):
     bound = 2.0 ** -8 * np.abs(cref) + 1e-5 * t + 2.0 ** -10 * gm
     assert np.all(np.isfinite(got)) and np.all(np.abs(got - cref) <= bound), \
         f"mxfp8 wide range k={k}: worst {np.max(np.abs(got - cref) / bound):.3g}"
+
+
+@pytest.mark.parametrize("k", [96, 128, 384, 512, 2048 + 512])
+def test_gemm_mxfp4_every_code(gpu_lib, k):
+    """Random bytes (every E2M1 code in both nibbles, both signs) with E8M0
+    scales in [107, 147], on the 16-byte-scale ring (K % 512 == 0), the
+    4-byte-scale ring (K % 128 == 0) and the register-staged path (K = 96).
+    The bound is the MXFP8 every-code one (see test_gemm_mxfp8_every_code):
+    2^-8 |C| + 1e-5 T + 2^-10 G, with G the sum of the largest |product| of
+    each aligned group of 8."""
+    r = np.random.Generator(np.random.PCG64(k + 3))
+    m, n = 260, 300
+    qa = (r.integers(0, 256, (m, k // 2)).astype(np.uint8), r.integers(107, 148, (m, k // 32)).astype(np.uint8))
+    qb = (r.integers(0, 256, (n, k // 2)).astype(np.uint8), r.integers(107, 148, (n, k // 32)).astype(np.uint8))
+    say("gemm mxfp4 every code, k =", k)
+    c = _gpu_gemm(L.BSGEMM_MXFP4, qa, qb, k)
+    cref, t = G.gemm_mxfp4(*qa, *qb)
+    gm = _group_max_products(G.dequant_mxfp4(*qa), G.dequant_mxfp4(*qb))
+    got = F.decode_bf16(c)
+    plain = 2.0 ** -8 * np.abs(cref) + 1e-5 * t
+    print(f"[info] mxfp4 every code k={k}: worst ratio to the plain bound "
+          f"{np.max(np.abs(got - cref) / plain):.3g}", flush=True)
+    bound = plain + 2.0 ** -10 * gm
+    assert np.all(np.isfinite(got)) and np.all(np.abs(got - cref) <= bound), \
+        f"mxfp4 every code k={k}: worst {np.max(np.abs(got - cref) / bound):.3g}"
