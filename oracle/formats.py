@@ -74,6 +74,19 @@ def decode_bf16(bits) -> np.ndarray:
         return b.view(np.float32).astype(np.float64)
 
 
+def decode_f16(bits) -> np.ndarray:
+    """IEEE binary16 bit patterns (uint16) -> float64, exactly, from the bit
+    fields: sign 1, exponent 5 (bias 15), fraction 10.  Exponent 0 is
+    subnormal (f * 2**-24); exponent 31 is Inf (f == 0) or NaN."""
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    sign = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(f, -24), np.ldexp(1024.0 + f, (e - 25).astype(np.int64)))
+    mag = np.where(e == 31, np.where(f == 0, np.inf, np.nan), mag)
+    return sign * mag
+
+
 def unpack_nibbles(packed) -> np.ndarray:
     """uint8 [..., K/2] -> uint8 [..., K]; element 2j is the low nibble of byte j."""
     p = np.asarray(packed, dtype=np.uint8)

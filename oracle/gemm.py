@@ -20,7 +20,7 @@ from fractions import Fraction
 import numpy as np
 
 from .formats import (decode_bf16, decode_e2m1, decode_e4m3, decode_e8m0,
-                      unpack_nibbles)
+                      decode_f16, unpack_nibbles)
 
 # ------------------------------------------------------------ dequantizers --
 
@@ -121,6 +121,64 @@ def grouped_nvfp4_bf16(a_codes, a_scales, a_ts, offsets, w_bf16, rows=None):
         xa = dequant_nvfp4(a_codes[rows[sel]], a_scales[rows[sel]], a_ts)
         cg, tg = _matmul_and_mag(xa, decode_bf16(w[g]))
         c[sel], t[sel] = cg, tg
+    return c, t
+
+
+def grouped_nvfp4_ex(a_codes, a_scales, a_ts, offsets, w_bits, w_dtype="bf16", bias=None,
+                     gamma=None, gather=None, scatter=None, out_rows=None):
+    """Ragged grouped NVFP4 x dense GEMM with the epilogue variants of "Triton
+    #11171 ...", sections "Scatter changes where output rows are written",
+    "Gamma adds a per-row scaling input", "The ordinary variants also exercise
+    the shared bias route" (NVFP4 x dense matmul + bias + optional gamma +
+    optional scatter), the gathered-activation variant named in "Filter 3:
+    gather variants are excluded", and the FP16 dense operand of the
+    rhs_dtype sweep.
+
+    Logical row r (off[g] <= r < off[g+1] puts it in group g):
+        src(r) = gather[r] if gather is given, else r      (row of A it reads)
+        y[r, n] = (s_t * sum_k x_hat_A[src(r), k] * W[g][n, k] + bias[g, n]) * gamma[r]
+        C[dst(r), n] = y[r, n],  dst(r) = scatter[r] if scatter is given, else r
+    bias ([G, N]) and gamma ([M]) are optional (absent = 0 and 1).  W holds
+    BF16 or FP16 bit patterns ([G, N, K] uint16), decoded exactly.  The
+    order (bias added to the scaled product, gamma applied to the sum) is the
+    order the page lists them in.
+
+    Returns (C_ref, T) over physical output rows 0..M-1 (or ``out_rows`` of
+    them, in order), with T[dst(r), n] = (s_t * sum_k |a w| + |bias|) * |gamma|.
+    A physical row that no logical row maps to stays 0 in both (scatter must
+    be a permutation for every row to be written)."""
+    off = np.asarray(offsets, dtype=np.int64)
+    G = len(off) - 1
+    w = np.asarray(w_bits)
+    assert w.shape[0] == G and off[0] == 0 and np.all(np.diff(off) >= 0)
+    M = int(off[-1])
+    N = w.shape[1]
+    decode = {"bf16": decode_bf16, "f16": decode_f16}[w_dtype]
+    a_codes, a_scales = np.asarray(a_codes), np.asarray(a_scales)
+    src = np.arange(M) if gather is None else np.asarray(gather, dtype=np.int64)
+    dst = np.arange(M) if scatter is None else np.asarray(scatter, dtype=np.int64)
+    assert src.shape == (M,) and dst.shape == (M,)
+    gam = np.ones(M) if gamma is None else np.asarray(gamma, dtype=np.float64)
+    if out_rows is None:
+        out_rows = np.arange(M)
+    out_rows = np.asarray(out_rows, dtype=np.int64)
+    logical_of = np.full(M, -1, dtype=np.int64)
+    logical_of[dst] = np.arange(M)
+    logical = logical_of[out_rows]
+    c = np.zeros((len(out_rows), N))
+    t = np.zeros((len(out_rows), N))
+    group_of = np.searchsorted(off, np.maximum(logical, 0), side="right") - 1
+    for g in np.unique(group_of[logical >= 0]):
+        sel = np.nonzero((group_of == g) & (logical >= 0))[0]
+        lr = logical[sel]
+        xa = dequant_nvfp4(a_codes[src[lr]], a_scales[src[lr]], 1.0)
+        cg, tg = _matmul_and_mag(xa, decode(w[g]))
+        cg, tg = cg * float(a_ts), tg * abs(float(a_ts))
+        if bias is not None:
+            b = np.asarray(bias, dtype=np.float64)[g]
+            cg, tg = cg + b[None, :], tg + np.abs(b)[None, :]
+        c[sel] = cg * gam[lr][:, None]
+        t[sel] = tg * np.abs(gam[lr])[:, None]
     return c, t
 
 

@@ -183,6 +183,108 @@ def test_grouped_reduces_to_per_group_products_and_handles_empty_groups():
     assert np.array_equal(c2, c[rows])
 
 
+def _f16_frac(bits):
+    """Exact value of a finite FP16 bit pattern, from its fields."""
+    b = int(bits) & 0xFFFF
+    sign = -1 if b >> 15 else 1
+    e, f = (b >> 10) & 0x1F, b & 0x3FF
+    assert e != 31
+    return sign * (Fraction(f, 1 << 24) if e == 0 else Fraction(1024 + f, 1 << 10) * Fraction(2) ** (e - 15))
+
+
+def test_decode_f16_matches_numpy_float16_on_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint16)
+    ours = F.decode_f16(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.all((ours == ref) | (np.isnan(ours) & np.isnan(ref)))
+    for b in (0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xC000, 0x8001):
+        assert Fraction(float(ours[b])) == _f16_frac(b)
+
+
+def _grouped_ex_case(seed, w_dtype):
+    r = np.random.Generator(np.random.PCG64(seed))
+    counts = np.array([3, 0, 4, 2])
+    off = synth.offsets_from_counts(counts)
+    M, K, N, a_rows = int(counts.sum()), 64, 5, 7
+    x = synth.normal_f32((a_rows, K), seed + 1)
+    x[2, 16:32] *= np.float32(0.01)
+    a = Q.quantize_nvfp4(x)
+    wf = synth.normal_f32((len(counts), N, K), seed + 2, std=0.5)
+    w = synth.bf16_bits(wf) if w_dtype == "bf16" else wf.astype(np.float16).view(np.uint16)
+    gather = r.integers(0, a_rows, M).astype(np.int32)
+    scatter = r.permutation(M).astype(np.int32)
+    bias = r.standard_normal((len(counts), N)).astype(np.float32)
+    gamma = r.uniform(-2, 2, M).astype(np.float32)
+    return a, off, w, gather, scatter, bias, gamma
+
+
+def _grouped_ex_exact(a, off, w, w_dtype, gather, scatter, bias, gamma):
+    """Element by element in rationals: y = (s_t sum a w + bias) gamma, stored
+    at the scattered row."""
+    ea = _exact_nvfp4(*a)
+    M, N = int(off[-1]), w.shape[1]
+    dec = (lambda v: Fraction(float(F.decode_bf16(v)))) if w_dtype == "bf16" else _f16_frac
+    out = {}
+    for g in range(len(off) - 1):
+        for r in range(off[g], off[g + 1]):
+            row = ea[int(gather[r])]
+            vals = []
+            for n in range(N):
+                acc = sum((x * dec(w[g, n, k]) for k, x in enumerate(row)), Fraction(0))
+                vals.append((acc + Fraction(float(bias[g, n]))) * Fraction(float(gamma[r])))
+            out[int(scatter[r])] = vals
+    assert sorted(out) == list(range(M))
+    return out
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+def test_grouped_ex_equals_exact_bruteforce(w_dtype):
+    a, off, w, gather, scatter, bias, gamma = _grouped_ex_case(91, w_dtype)
+    c, t = G.grouped_nvfp4_ex(*a, off, w, w_dtype, bias, gamma, gather, scatter)
+    ex = _grouped_ex_exact(a, off, w, w_dtype, gather, scatter, bias, gamma)
+    for row, vals in ex.items():
+        for n, v in enumerate(vals):
+            assert abs(Fraction(float(c[row, n])) - v) <= Fraction(1e-12) * (1 + abs(v)), (row, n)
+            assert t[row, n] >= abs(float(v)) * (1 - 1e-12)
+    # planted mistakes: gamma taken by physical row, or bias of the wrong group
+    cw, _ = G.grouped_nvfp4_ex(*a, off, w, w_dtype, bias, gamma[scatter], gather, scatter)
+    assert not np.allclose(cw, c, rtol=1e-9, atol=1e-9)
+    cb, _ = G.grouped_nvfp4_ex(*a, off, w, w_dtype, bias[::-1].copy(), gamma, gather, scatter)
+    assert not np.allclose(cb, c, rtol=1e-9, atol=1e-9)
+
+
+def test_grouped_ex_reductions():
+    a, off, w, gather, scatter, bias, gamma = _grouped_ex_case(92, "bf16")
+    M = int(off[-1])
+    # no variants: the plain grouped reference on the same rows of A
+    ident = np.arange(M)
+    x = synth.normal_f32((M, 64), 93)
+    aq = Q.quantize_nvfp4(x)
+    c0, t0 = G.grouped_nvfp4_bf16(*aq, off, w)
+    c1, t1 = G.grouped_nvfp4_ex(*aq, off, w, "bf16", gather=ident, scatter=ident)
+    assert np.allclose(c0, c1, rtol=1e-14, atol=1e-14 * t0.max()) and np.allclose(t0, t1, rtol=1e-14)
+    c2, _ = G.grouped_nvfp4_ex(*aq, off, w, "bf16", bias=np.zeros((len(off) - 1, w.shape[1]), np.float32),
+                               gamma=np.ones(M, np.float32))
+    assert np.allclose(c0, c2, rtol=1e-14, atol=1e-14 * t0.max())
+    # gamma = 2^j scales rows exactly; scatter permutes rows
+    gam = np.exp2(np.arange(M) % 5 - 2).astype(np.float32)
+    c3, _ = G.grouped_nvfp4_ex(*aq, off, w, "bf16", gamma=gam)
+    assert np.array_equal(c3, c0 * gam[:, None].astype(np.float64))
+    perm = np.random.Generator(np.random.PCG64(94)).permutation(M)
+    c4, _ = G.grouped_nvfp4_ex(*aq, off, w, "bf16", scatter=perm)
+    assert np.array_equal(c4[perm], c0)
+    # zero activations leave bias * gamma (closed form)
+    z = (np.zeros_like(aq[0]), aq[1], aq[2])
+    c5, _ = G.grouped_nvfp4_ex(*z, off, w, "bf16", bias=bias, gamma=gamma[:M])
+    grp = np.searchsorted(off, np.arange(M), side="right") - 1
+    assert np.array_equal(c5, bias[grp].astype(np.float64) * gamma[:M, None].astype(np.float64))
+    # out_rows selects physical rows
+    rows = np.array([5, 0, 8])
+    c6, _ = G.grouped_nvfp4_ex(*a, off, w, "bf16", bias, gamma, gather, scatter, out_rows=rows)
+    c7, _ = G.grouped_nvfp4_ex(*a, off, w, "bf16", bias, gamma, gather, scatter)
+    assert np.array_equal(c6, c7[rows])
+
+
 def test_w4a16_equals_exact_bruteforce():
     M, N, K = 3, 4, 64
     x = synth.bf16_bits(synth.normal_f32((M, K), 71))
