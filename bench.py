@@ -17,7 +17,8 @@ The same JSON line carries:
   - ``rows``: the other parts of the hot path, each timed with HIP events:
     the MXFP8 GEMM at 16384^3 and 4096^3, the MXFP4 GEMM at 16384^3 (on
     the MXFP8 row's N(0, 1) inputs), the ragged grouped NVFP4 x BF16
-    GEMM, the W4A16 GEMM at M = 1, 16, 64, 256 with weights rotated through
+    GEMM (and the same problem with FP16 weights and every routing and
+    epilogue variant), the W4A16 GEMM at M = 1, 16, 64, 256 with weights rotated through
     16 copies (cold cache), the three quantizers at 16384^2, and the
     256 x 256 x 128 NVFP4 GEMM latency.
 
@@ -234,7 +235,22 @@ def main():
     rows["grouped_nvfp4_bf16"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
                                   "gbps_algorithmic": round(gbytes / (ms * 1e-3) / 1e9, 1),
                                   "groups_nonempty": int((counts > 0).sum()), "max_group_rows": int(counts.max())}
-    del qg, dw, doff, cg
+    # the same problem through the variant entry point: FP16 weights (the BF16
+    # weights converted to FP16 on the device), gather over all rows, a
+    # scatter permutation, bias and gamma
+    rng = np.random.Generator(np.random.PCG64(4200))
+    dw16 = dw.view(torch.bfloat16).to(torch.float16).view(torch.int16)
+    vg = torch.from_numpy(rng.integers(0, 16384, 16384).astype(np.int32)).to(dev)
+    vs = torch.from_numpy(rng.permutation(16384).astype(np.int32)).to(dev)
+    vb = torch.from_numpy((rng.standard_normal((32, 2048)) * 0.1).astype(np.float32)).to(dev)
+    vgm = torch.from_numpy(rng.uniform(-2, 2, 16384).astype(np.float32)).to(dev)
+    ms = time_events(lambda i: L.bsgemm_grouped_run_ex(*qg, doff, dw16, 7168, w_dtype=L.BSGEMM_W_F16, bias=vb,
+                                                       gamma=vgm, gather_idx=vg, scatter_idx=vs, c=cg), 10, 3)
+    tf = gflops / (ms * 1e-3) / 1e12
+    rows["grouped_nvfp4_f16_all_variants"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                              "frac_f16_peak": round(tf / PEAK["f16"], 4),
+                                              "variants": "gather + scatter + bias + gamma, FP16 W"}
+    del qg, dw, doff, cg, dw16, vg, vs, vb, vgm
 
     # --------------------------------------------------------------- W4A16
     Nw, Kw = 14336, 4096

@@ -136,7 +136,7 @@ int check_limits(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k) {
 
 extern "C" {
 
-int bsgemm_version(void) { return 200; }   // 0.2.0: MXFP4
+int bsgemm_version(void) { return 300; }   // 0.3.0: grouped variants
 
 const char* bsgemm_status_string(int status) {
   switch (status) {
@@ -293,8 +293,56 @@ int bsgemm_grouped_run(int num_groups, int64_t m_total, int64_t n, int64_t k, co
     if (int s = check_device(fn, &num_cus)) return s;
     if (m_total == 0 || n == 0) return ok();
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return finish_launch(fn, bsg::launch_grouped(num_groups, m_total, n, k, a, a_scales, a_tscale,
-                                                 group_offsets, w_bf16, c_bf16, st), st);
+    bsg::GroupedCall call{num_groups, m_total, m_total, n, k, a, a_scales, a_tscale, group_offsets,
+                          w_bf16, false, nullptr, nullptr, nullptr, nullptr, c_bf16};
+    return finish_launch(fn, bsg::launch_grouped(call, st), st);
+  } catch (...) {
+    return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
+  }
+}
+
+int bsgemm_grouped_run_ex(int num_groups, int64_t m_total, int64_t n, int64_t k, int64_t a_rows,
+                          const uint8_t* a, const uint8_t* a_scales, const float* a_tscale,
+                          const int32_t* group_offsets, int w_dtype, const uint16_t* w,
+                          const float* bias, const float* gamma, const int32_t* gather_idx,
+                          const int32_t* scatter_idx, uint16_t* c_bf16, void* stream) {
+  static const char* fn = "bsgemm_grouped_run_ex";
+  try {
+    if (num_groups < 1) return fail(BSGEMM_ERR_INVALID_ARG, "%s: num_groups must be >= 1", fn);
+    if (m_total < 0 || n < 0 || k < 0 || a_rows < 0)
+      return fail(BSGEMM_ERR_INVALID_ARG, "%s: negative size", fn);
+    if (gather_idx == nullptr && a_rows != m_total)
+      return fail(BSGEMM_ERR_INVALID_ARG, "%s: without gather_idx, a_rows must equal m_total", fn);
+    REQUIRE_PTR(a, a_rows * k);
+    REQUIRE_PTR(a_scales, a_rows * k);
+    REQUIRE_PTR(w, n * k);
+    REQUIRE_PTR(c_bf16, m_total * n);
+    if (a_tscale == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: a_tscale is NULL", fn);
+    if (group_offsets == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: group_offsets is NULL", fn);
+    if (w_dtype != BSGEMM_W_BF16 && w_dtype != BSGEMM_W_F16)
+      return fail(BSGEMM_ERR_UNSUPPORTED, "%s: unknown w_dtype %d", fn, w_dtype);
+    if (int s = check_k(fn, k)) return s;
+    REQUIRE_ALIGNED(a);
+    REQUIRE_ALIGNED(a_scales);
+    REQUIRE_ALIGNED(w);
+    REQUIRE_ALIGNED(c_bf16);
+    for (const void* q : {static_cast<const void*>(bias), static_cast<const void*>(gamma),
+                          static_cast<const void*>(gather_idx), static_cast<const void*>(scatter_idx)})
+      if ((reinterpret_cast<uintptr_t>(q) & 3u) != 0)
+        return fail(BSGEMM_ERR_BAD_ALIGNMENT, "%s: bias, gamma and index arrays must be 4-byte aligned", fn);
+    if (int s = check_limits(fn, m_total, n, k)) return s;
+    if (a_rows > MAX_ROWS || a_rows * (k / 2) > MAX_ROWS)
+      return fail(BSGEMM_ERR_RESOURCE, "%s: A (%lld rows of %lld code bytes) exceeds 2^31 bytes", fn,
+                  (long long)a_rows, (long long)(k / 2));
+    if ((m_total / 256 + num_groups) * ((n + 255) / 256) > MAX_ROWS)
+      return fail(BSGEMM_ERR_RESOURCE, "%s: too many tiles", fn);
+    int num_cus = 0;
+    if (int s = check_device(fn, &num_cus)) return s;
+    if (m_total == 0 || n == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bsg::GroupedCall call{num_groups, m_total, a_rows, n, k, a, a_scales, a_tscale, group_offsets,
+                          w, w_dtype == BSGEMM_W_F16, bias, gamma, gather_idx, scatter_idx, c_bf16};
+    return finish_launch(fn, bsg::launch_grouped(call, st), st);
   } catch (...) {
     return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
   }

@@ -1,4 +1,5 @@
-// Ragged grouped GEMM: NVFP4 activations x dense BF16 weights, BF16 output.
+// Ragged grouped GEMM: NVFP4 activations x dense BF16 or FP16 weights, BF16
+// output, with the optional epilogue and routing variants.
 //
 // Source: "Triton #11171 -- Why Two New NVFP4 Test Cases Produced Twelve
 // Tensor-Memory Failures", sections "Ragged mode added routing rather than a
@@ -6,7 +7,20 @@
 // grouped per slice (expert), and each slice meets its own dense operand.
 // That page stages an expanded (dequantised) copy of the NVFP4 operand for
 // the dense MMA.  Here each wave expands its own fragments in registers
-// instead, exactly, to BF16.
+// instead, exactly: to BF16 for BF16 weights (BF16 MFMA), to FP16 for FP16
+// weights (FP16 MFMA; e2m1 * e4m3 is exact in FP16 too).
+//
+// Variants (same page: "Scatter changes where output rows are written",
+// "Gamma adds a per-row scaling input", "The ordinary variants also exercise
+// the shared bias route", "Filter 3: gather variants are excluded"), for
+// logical row r of group g:
+//   A row read   src(r) = gather[r] (else r);
+//   y[r][n]      = (s_t * acc + bias[g][n]) * gamma[r];
+//   stored at    C[scatter[r]][n] (else C[r][n]).
+// Gather changes only the A load offsets (computed once per tile); the
+// epilogue reads the tile's gamma and destination rows from LDS.  Indices
+// outside [0, a_rows) (gather) or [0, m_total) (scatter) read zeros or skip
+// the store, so malformed indices stay inside the buffers.
 //
 // Scheduling.  The host knows only G, m_total and n; the row counts stay on
 // the device.  The grid therefore covers an upper bound on the number of
@@ -53,6 +67,74 @@ __device__ __forceinline__ int aswz(int row, int chunk) { return row * ARC + (ch
 // reading one chunk cover all 16 bank groups.
 __device__ __forceinline__ int wswz(int row, int chunk) { return row * WRC + (chunk ^ ((row >> 1) & 7)); }
 
+// Everything a grouped launch needs.  bias, gamma, gather and scatter may be
+// null.  W holds BF16 or FP16 bit patterns (the kernel's F16 parameter).
+struct GArgs {
+  const uint8_t* A;
+  const uint8_t* As;
+  const float* Ats;
+  const int32_t* off;
+  const uint16_t* W;
+  uint16_t* C;
+  const float* bias;      // [G][N]
+  const float* gamma;     // [M]
+  const int32_t* gather;  // [M], rows of A
+  const int32_t* scatter; // [M], rows of C
+  int G, M, a_rows, N, K, tiles_n;
+};
+
+// Operand type, exact dequantisation and MFMA of the two weight types.
+template <bool F16> struct GMath;
+template <> struct GMath<false> {
+  typedef v8bf vec;
+  // (1 + f) of the scale as FP32 bits (0 for a zero scale)
+  static __device__ __forceinline__ uint32_t mant(float s) { return __float_as_uint(scale_mantissa_f32(s)); }
+  static __device__ __forceinline__ vec dq8(uint32_t codes, float s, uint32_t m) {
+    return dequant8_bf16(codes, s, __uint_as_float(m));
+  }
+  static __device__ __forceinline__ v16f mfma(const vec& a, const vec& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct GMath<true> {
+  typedef v8h vec;
+  // (1 + f) of the scale as an FP16 pair (0 for a zero scale)
+  static __device__ __forceinline__ uint32_t mant(float s) { return scale_mantissa_f16x2(s); }
+  static __device__ __forceinline__ vec dq8(uint32_t codes, float s, uint32_t m) { return dequant8_f16(codes, s, m); }
+  static __device__ __forceinline__ v16f mfma(const vec& a, const vec& b, const v16f& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// Per-tile epilogue data in LDS: the destination row of each of the tile's
+// 256 logical rows (-1: no store) and its gamma.
+struct GEpi {
+  int dst[BM];
+  float gamma[BM];
+};
+
+// Thread t < BM fills row t of the tile starting at logical row r0 with
+// rows_a valid rows.
+__device__ __forceinline__ void fill_epi(const GArgs& p, int r0, int rows_a, int t, GEpi& e) {
+  if (t >= BM) return;
+  int dst = -1;
+  float gm = 1.0f;
+  if (t < rows_a) {
+    dst = p.scatter ? p.scatter[r0 + t] : r0 + t;
+    if ((unsigned)dst >= (unsigned)p.M) dst = -1;
+    if (p.gamma) gm = p.gamma[r0 + t];
+  }
+  e.dst[t] = dst;
+  e.gamma[t] = gm;
+}
+
+// Source row of logical tile row `row` (gather), or -1 when it reads zeros.
+__device__ __forceinline__ int gather_row(const GArgs& p, int r0, int rows_a, int row) {
+  if (row >= rows_a) return -1;
+  const int src = p.gather[r0 + row];
+  return (unsigned)src < (unsigned)p.a_rows ? src : -1;
+}
+
 // Find the group holding global m-tile `mt` (tiles of BM rows counted group by
 // group).  Run by wave 0.  Writes {group, first row, end row} to `info`, or
 // group = -1 when mt is past the last tile.
@@ -84,19 +166,20 @@ __device__ void find_tile(const int32_t* __restrict__ off, int G, int mt, int la
   if (lane == 0) info[0] = -1;
 }
 
-template <bool SCALE_DW>
-__global__ __launch_bounds__(NT, 1) void grouped_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
-    const int32_t* __restrict__ off, const uint16_t* __restrict__ W, uint16_t* __restrict__ C,
-    int G, int M, int N, int K, int tiles_n) {
+template <bool F16>
+__global__ __launch_bounds__(NT, 1) void grouped_kernel(const GArgs p) {
+  using GM = GMath<F16>;
+  using VT = typename GM::vec;
   __shared__ Smem sm;
+  __shared__ GEpi epi;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = t / tiles_n, nt = t - mt * tiles_n;
-  if (wave == 0) find_tile(off, G, mt, lane, sm.tile_info);
+  const int mt = t / p.tiles_n, nt = t - mt * p.tiles_n;
+  if (wave == 0) find_tile(p.off, p.G, mt, lane, sm.tile_info);
   __syncthreads();
   const int grp = sm.tile_info[0];
   if (grp < 0) return;                      // uniform over the workgroup
+  const int M = p.M, N = p.N, K = p.K;
   // Offsets are a documented precondition; clamping keeps even malformed
   // ones inside the A and C buffers.
   const int r0 = min(max(sm.tile_info[1], 0), M), r1 = min(max(sm.tile_info[2], r0), M);
@@ -105,14 +188,31 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
   const int KH = K / 2, KB = K / 16;
 
   const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
-  const auto ca_rsrc = make_rsrc(A + (int64_t)r0 * KH, rows_a * KH);
-  const auto sa_rsrc = make_rsrc(As + (int64_t)r0 * KB, rows_a * KB);
-  const auto w_rsrc = make_rsrc(W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  const bool gat = p.gather != nullptr;
+  // With gather the resources span all of A and rows are addressed by their
+  // source index; otherwise they span the tile's rows.
+  const auto ca_rsrc = make_rsrc(gat ? p.A : p.A + (int64_t)r0 * KH, (gat ? p.a_rows : rows_a) * KH);
+  const auto sa_rsrc = make_rsrc(gat ? p.As : p.As + (int64_t)r0 * KB, (gat ? p.a_rows : rows_a) * KB);
+  const auto w_rsrc = make_rsrc(p.W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  fill_epi(p, r0, rows_a, tid, epi);
 
-  // staging: A chunk (tid & 1) of rows (tid >> 1) + 128 i; A scale dword of
+  // staging: A chunk (tid & 1) of rows (tid >> 1) + 128 i; A scale bytes of
   // row tid; W chunk (tid & 7) of rows (tid >> 3) + 32 i.
   const int alc = tid & 1, alr = tid >> 1;
   const int wlc = tid & 7, wlr = tid >> 3;
+  int a_base[2], s_base;
+  bool a_ok[2], s_ok;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int src = gat ? gather_row(p, r0, rows_a, alr + 128 * i) : alr + 128 * i;
+    a_ok[i] = src >= 0;
+    a_base[i] = src * KH;
+  }
+  {
+    const int src = gat ? gather_row(p, r0, rows_a, tid) : tid;
+    s_ok = src >= 0;
+    s_base = src * KB;
+  }
   uint4 ra[2], rw[8];
   uint32_t sa_raw[2];
   // Loads only issue here (no branches, no uses); see sstore.
@@ -120,13 +220,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
     const int aofs = kt * AROWB + alc * 16 < KH ? kt * AROWB + alc * 16 : OOB;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      ra[i] = buffer_load_x4(ca_rsrc, aofs == OOB ? OOB : (alr + 128 * i) * KH + aofs);
-    if (SCALE_DW) {            // K % 64 == 0: the step's 4 scale bytes are one dword
-      sa_raw[0] = buffer_load_u32(sa_rsrc, tid * KB + kt * 4);
-    } else {                   // two pairs of blocks; a pair past K reads as 0
-      sa_raw[0] = buffer_load_u16(sa_rsrc, tid * KB + kt * 4);
-      sa_raw[1] = buffer_load_u16(sa_rsrc, kt * 4 + 2 < KB ? tid * KB + kt * 4 + 2 : OOB);
-    }
+      ra[i] = buffer_load_x4(ca_rsrc, (aofs == OOB || !a_ok[i]) ? OOB : a_base[i] + aofs);
+    // two pairs of blocks; a pair past K reads as 0
+    sa_raw[0] = buffer_load_u16(sa_rsrc, s_ok ? s_base + kt * 4 : OOB);
+    sa_raw[1] = buffer_load_u16(sa_rsrc, (s_ok && kt * 4 + 2 < KB) ? s_base + kt * 4 + 2 : OOB);
     const int wofs = kt * BK + wlc * 8 < K ? (kt * BK + wlc * 8) * 2 : OOB;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -136,7 +233,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       sm.a[buf][aswz(alr + 128 * i, alc)] = ra[i];
-    sm.as[buf][tid] = SCALE_DW ? sa_raw[0] : (sa_raw[0] | (sa_raw[1] << 16));
+    sm.as[buf][tid] = sa_raw[0] | (sa_raw[1] << 16);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       sm.w[buf][wswz(wlr + 32 * i, wlc)] = rw[i];
@@ -159,25 +256,26 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
     const int buf = kt & 1;
     if (kt + 1 < KT) gload(kt + 1);
     uint4 ca[4];
-    float s[4][2], mant[4][2];
+    float sc[4][2];
+    uint32_t mant[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + r;
       ca[i] = sm.a[buf][aswz(row, g)];
-      const uint32_t sc = sm.as[buf][row];
+      const uint32_t sw = sm.as[buf][row];
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        s[i][b] = e4m3_scale_value((sc >> (16 * g + 8 * b)) & 0xFFu);
-        mant[i][b] = scale_mantissa_f32(s[i][b]);
+        sc[i][b] = e4m3_scale_value((sw >> (16 * g + 8 * b)) & 0xFFu);
+        mant[i][b] = GM::mant(sc[i][b]);
       }
     }
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) {
-      v8bf av[4], bv[4];
+      VT av[4], bv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t d = sp == 0 ? ca[i].x : sp == 1 ? ca[i].y : sp == 2 ? ca[i].z : ca[i].w;
-        av[i] = dequant8_bf16(d, s[i][sp >> 1], mant[i][sp >> 1]);
+        av[i] = GM::dq8(d, sc[i][sp >> 1], mant[i][sp >> 1]);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -188,26 +286,29 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[i][j] = GM::mfma(av[i], bv[j], acc[i][j]);
     }
     if (kt + 1 < KT) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  const float alpha = *Ats;
+  const float alpha = *p.Ats;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int col = n0 + wn * 128 + j * 32 + r;
+    const float b = (p.bias && col < N) ? p.bias[(int64_t)grp * N + col] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + r;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = r0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (row < r1 && col < N)
-          C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+        const int lr = wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+        const int dst = epi.dst[lr];
+        float y = acc[i][j][v] * alpha;
+        if (p.bias) y += b;
+        if (p.gamma) y *= epi.gamma[lr];
+        if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -233,13 +334,13 @@ struct GRingSmem {
   uint4 w[GR_NS][BN * WRC];
   uint32_t as[GR_SBUF][BM * SB / 4];
   int tile_info[4];
+  GEpi epi;
 };
 
-template <int SB>
-__global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
-    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
-    const int32_t* __restrict__ off, const uint16_t* __restrict__ W, uint16_t* __restrict__ C,
-    int G, int M, int N, int K, int tiles_n) {
+template <int SB, bool F16>
+__global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
+  using GM = GMath<F16>;
+  using VT = typename GM::vec;
   constexpr int U = SB / 4;                  // steps per scale load
   __shared__ GRingSmem<SB> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -248,12 +349,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
   // from HBM about once and re-read from L2; A (small) is shared through the
   // infinity cache across panels.
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int mtiles = gridDim.x / tiles_n;
+  const int mtiles = gridDim.x / p.tiles_n;
   const int nt = t / mtiles, mt = t - nt * mtiles;
-  if (wave == 0) find_tile(off, G, mt, lane, sm.tile_info);
+  if (wave == 0) find_tile(p.off, p.G, mt, lane, sm.tile_info);
   __syncthreads();
   const int grp = sm.tile_info[0];
   if (grp < 0) return;                      // uniform over the workgroup
+  const int M = p.M, N = p.N, K = p.K;
   // Offsets are a documented precondition; clamping keeps even malformed
   // ones inside the A and C buffers.
   const int r0 = min(max(sm.tile_info[1], 0), M), r1 = min(max(sm.tile_info[2], r0), M);
@@ -261,19 +363,26 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
   const int KT = K / BK;                    // a positive multiple of U
   const int KH = K / 2, KB = K / 16;
   const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
-  const rsrc4_t ra = make_rsrc4(A + (int64_t)r0 * KH, rows_a * KH);
-  const rsrc4_t rsa = make_rsrc4(As + (int64_t)r0 * KB, rows_a * KB);
-  const rsrc4_t rw = make_rsrc4(W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  const bool gat = p.gather != nullptr;
+  // With gather the A resources span all of A and rows are addressed by
+  // their source index; otherwise they span the tile's rows.
+  const rsrc4_t ra = make_rsrc4(gat ? p.A : p.A + (int64_t)r0 * KH, (gat ? p.a_rows : rows_a) * KH);
+  const rsrc4_t rsa = make_rsrc4(gat ? p.As : p.As + (int64_t)r0 * KB, (gat ? p.a_rows : rows_a) * KB);
+  const rsrc4_t rw = make_rsrc4(p.W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  fill_epi(p, r0, rows_a, tid, sm.epi);   // visible after the prologue's barrier
 
   // Load geometry.  A instruction u covers rows 32 (2 wave + u) .. +31 (two
   // lanes per row); W instruction u covers rows 8 (8 wave + u) .. +7 (eight
   // lanes per row).  Each lane fetches the global chunk that the swizzle puts
   // in its LDS slot.
   int a_off[2];
+  bool a_ok[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int row = 32 * (2 * wave + u) + (lane >> 1);
-    a_off[u] = row * KH + (((lane & 1) ^ ((row >> 3) & 1)) * 16);
+    const int src = gat ? gather_row(p, r0, rows_a, row) : row;
+    a_ok[u] = src >= 0;
+    a_off[u] = src * KH + (((lane & 1) ^ ((row >> 3) & 1)) * 16);
   }
   int w_off[2];   // even and odd u differ in the swizzle; rows step by 16 per pair
 #pragma unroll
@@ -281,21 +390,23 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
     const int row = 8 * (8 * wave + u) + (lane >> 3);
     w_off[u] = row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
   }
-  const int s_off = (64 * wave + lane) * KB;
+  const int s_src = gat ? gather_row(p, r0, rows_a, 64 * wave + lane) : 64 * wave + lane;
+  const bool s_ok = s_src >= 0;
+  const int s_off = s_src * KB;
 
   auto issue = [&](int st, auto WITH_SCALES) {
     const int slot = st % GR_NS;
     const bool live = st < KT;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      dma_x4(ra, lds_addr(&sm.a[slot][64 * (2 * wave + u)]), live ? a_off[u] + st * AROWB : OOB);
+      dma_x4(ra, lds_addr(&sm.a[slot][64 * (2 * wave + u)]), (live && a_ok[u]) ? a_off[u] + st * AROWB : OOB);
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       dma_x4(rw, lds_addr(&sm.w[slot][64 * (8 * wave + u)]),
              live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
     if (decltype(WITH_SCALES)::value) {
       const int sbuf = (st / U) % GR_SBUF;
-      const int soff = live ? s_off + (st / U) * SB : OOB;
+      const int soff = (live && s_ok) ? s_off + (st / U) * SB : OOB;
       if (SB == 16) dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
       else dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
     }
@@ -309,7 +420,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
 
   struct AFrag {
     uint4 c[2];
-    float s[2][2], m[2][2];
+    float s[2][2];
+    uint32_t m[2][2];   // (1 + f) in the weight type's form (GMath::mant)
   };
   // A codes and decoded scales of stage st for this lane's 2 row fragments.
   // The step's 4 scale bytes are dword `in` of the row's SB-byte entry; lane
@@ -326,11 +438,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         f.s[i][b] = sv[b];
-        f.m[i][b] = scale_mantissa_f32(sv[b]);
+        f.m[i][b] = GM::mant(sv[b]);
       }
     }
   };
-  auto read_w = [&](int st, int sp, v8bf* bv) {
+  auto read_w = [&](int st, int sp, VT* bv) {
     const int slot = st % GR_NS;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -338,11 +450,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
       __builtin_memcpy(&bv[j], &q, 16);
     }
   };
-  auto dequant = [&](const AFrag& f, int sp, v8bf* av) {
+  auto dequant = [&](const AFrag& f, int sp, VT* av) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t d = sp == 0 ? f.c[i].x : sp == 1 ? f.c[i].y : sp == 2 ? f.c[i].z : f.c[i].w;
-      av[i] = dequant8_bf16(d, f.s[i][sp >> 1], f.m[i][sp >> 1]);
+      av[i] = GM::dq8(d, f.s[i][sp >> 1], f.m[i][sp >> 1]);
     }
   };
 
@@ -351,12 +463,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v16f{};
-  auto mfmas = [&](const v8bf* av, const v8bf* bv) {
+  auto mfmas = [&](const VT* av, const VT* bv) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 8; ++j) acc[i][j] = GM::mfma(av[i], bv[j], acc[i][j]);
   };
   auto interleave = [] {
 #pragma unroll
@@ -370,7 +481,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
   auto loads_of = [](int s_mod) { return GR_LOADS + (s_mod == 0 ? 1 : 0); };
 
   AFrag fa[2];
-  v8bf av[2][2], bv[2][8];
+  VT av[2][2], bv[2][8];
   // Step kt, kt % U == IN (static); fa[CUR] holds stage kt's A data, and
   // av[0] / bv[0] its sub-step 0 operands.
   auto step = [&](int kt, auto INC) {
@@ -441,9 +552,12 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
   }
 
   // Epilogue: C rows r0..r1 of this group, scaled by the tensor scale.
-  const float alpha = *Ats;
-  if (r0 + BM <= r1 && n0 + BN <= N) {
-    uint16_t* cw = C + (int64_t)(r0 + wave * 64 + g * 4) * N + n0 + r;
+  // Plain full tiles store rows in place without per-element checks; the
+  // ragged edge and every variant go through the tile's LDS row table.
+  const float alpha = *p.Ats;
+  const bool plain = !p.bias && !p.gamma && !p.scatter;
+  if (plain && r0 + BM <= r1 && n0 + BN <= N) {
+    uint16_t* cw = p.C + (int64_t)(r0 + wave * 64 + g * 4) * N + n0 + r;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -454,38 +568,50 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(
               (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 8; ++j) {
+      const int col = n0 + j * 32 + r;
+      const float b = (p.bias && col < N) ? p.bias[(int64_t)grp * N + col] : 0.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int col = n0 + j * 32 + r;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int row = r0 + wave * 64 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          if (row < r1 && col < N)
-            C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+          const int lr = wave * 64 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          const int dst = sm.epi.dst[lr];
+          float y = acc[i][j][v] * alpha;
+          if (p.bias) y += b;
+          if (p.gamma) y *= sm.epi.gamma[lr];
+          if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
         }
-      }
+    }
   }
 }
 
 }  // namespace
 
-hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
-                          const uint8_t* a, const uint8_t* as, const float* ats,
-                          const int32_t* offsets, const uint16_t* w, uint16_t* c,
-                          hipStream_t stream) {
-  const int tiles_n = (int)ceil_div(n, BN);
-  const int64_t mtiles_max = m_total / BM + num_groups;   // >= sum_g ceil(c_g / BM)
-  const dim3 grid((unsigned)(mtiles_max * tiles_n));
-  if (k % 256 == 0 && k > 0)
-    hipLaunchKernelGGL(grouped_ring_kernel<16>, grid, dim3(NT), 0, stream, a, as, ats, offsets, w, c,
-                       num_groups, (int)m_total, (int)n, (int)k, tiles_n);
-  else if (k % 64 == 0 && k > 0)
-    hipLaunchKernelGGL(grouped_ring_kernel<4>, grid, dim3(NT), 0, stream, a, as, ats, offsets, w, c,
-                       num_groups, (int)m_total, (int)n, (int)k, tiles_n);
-  else
-    hipLaunchKernelGGL(grouped_kernel<false>, grid, dim3(NT), 0, stream, a, as, ats, offsets, w, c,
-                       num_groups, (int)m_total, (int)n, (int)k, tiles_n);
+hipError_t launch_grouped(const GroupedCall& c, hipStream_t stream) {
+  GArgs p;
+  p.A = c.a; p.As = c.as; p.Ats = c.ats; p.off = c.offsets; p.W = c.w; p.C = c.c;
+  p.bias = c.bias; p.gamma = c.gamma; p.gather = c.gather; p.scatter = c.scatter;
+  p.G = c.num_groups; p.M = (int)c.m_total; p.a_rows = (int)c.a_rows; p.N = (int)c.n; p.K = (int)c.k;
+  p.tiles_n = (int)ceil_div(c.n, BN);
+  const int64_t mtiles_max = c.m_total / BM + c.num_groups;   // >= sum_g ceil(c_g / BM)
+  const dim3 grid((unsigned)(mtiles_max * p.tiles_n));
+  const int64_t k = c.k;
+  if (c.w_f16) {
+    if (k % 256 == 0 && k > 0)
+      hipLaunchKernelGGL((grouped_ring_kernel<16, true>), grid, dim3(NT), 0, stream, p);
+    else if (k % 64 == 0 && k > 0)
+      hipLaunchKernelGGL((grouped_ring_kernel<4, true>), grid, dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL(grouped_kernel<true>, grid, dim3(NT), 0, stream, p);
+  } else {
+    if (k % 256 == 0 && k > 0)
+      hipLaunchKernelGGL((grouped_ring_kernel<16, false>), grid, dim3(NT), 0, stream, p);
+    else if (k % 64 == 0 && k > 0)
+      hipLaunchKernelGGL((grouped_ring_kernel<4, false>), grid, dim3(NT), 0, stream, p);
+    else
+      hipLaunchKernelGGL(grouped_kernel<false>, grid, dim3(NT), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

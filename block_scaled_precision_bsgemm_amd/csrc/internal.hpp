@@ -26,10 +26,24 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* as, const float* ats, const uint8_t* b,
                              const uint8_t* bs, const float* bts, uint16_t* c,
                              hipStream_t stream);
-hipError_t launch_grouped(int num_groups, int64_t m_total, int64_t n, int64_t k,
-                          const uint8_t* a, const uint8_t* as, const float* ats,
-                          const int32_t* offsets, const uint16_t* w, uint16_t* c,
-                          hipStream_t stream);
+// One grouped launch: bias, gamma, gather and scatter may be null; w holds
+// BF16 (w_f16 false) or FP16 bit patterns.
+struct GroupedCall {
+  int num_groups;
+  int64_t m_total, a_rows, n, k;
+  const uint8_t* a;
+  const uint8_t* as;
+  const float* ats;
+  const int32_t* offsets;
+  const uint16_t* w;
+  bool w_f16;
+  const float* bias;
+  const float* gamma;
+  const int32_t* gather;
+  const int32_t* scatter;
+  uint16_t* c;
+};
+hipError_t launch_grouped(const GroupedCall& call, hipStream_t stream);
 hipError_t launch_w4a16(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream);
 

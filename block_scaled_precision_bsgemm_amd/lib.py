@@ -25,6 +25,8 @@ BSGEMM_ERR_LAUNCH = 6
 BSGEMM_NVFP4 = 1
 BSGEMM_MXFP8 = 2
 BSGEMM_MXFP4 = 3
+BSGEMM_W_BF16 = 1
+BSGEMM_W_F16 = 2
 
 # Symbols declared in include/bsgemm.h with their ctypes signatures.
 _i64, _p, _int = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
@@ -34,6 +36,8 @@ SIGNATURES = {
     "bsgemm_quantize_mxfp4": (_int, [_i64, _i64, _p, _p, _p, _p]),
     "bsgemm_run": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p, _p]),
     "bsgemm_grouped_run": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
+    "bsgemm_grouped_run_ex": (_int, [_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _p, _p, _p,
+                                     _p, _p]),
     "bsgemm_w4a16_run": (_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "bsgemm_status_string": (ctypes.c_char_p, [_int]),
     "bsgemm_last_error": (ctypes.c_char_p, []),
@@ -131,6 +135,22 @@ def bsgemm_grouped_run(a, a_scales, a_tscale, group_offsets, w_bf16, k, c=None, 
     c = _empty((m_total, n), torch.int16, a) if c is None else c
     _check(load().bsgemm_grouped_run(G, m_total, n, k, _ptr(a), _ptr(a_scales), _ptr(a_tscale),
                                      _ptr(group_offsets), _ptr(w_bf16), _ptr(c), _stream(stream)))
+    return c
+
+
+def bsgemm_grouped_run_ex(a, a_scales, a_tscale, group_offsets, w, k, w_dtype=BSGEMM_W_BF16, bias=None,
+                          gamma=None, gather_idx=None, scatter_idx=None, m_total=None, c=None, stream=None):
+    """Grouped NVFP4 A [a_rows, k] x dense W [G, n, k] (BF16 or FP16 bits) with optional
+    bias [G, n], gamma [m_total], gather_idx [m_total] and scatter_idx [m_total] -> C
+    [m_total, n] (BF16 bits).  m_total defaults to the gather length, else to a_rows."""
+    G, n = w.shape[0], w.shape[1]
+    a_rows = a.shape[0]
+    if m_total is None:
+        m_total = gather_idx.shape[0] if gather_idx is not None else a_rows
+    c = _empty((m_total, n), torch.int16, a) if c is None else c
+    _check(load().bsgemm_grouped_run_ex(G, m_total, n, k, a_rows, _ptr(a), _ptr(a_scales), _ptr(a_tscale),
+                                        _ptr(group_offsets), w_dtype, _ptr(w), _ptr(bias), _ptr(gamma),
+                                        _ptr(gather_idx), _ptr(scatter_idx), _ptr(c), _stream(stream)))
     return c
 
 

@@ -69,7 +69,7 @@ enum bsgemm_status {
   BSGEMM_OK = 0,
   BSGEMM_ERR_INVALID_ARG = 1,   /* null pointer, negative size, num_groups < 1 */
   BSGEMM_ERR_UNSUPPORTED = 2,   /* k % 32 != 0, unknown format, bad format/scale combination */
-  BSGEMM_ERR_BAD_ALIGNMENT = 3, /* a pointer required to be 16-byte aligned is not */
+  BSGEMM_ERR_BAD_ALIGNMENT = 3, /* a pointer is not aligned as its call requires */
   BSGEMM_ERR_DEVICE = 4,        /* no HIP device, or the current device is not gfx950 */
   BSGEMM_ERR_RESOURCE = 5,      /* no kernel configuration fits the problem */
   BSGEMM_ERR_LAUNCH = 6         /* the HIP runtime reported a launch failure */
@@ -221,6 +221,58 @@ int bsgemm_grouped_run(int num_groups, int64_t m_total, int64_t n, int64_t k,
                        const uint8_t* a, const uint8_t* a_scales, const float* a_tscale,
                        const int32_t* group_offsets, const uint16_t* w_bf16,
                        uint16_t* c_bf16, void* stream);
+
+/* Element type of the dense grouped operand. */
+enum bsgemm_wtype {
+  BSGEMM_W_BF16 = 1,
+  BSGEMM_W_F16 = 2
+};
+
+/*
+ * Ragged grouped GEMM with the routing and epilogue variants: NVFP4
+ * activations x dense BF16 or FP16 weights.  For logical row r of group g
+ * (off[g] <= r < off[g+1]):
+ *   src(r)  = gather_idx[r] if gather_idx is given, else r   (row of A read)
+ *   y[r][n] = (s_t * sum_k (e2m1 * e4m3)(A)[src(r)][k] * W[g][n][k] + bias[g][n]) * gamma[r]
+ *   C[dst(r)][n] = bf16_RNE(y[r][n]),  dst(r) = scatter_idx[r] if given, else r
+ * with FP32 accumulation and FP32 epilogue arithmetic; an absent bias adds 0
+ * and an absent gamma multiplies by 1.  Bias is added to the scaled product
+ * and gamma multiplies the sum: the order in which the page lists them.
+ * Source: "Triton #11171 -- Why Two New NVFP4 Test Cases Produced Twelve
+ * Tensor-Memory Failures", sections "Scatter changes where output rows are
+ * written" (a permutation of output rows), "Gamma adds a per-row scaling
+ * input", "The ordinary variants also exercise the shared bias route"
+ * (matmul + bias + optional gamma + optional scatter), "Filter 3: gather
+ * variants are excluded" (gathered activation rows) and the rhs_dtype sweep
+ * over bfloat16 and float16 in "The missing case was defined by shape,
+ * layout, and execution mode together".
+ *
+ * Arguments (as bsgemm_grouped_run, plus):
+ *   a_rows       rows of A (and of a_scales).  Must equal m_total when
+ *                gather_idx is NULL.
+ *   w_dtype      BSGEMM_W_BF16 or BSGEMM_W_F16: the bit patterns in w
+ *   w            device uint16[G][n][k], 16-byte aligned
+ *   bias         device float[G][n] or NULL
+ *   gamma        device float[m_total] or NULL
+ *   gather_idx   device int32[m_total] or NULL; entries in [0, a_rows)
+ *   scatter_idx  device int32[m_total] or NULL; a permutation of
+ *                [0, m_total), so every row of C is written once
+ *   bias, gamma and the index arrays need 4-byte alignment.
+ * Device-side preconditions (documented, not checked on the host): offsets
+ * as for bsgemm_grouped_run; index entries in range.  A gather entry out of
+ * range reads a zero row and a scatter entry out of range skips its store,
+ * so bad indices never touch memory outside the buffers; a scatter that is
+ * not a permutation leaves some rows of C unwritten.
+ * Sizes: m_total, n, k, a_rows >= 0, k % 32 == 0, a_rows * k / 2 < 2^31.
+ *   m_total == 0 or n == 0: BSGEMM_OK and nothing is launched.
+ * With all four of bias, gamma, gather_idx and scatter_idx NULL and
+ * w_dtype BSGEMM_W_BF16 this is bsgemm_grouped_run.
+ */
+int bsgemm_grouped_run_ex(int num_groups, int64_t m_total, int64_t n, int64_t k, int64_t a_rows,
+                          const uint8_t* a, const uint8_t* a_scales, const float* a_tscale,
+                          const int32_t* group_offsets, int w_dtype, const uint16_t* w,
+                          const float* bias, const float* gamma, const int32_t* gather_idx,
+                          const int32_t* scatter_idx, uint16_t* c_bf16, void* stream);
 
 /*
  * Small-M weight-only 4-bit GEMM: BF16 activations x NVFP4 weights.

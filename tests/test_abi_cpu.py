@@ -42,7 +42,7 @@ def test_status_strings_and_version(so):
                        (5, b"BSGEMM_ERR_RESOURCE"), (6, b"BSGEMM_ERR_LAUNCH")]:
         assert so.bsgemm_status_string(code) == name
     assert so.bsgemm_status_string(99) == b"unknown status"
-    assert so.bsgemm_version() == 200
+    assert so.bsgemm_version() == 300
 
 
 def run(so, fmt=L.BSGEMM_NVFP4, m=64, n=64, k=64, a=P, sa=P, ta=P, b=P, sb=P, tb=P, c=P):
@@ -107,6 +107,28 @@ def test_grouped_and_w4a16_validation(so):
     assert w(1, 64, 80, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert w(1, 64, 64, MIS, P, P, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert w(1, 64, 64, P, P, MIS, P, P, None) == L.BSGEMM_ERR_BAD_ALIGNMENT
+
+
+def test_grouped_ex_validation(so):
+    def gx(G=2, m=64, n=64, k=64, a_rows=64, a=P, sa=P, ta=P, off=P, wd=L.BSGEMM_W_BF16, w=P,
+           bias=None, gamma=None, gather=None, scatter=None, c=P):
+        return so.bsgemm_grouped_run_ex(G, m, n, k, a_rows, a, sa, ta, off, wd, w, bias, gamma, gather,
+                                        scatter, c, None)
+    assert gx(G=0) == L.BSGEMM_ERR_INVALID_ARG
+    assert gx(a_rows=-1) == L.BSGEMM_ERR_INVALID_ARG
+    assert gx(a_rows=32) == L.BSGEMM_ERR_INVALID_ARG          # a_rows != m without gather
+    assert b"a_rows must equal m_total" in so.bsgemm_last_error()
+    assert gx(ta=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert gx(off=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert gx(wd=7) == L.BSGEMM_ERR_UNSUPPORTED
+    assert gx(k=48) == L.BSGEMM_ERR_UNSUPPORTED
+    assert gx(w=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert gx(gamma=0x10002) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert gx(scatter=0x10001) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert gx(gather=P, a_rows=1 << 26, k=1024) == L.BSGEMM_ERR_RESOURCE   # A past 2^31 bytes
+    import torch
+    if not torch.cuda.is_available():
+        assert gx(gather=P, a_rows=32, bias=P, gamma=P, scatter=P, wd=L.BSGEMM_W_F16) == L.BSGEMM_ERR_DEVICE
 
 
 def test_last_error_is_per_thread(so):

@@ -385,6 +385,131 @@ def test_grouped_config_sampled(gpu_lib):
     assert not np.any(got == SENTINEL)
 
 
+# ------------------------------------------- grouped: routing / epilogue --
+
+def _variant_case(counts, n, k, seed, w_dtype, a_rows=None):
+    """Grouped inputs with every variant: gather from a_rows rows of A (with
+    repeats), a scatter permutation, bias [G, n] and gamma [m]."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    off = synth.offsets_from_counts(np.asarray(counts))
+    m = int(off[-1])
+    a_rows = m if a_rows is None else a_rows
+    x = synth.normal_f32((a_rows, k), seed + 1)
+    qa = Q.quantize_nvfp4(x)
+    wf = synth.normal_f32((len(counts), n, k), seed + 2, std=0.02)
+    w = synth.bf16_bits(wf) if w_dtype == "bf16" else wf.astype(np.float16).view(np.uint16)
+    v = {"gather": r.integers(0, a_rows, m).astype(np.int32),
+         "scatter": r.permutation(m).astype(np.int32),
+         "bias": (r.standard_normal((len(counts), n)) * 0.1).astype(np.float32),
+         "gamma": r.uniform(-2, 2, m).astype(np.float32)}
+    return qa, off, w, v
+
+
+def _gpu_grouped_ex(qa, off, w, k, w_dtype, v, use, m):
+    c = out_bf16(m, w.shape[1])
+    opt = {key: (dev(v[key]) if key in use else None) for key in ("bias", "gamma", "gather", "scatter")}
+    L.bsgemm_grouped_run_ex(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)), dev(off), dev(w), k,
+                            w_dtype=L.BSGEMM_W_F16 if w_dtype == "f16" else L.BSGEMM_W_BF16,
+                            bias=opt["bias"], gamma=opt["gamma"], gather_idx=opt["gather"],
+                            scatter_idx=opt["scatter"], m_total=m, c=c)
+    return u16(c)
+
+
+def _ref_ex(qa, off, w, w_dtype, v, use, rows=None):
+    return G.grouped_nvfp4_ex(*qa, off, w, w_dtype, *(v[key] if key in use else None
+                                                      for key in ("bias", "gamma", "gather", "scatter")),
+                              out_rows=rows)
+
+
+ALL = ("bias", "gamma", "gather", "scatter")
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("k", [96, 320, 512])
+def test_grouped_ex_all_variants(gpu_lib, w_dtype, k):
+    """bias + gamma + gather (from fewer A rows than m, with repeats) + scatter,
+    on the register-staged (K = 96), 4-byte-scale ring (K % 64) and
+    16-byte-scale ring (K % 256) kernels, BF16 and FP16 weights."""
+    counts, n = [77, 256, 0, 300], 260
+    m = sum(counts)
+    qa, off, w, v = _variant_case(counts, n, k, 700 + k, w_dtype, a_rows=500)
+    say("grouped_ex all variants", w_dtype, counts, n, k)
+    c = _gpu_grouped_ex(qa, off, w, k, w_dtype, v, ALL, m)
+    assert_ok(G.check(c, *_ref_ex(qa, off, w, w_dtype, v, ALL)), f"grouped_ex {w_dtype} k={k}")
+    assert not np.any(c == SENTINEL)
+
+
+@pytest.mark.parametrize("use", [(), ("bias",), ("gamma",), ("gather",), ("scatter",), ("bias", "scatter")])
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+def test_grouped_ex_single_variants(gpu_lib, use, w_dtype):
+    counts, n, k = [300, 0, 5, 256], 136, 256
+    m = sum(counts)
+    qa, off, w, v = _variant_case(counts, n, k, 800 + len(use), w_dtype)
+    say("grouped_ex", w_dtype, use)
+    c = _gpu_grouped_ex(qa, off, w, k, w_dtype, v, use, m)
+    assert_ok(G.check(c, *_ref_ex(qa, off, w, w_dtype, v, use)), f"grouped_ex {w_dtype} {use}")
+
+
+def test_grouped_ex_plain_equals_grouped_run(gpu_lib):
+    qa, off, w = _grouped_case([600, 0, 0, 900], 512, 256, 31)
+    m = int(off[-1])
+    say("grouped_ex plain vs grouped_run")
+    c1 = _gpu_grouped(qa, off, w, 256)
+    c2 = _gpu_grouped_ex(qa, off, w, 256, "bf16", {}, (), m)
+    assert np.array_equal(c1, c2)
+
+
+def test_grouped_ex_out_of_range_indices(gpu_lib):
+    """A gather entry outside [0, a_rows) reads a zero row; a scatter entry
+    outside [0, m) skips its store (that physical row keeps its old value)."""
+    counts, n, k = [100, 60], 64, 128
+    m = sum(counts)
+    qa, off, w, v = _variant_case(counts, n, k, 901, "bf16", a_rows=90)
+    v["gather"][7] = 90            # == a_rows: out of range
+    v["gather"][130] = -3
+    lost = int(v["scatter"][11])
+    v["scatter"][11] = m + 5       # physical row `lost` is then never written
+    say("grouped_ex out-of-range indices")
+    c = _gpu_grouped_ex(qa, off, w, k, "bf16", v, ALL, m)
+    # reference: the bad gather entries read an appended all-zero row of A
+    za = (np.concatenate([qa[0], np.zeros((1, k // 2), np.uint8)]),
+          np.concatenate([qa[1], np.zeros((1, k // 16), np.uint8)]), qa[2])
+    g2 = v["gather"].copy()
+    g2[[7, 130]] = 90
+    s2 = v["scatter"].copy()
+    s2[11] = lost
+    cref, t = G.grouped_nvfp4_ex(*za, off, w, "bf16", v["bias"], v["gamma"], g2, s2)
+    keep = np.arange(m) != lost
+    assert_ok(G.check(c[keep], cref[keep], t[keep]), "grouped_ex out-of-range indices")
+    assert np.all(c[lost] == SENTINEL)
+
+
+def test_grouped_ex_config_sampled(gpu_lib):
+    """The 32-group config (m = 16384, K = 7168, N = 2048) with FP16 weights and
+    every variant (gather over all 16384 rows, random permutation scatter,
+    bias, gamma); sampled physical rows, all columns."""
+    x, off, w_bf = synth.grouped_inputs()
+    del w_bf
+    r = np.random.Generator(np.random.PCG64(4100))
+    m, n, k, G_ = 16384, 2048, 7168, 32
+    w = synth.normal_f32((G_, n, k), synth.SEEDS["grouped.W"], std=0.02).astype(np.float16).view(np.uint16)
+    v = {"gather": r.integers(0, m, m).astype(np.int32), "scatter": r.permutation(m).astype(np.int32),
+         "bias": (r.standard_normal((G_, n)) * 0.1).astype(np.float32),
+         "gamma": r.uniform(-2, 2, m).astype(np.float32)}
+    ca, sa, ta = L.bsgemm_quantize_nvfp4(dev(x))
+    del x
+    say("grouped_ex 32 x (2048 x 7168) f16, all variants")
+    c = out_bf16(m, n)
+    L.bsgemm_grouped_run_ex(ca, sa, ta, dev(off), dev(w), k, w_dtype=L.BSGEMM_W_F16, bias=dev(v["bias"]),
+                            gamma=dev(v["gamma"]), gather_idx=dev(v["gather"]), scatter_idx=dev(v["scatter"]),
+                            c=c)
+    got = u16(c)
+    rows = _sample(m, 384, 22)
+    qa = (ca.cpu().numpy(), sa.cpu().numpy(), np.float32(ta.item()))
+    assert_ok(G.check(got[rows], *_ref_ex(qa, off, w, "f16", v, ALL, rows=rows)), "grouped_ex config sampled")
+    assert not np.any(got == SENTINEL)
+
+
 # ---------------------------------------------------------------- W4A16 --
 
 def _gpu_w4a16(x, qw, m):
