@@ -136,7 +136,7 @@ int check_limits(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k) {
 
 extern "C" {
 
-int bsgemm_version(void) { return 300; }   // 0.3.0: grouped variants
+int bsgemm_version(void) { return 400; }   // 0.4.0: W4A16 configurations
 
 const char* bsgemm_status_string(int status) {
   switch (status) {
@@ -348,31 +348,91 @@ int bsgemm_grouped_run_ex(int num_groups, int64_t m_total, int64_t n, int64_t k,
   }
 }
 
+}  // extern "C"
+
+namespace {
+
+// Configuration forced through the environment for bsgemm_w4a16_run
+// (BSGEMM_W4A16_FORCE_CONFIG = an id or a name): -1 when unset, -2 when set
+// to something that names no configuration.
+int forced_w4a16_config() {
+  const char* e = std::getenv("BSGEMM_W4A16_FORCE_CONFIG");
+  if (e == nullptr || e[0] == '\0') return -1;
+  const int n = bsg::w4a16_num_configs();
+  for (int i = 0; i < n; ++i)
+    if (std::strcmp(e, bsg::w4a16_config_name(i)) == 0) return i;
+  char* end = nullptr;
+  const long v = std::strtol(e, &end, 10);
+  if (end != e && *end == '\0' && v >= 0 && v < n) return (int)v;
+  return -2;
+}
+
+// Shared body of the W4A16 entry points; config -1 = the selector's choice.
+int w4a16_call(const char* fn, int config, int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
+               const uint8_t* w, const uint8_t* w_scales, const float* w_tscale, uint16_t* c_bf16,
+               void* stream) {
+  if (m < 0 || n < 0 || k < 0) return fail(BSGEMM_ERR_INVALID_ARG, "%s: negative size", fn);
+  REQUIRE_PTR(x_bf16, m * k);
+  REQUIRE_PTR(w, n * k);
+  REQUIRE_PTR(w_scales, n * k);
+  REQUIRE_PTR(c_bf16, m * n);
+  if (w_tscale == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: w_tscale is NULL", fn);
+  if (config >= bsg::w4a16_num_configs() || config < -1)
+    return fail(BSGEMM_ERR_UNSUPPORTED, "%s: unknown configuration %d", fn, config);
+  if (int s = check_k(fn, k)) return s;
+  REQUIRE_ALIGNED(x_bf16);
+  REQUIRE_ALIGNED(w);
+  REQUIRE_ALIGNED(w_scales);
+  REQUIRE_ALIGNED(c_bf16);
+  if (int s = check_limits(fn, m, n, k)) return s;
+  const int cfg = config >= 0 ? config : bsg::w4a16_select(m, n, k);
+  if (m > bsg::w4a16_config_max_m(cfg))
+    return fail(BSGEMM_ERR_RESOURCE, "%s: configuration %s takes m <= %d", fn, bsg::w4a16_config_name(cfg),
+                bsg::w4a16_config_max_m(cfg));
+  int num_cus = 0;
+  if (int s = check_device(fn, &num_cus)) return s;
+  if (m == 0 || n == 0) return ok();
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return finish_launch(fn, bsg::launch_w4a16(cfg, m, n, k, x_bf16, w, w_scales, w_tscale, c_bf16, st), st);
+}
+
+}  // namespace
+
+extern "C" {
+
 int bsgemm_w4a16_run(int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16, const uint8_t* w,
                      const uint8_t* w_scales, const float* w_tscale, uint16_t* c_bf16,
                      void* stream) {
   static const char* fn = "bsgemm_w4a16_run";
   try {
-    if (m < 0 || n < 0 || k < 0) return fail(BSGEMM_ERR_INVALID_ARG, "%s: negative size", fn);
-    REQUIRE_PTR(x_bf16, m * k);
-    REQUIRE_PTR(w, n * k);
-    REQUIRE_PTR(w_scales, n * k);
-    REQUIRE_PTR(c_bf16, m * n);
-    if (w_tscale == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: w_tscale is NULL", fn);
-    if (int s = check_k(fn, k)) return s;
-    REQUIRE_ALIGNED(x_bf16);
-    REQUIRE_ALIGNED(w);
-    REQUIRE_ALIGNED(w_scales);
-    REQUIRE_ALIGNED(c_bf16);
-    if (int s = check_limits(fn, m, n, k)) return s;
-    int num_cus = 0;
-    if (int s = check_device(fn, &num_cus)) return s;
-    if (m == 0 || n == 0) return ok();
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    return finish_launch(fn, bsg::launch_w4a16(m, n, k, x_bf16, w, w_scales, w_tscale, c_bf16, st), st);
+    const int forced = forced_w4a16_config();
+    if (forced == -2)
+      return fail(BSGEMM_ERR_UNSUPPORTED, "%s: BSGEMM_W4A16_FORCE_CONFIG names no configuration", fn);
+    return w4a16_call(fn, forced, m, n, k, x_bf16, w, w_scales, w_tscale, c_bf16, stream);
   } catch (...) {
     return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
   }
+}
+
+int bsgemm_w4a16_run_config(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
+                            const uint8_t* w, const uint8_t* w_scales, const float* w_tscale,
+                            uint16_t* c_bf16, void* stream) {
+  static const char* fn = "bsgemm_w4a16_run_config";
+  try {
+    if (config < 0) return fail(BSGEMM_ERR_UNSUPPORTED, "%s: unknown configuration %d", fn, config);
+    return w4a16_call(fn, config, m, n, k, x_bf16, w, w_scales, w_tscale, c_bf16, stream);
+  } catch (...) {
+    return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
+  }
+}
+
+int bsgemm_w4a16_num_configs(void) { return bsg::w4a16_num_configs(); }
+
+const char* bsgemm_w4a16_config_name(int config) { return bsg::w4a16_config_name(config); }
+
+int bsgemm_w4a16_select(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 0 || k % 32 != 0) return -1;
+  return bsg::w4a16_select(m, n, k);
 }
 
 }  // extern "C"

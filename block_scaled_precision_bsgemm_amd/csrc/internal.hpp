@@ -44,7 +44,13 @@ struct GroupedCall {
   uint16_t* c;
 };
 hipError_t launch_grouped(const GroupedCall& call, hipStream_t stream);
-hipError_t launch_w4a16(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
+// W4A16 configurations: count, names, largest m each accepts, the selector,
+// and a launch of one configuration (config must be a valid id).
+int w4a16_num_configs();
+const char* w4a16_config_name(int config);
+int w4a16_config_max_m(int config);
+int w4a16_select(int64_t m, int64_t n, int64_t k);
+hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream);
 
 }  // namespace bsg

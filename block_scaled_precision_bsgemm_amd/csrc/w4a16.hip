@@ -23,6 +23,7 @@ typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 
 // ------------------------------------------------------------------ m == 1
+// (one X row per blockIdx.y)
 //
 // Wave = GV_ROWS weight rows.  In each 4096-element chunk of K, lane l owns K
 // [32 l, 32 l + 32) and [2048 + 32 l, 2048 + 32 l + 32): one 16-byte code
@@ -98,6 +99,10 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     const float* __restrict__ Wts, uint16_t* __restrict__ C, int N, int K) {
   constexpr int R = GV_ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // row blockIdx.y of X and C (the vector-ALU path forced on m > 1 re-reads
+  // W once per row)
+  X += (int64_t)blockIdx.y * K;
+  C += (int64_t)blockIdx.y * N;
   const int n0 = (blockIdx.x * GV_WAVES + wave) * R;
   const int KH = K / 2, KB = K / 16;
   const int rows = max(0, min(N - n0, R));
@@ -343,11 +348,20 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
   }
 }
 
+constexpr int64_t kW4Workgroups = 256;   // one wave of workgroups: the MI355X CU count
+
+// "fit" tile width along N: the narrowest W slab (16..64 rows) for which the
+// whole grid still fits in one wave of workgroups.
+int64_t w4a16_fit_nb(int64_t m, int64_t n, int mt) {
+  const int64_t per_mtile = std::max<int64_t>(1, kW4Workgroups / ceil_div(m, mt));   // n tiles allowed
+  return std::min<int64_t>(64, std::max<int64_t>(16, ceil_div(n, per_mtile)));
+}
+
 template <int MT, int TP, int NSLOT, int RING>
 void launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w, const uint8_t* ws,
-                   const float* wts, uint16_t* c, hipStream_t stream) {
-  // W rows per workgroup: about one workgroup per CU for the W slab, 16..64
-  const int nb = (int)std::min<int64_t>(64, std::max<int64_t>(16, ceil_div(n, 256)));
+                   const float* wts, uint16_t* c, int nb_forced, hipStream_t stream) {
+  // W rows per workgroup (the tile width along N): forced, or the fit width
+  const int nb = nb_forced > 0 ? nb_forced : (int)w4a16_fit_nb(m, n, MT);
   const int n_tiles = (int)ceil_div(n, nb), m_tiles = (int)ceil_div(m, MT);
   const dim3 grid((unsigned)(n_tiles * m_tiles));
   if (k % 256 == 0)
@@ -360,17 +374,98 @@ void launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uin
 
 }  // namespace
 
-hipError_t launch_w4a16(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
+// ------------------------------------------------------------ dispatch
+//
+// The configurations a W4A16 call can run, the selector, and a forced path
+// that runs any configuration on any shape: the calibration method of "Add
+// sm121 (GB10) tier to the 4-bit GEMM dispatch heuristic", tile-selection
+// follow-up (one build runs every legal tile on every shape through the same
+// forced path, and the selector is changed only where rechecked measurements
+// support a rule).  Every configuration is legal for every shape the C ABI
+// accepts (the vector-ALU one for m <= 65535), and the dispatch below has a
+// final else: no configuration id can launch nothing.
+
+namespace {
+
+struct W4Config {
+  const char* name;
+  int mt;   // 0: vector-ALU gemv (one X row per grid row); else the MFMA kernel's m tile
+  int nb;   // W rows per workgroup; 0 = the fit width (w4a16_fit_nb)
+};
+
+constexpr W4Config kW4Configs[] = {
+    {"valu_gemv", 0, 0},
+    {"mfma_m16_nfit", 16, 0}, {"mfma_m16_n16", 16, 16}, {"mfma_m16_n32", 16, 32}, {"mfma_m16_n64", 16, 64},
+    {"mfma_m32_nfit", 32, 0}, {"mfma_m32_n16", 32, 16}, {"mfma_m32_n32", 32, 32}, {"mfma_m32_n64", 32, 64},
+    {"mfma_m64_nfit", 64, 0}, {"mfma_m64_n16", 64, 16}, {"mfma_m64_n32", 64, 32}, {"mfma_m64_n64", 64, 64},
+};
+constexpr int kW4NumConfigs = sizeof(kW4Configs) / sizeof(kW4Configs[0]);
+
+}  // namespace
+
+int w4a16_num_configs() { return kW4NumConfigs; }
+
+const char* w4a16_config_name(int config) {
+  return (config >= 0 && config < kW4NumConfigs) ? kW4Configs[config].name : nullptr;
+}
+
+int w4a16_config_max_m(int config) { return kW4Configs[config].mt == 0 ? 65535 : (1 << 30); }
+
+// The selector, fitted to rechecked calibration measurements (N x K in
+// {14336 x 4096, 4096 x 14336, 4096 x 4096, 1536 x 8960}) and checked on
+// held-out shapes (2048 x 8192, 3072 x 4096, 5120 x 4096, 8192 x 2048,
+// 896 x 4864, 6144 x 4096, 10240 x 2560, 2560 x 10240, 1024 x 1024), M from 1
+// to 256.  One rule with a physical reason:
+//   - vector ALU for m <= 2, or m <= 8 with m * n <= 24576: it re-reads W
+//     once per row (from the infinity cache) but has no fixed MFMA-pipeline
+//     cost;
+//   - otherwise the MFMA kernel, whose workgroups each hold a whole CU.
+//     While the grid fits in one wave of workgroups (one per CU), time
+//     follows the work per workgroup: take the smallest m tile whose grid
+//     fits with 64-row W slabs, then the narrowest slab that still fits (the
+//     fit width), which fills the wave.
+//   - If no m tile fits, 64-row slabs and the m tile with the fewest
+//     weighted waves: a wave of 16-, 32- and 64-row tiles costs about 0.8,
+//     1 and 1.5 (measured: workgroup time is mostly the W stream, not the
+//     MFMA work); ties go to the larger tile.
+// The previous rule (m tile by m alone, slab width from n alone) was within
+// 3% only for n >= 12288; at n = 4096 its 16-row slabs re-read X for little W
+// and ran up to 3.4x slower.
+int w4a16_config_id(int mt, int nb) {
+  const int base = mt == 16 ? 1 : mt == 32 ? 5 : 9;
+  return base + (nb == 0 ? 0 : nb == 16 ? 1 : nb == 32 ? 2 : 3);
+}
+
+int w4a16_select(int64_t m, int64_t n, int64_t k) {
+  (void)k;
+  if (m <= 2 || (m <= 8 && m * n <= 24576)) return 0;   // valu_gemv
+  for (int mt : {16, 32, 64})
+    if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) return w4a16_config_id(mt, 0);
+  int best = 64;
+  double best_cost = 0;
+  for (int mt : {64, 32, 16}) {
+    const double weight = mt == 16 ? 0.8 : mt == 32 ? 1.0 : 1.5;
+    const double cost = weight * (double)ceil_div(ceil_div(n, 64) * ceil_div(m, mt), kW4Workgroups);
+    if (mt == 64 || cost < best_cost) {
+      best = mt;
+      best_cost = cost;
+    }
+  }
+  return w4a16_config_id(best, 64);
+}
+
+hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream) {
-  if (m == 1) {
-    hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)ceil_div(n, GV_ROWS * GV_WAVES)), dim3(64 * GV_WAVES), 0,
-                       stream, x, w, ws, wts, c, (int)n, (int)k);
-  } else if (m <= 16) {
-    launch_skinny<16, 2, 8, 1>(m, n, k, x, w, ws, wts, c, stream);
-  } else if (m <= 32) {
-    launch_skinny<32, 2, 4, 1>(m, n, k, x, w, ws, wts, c, stream);
+  const W4Config& cf = kW4Configs[config];
+  if (cf.mt == 0) {
+    hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)ceil_div(n, GV_ROWS * GV_WAVES), (unsigned)m), dim3(64 * GV_WAVES),
+                       0, stream, x, w, ws, wts, c, (int)n, (int)k);
+  } else if (cf.mt == 16) {
+    launch_skinny<16, 2, 8, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+  } else if (cf.mt == 32) {
+    launch_skinny<32, 2, 4, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else {
-    launch_skinny<64, 4, 4, 2>(m, n, k, x, w, ws, wts, c, stream);
+    launch_skinny<64, 4, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   }
   return hipGetLastError();
 }

@@ -39,6 +39,10 @@ SIGNATURES = {
     "bsgemm_grouped_run_ex": (_int, [_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _p, _p, _p,
                                      _p, _p]),
     "bsgemm_w4a16_run": (_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "bsgemm_w4a16_run_config": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
+    "bsgemm_w4a16_num_configs": (_int, []),
+    "bsgemm_w4a16_config_name": (ctypes.c_char_p, [_int]),
+    "bsgemm_w4a16_select": (_int, [_i64, _i64, _i64]),
     "bsgemm_status_string": (ctypes.c_char_p, [_int]),
     "bsgemm_last_error": (ctypes.c_char_p, []),
     "bsgemm_version": (_int, []),
@@ -162,6 +166,32 @@ def bsgemm_w4a16_run(x_bf16, w, w_scales, w_tscale, c=None, stream=None):
     _check(load().bsgemm_w4a16_run(m, n, k, _ptr(x_bf16), _ptr(w), _ptr(w_scales), _ptr(w_tscale),
                                    _ptr(c), _stream(stream)))
     return c
+
+
+def bsgemm_w4a16_run_config(config, x_bf16, w, w_scales, w_tscale, c=None, stream=None):
+    """bsgemm_w4a16_run with configuration `config` (id or name) forced."""
+    if isinstance(config, str):
+        config = w4a16_config_id(config)
+    m, k = x_bf16.shape
+    n = w.shape[0]
+    c = _empty((m, n), torch.int16, x_bf16) if c is None else c
+    _check(load().bsgemm_w4a16_run_config(config, m, n, k, _ptr(x_bf16), _ptr(w), _ptr(w_scales),
+                                          _ptr(w_tscale), _ptr(c), _stream(stream)))
+    return c
+
+
+def w4a16_configs():
+    """Names of the W4A16 configurations, indexed by id."""
+    lib = load()
+    return [lib.bsgemm_w4a16_config_name(i).decode() for i in range(lib.bsgemm_w4a16_num_configs())]
+
+
+def w4a16_config_id(name):
+    return w4a16_configs().index(name)
+
+
+def bsgemm_w4a16_select(m, n, k):
+    return load().bsgemm_w4a16_select(m, n, k)
 
 
 def version() -> int:

@@ -296,6 +296,44 @@ int bsgemm_w4a16_run(int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
                      const uint8_t* w, const uint8_t* w_scales, const float* w_tscale,
                      uint16_t* c_bf16, void* stream);
 
+/*
+ * W4A16 configurations and a forced path, for calibrating the selector the
+ * way "Add sm121 (GB10) tier to the 4-bit GEMM dispatch heuristic",
+ * tile-selection follow-up, does: one build runs every legal configuration
+ * on every shape through the same forced path, the selector's decisions can
+ * be enumerated exhaustively on the host, and no configuration id launches
+ * nothing (an invalid one is an error, never a silent no-op).
+ *
+ * Configurations (ids 0 .. bsgemm_w4a16_num_configs() - 1):
+ *   "valu_gemv"          vector-ALU dot products, one X row per grid row
+ *                        (re-reads W once per row; m <= 65535);
+ *   "mfma_m{16,32,64}_n{fit,16,32,64}"
+ *                        BF16 MFMA kernel with that m tile and that many W
+ *                        rows per workgroup (the tile width along N); "fit"
+ *                        takes the narrowest width (16..64) whose grid fits
+ *                        in one wave of 256 workgroups.
+ * bsgemm_w4a16_run runs bsgemm_w4a16_select(m, n, k), unless the environment
+ * variable BSGEMM_W4A16_FORCE_CONFIG holds a configuration id or name; a
+ * value that names none makes the call fail with BSGEMM_ERR_UNSUPPORTED.
+ * Every configuration computes the same C within the documented tolerance.
+ */
+int bsgemm_w4a16_num_configs(void);
+
+/* Static name of configuration `config`; NULL if there is none. */
+const char* bsgemm_w4a16_config_name(int config);
+
+/* The configuration bsgemm_w4a16_run picks for (m, n, k) without an
+ * override; host-only, no device needed.  -1 for negative sizes or
+ * k % 32 != 0. */
+int bsgemm_w4a16_select(int64_t m, int64_t n, int64_t k);
+
+/* bsgemm_w4a16_run with configuration `config` forced (the environment
+ * override is ignored).  BSGEMM_ERR_UNSUPPORTED for an unknown id;
+ * BSGEMM_ERR_RESOURCE when m exceeds what the configuration takes. */
+int bsgemm_w4a16_run_config(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
+                            const uint8_t* w, const uint8_t* w_scales, const float* w_tscale,
+                            uint16_t* c_bf16, void* stream);
+
 /* Static name of a status code ("BSGEMM_OK", ...); "unknown status" otherwise. */
 const char* bsgemm_status_string(int status);
 

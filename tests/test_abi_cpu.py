@@ -42,7 +42,7 @@ def test_status_strings_and_version(so):
                        (5, b"BSGEMM_ERR_RESOURCE"), (6, b"BSGEMM_ERR_LAUNCH")]:
         assert so.bsgemm_status_string(code) == name
     assert so.bsgemm_status_string(99) == b"unknown status"
-    assert so.bsgemm_version() == 300
+    assert so.bsgemm_version() == 400
 
 
 def run(so, fmt=L.BSGEMM_NVFP4, m=64, n=64, k=64, a=P, sa=P, ta=P, b=P, sb=P, tb=P, c=P):
@@ -129,6 +129,61 @@ def test_grouped_ex_validation(so):
     import torch
     if not torch.cuda.is_available():
         assert gx(gather=P, a_rows=32, bias=P, gamma=P, scatter=P, wd=L.BSGEMM_W_F16) == L.BSGEMM_ERR_DEVICE
+
+
+def test_w4a16_configs_and_exhaustive_selector(so):
+    n_cfg = so.bsgemm_w4a16_num_configs()
+    names = [so.bsgemm_w4a16_config_name(i).decode() for i in range(n_cfg)]
+    assert n_cfg == 13 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
+    assert so.bsgemm_w4a16_config_name(n_cfg) is None and so.bsgemm_w4a16_config_name(-1) is None
+    tile = {nm: (0 if nm == "valu_gemv" else int(nm.split("_")[1][1:])) for nm in names}
+
+    def mtile(nm):
+        return int(nm.split("_")[1][1:])
+
+    def grid(m, n, mt, nb):
+        return -(-n // nb) * -(-m // mt)
+    # Exhaustive over the grid, checking the selector's stated rule by its
+    # properties: the vector ALU exactly for m <= 2, or m <= 8 with
+    # m * n <= 24576; an MFMA pick with the fit width has an m tile whose
+    # grid fits one wave of 256 workgroups with 64-row slabs, and no smaller
+    # tile does; otherwise no tile fits and the pick uses 64-row slabs.
+    decisions = 0
+    for n in (1, 64, 896, 1536, 3072, 4096, 5120, 8192, 10240, 14336, 65536):
+        for k in (32, 4096, 14336):
+            for m in list(range(0, 130)) + [192, 256, 384, 1024, 1 << 20]:
+                c = so.bsgemm_w4a16_select(m, n, k)
+                decisions += 1
+                assert 0 <= c < n_cfg
+                nm = names[c]
+                assert (nm == "valu_gemv") == (m <= 2 or (m <= 8 and m * n <= 24576)), (m, n, nm)
+                if nm == "valu_gemv":
+                    continue
+                fits = [t for t in (16, 32, 64) if grid(m, n, t, 64) <= 256]
+                if fits:
+                    assert nm == f"mfma_m{fits[0]}_nfit", (m, n, nm)
+                else:
+                    assert nm.endswith("_n64"), (m, n, nm)
+    assert decisions == 11 * 3 * 135
+    assert so.bsgemm_w4a16_select(4, 64, 48) == -1 and so.bsgemm_w4a16_select(-1, 64, 64) == -1
+
+
+def test_w4a16_forced_config_validation(so, monkeypatch):
+    rc = so.bsgemm_w4a16_run_config
+    assert rc(99, 1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert rc(-1, 1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert rc(0, 70000, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_RESOURCE     # vector ALU: m <= 65535
+    assert b"valu_gemv" in so.bsgemm_last_error()
+    assert rc(3, 1, 64, 80, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED      # k % 32
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "no_such_tile")
+    assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    assert b"FORCE_CONFIG" in so.bsgemm_last_error()
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "13")
+    assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "mfma_m32_n16")
+        assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_DEVICE
 
 
 def test_last_error_is_per_thread(so):

@@ -546,6 +546,39 @@ def test_w4a16_config_sampled(gpu_lib, m):
     assert not np.any(got == SENTINEL)
 
 
+def _w4_case(m, n, k, seed):
+    x = synth.bf16_bits(synth.normal_f32((m, k), seed))
+    qw = Q.quantize_nvfp4(synth.normal_f32((n, k), seed + 1, std=0.02))
+    return x, qw
+
+
+@pytest.mark.parametrize("config", range(13))
+def test_w4a16_every_config(gpu_lib, config):
+    """Each configuration, forced, on shapes it would never be chosen for:
+    ragged m, n and K tails (K % 256 != 0 uses per-lane scale loads)."""
+    name = L.w4a16_configs()[config]
+    for (m, n, k) in [(1, 300, 1024), (5, 72, 2048 + 96), (33, 129, 512), (70, 260, 4096 + 256)]:
+        x, qw = _w4_case(m, n, k, 1000 * config + m)
+        say("w4a16 forced", name, m, n, k)
+        c = out_bf16(m, n)
+        L.bsgemm_w4a16_run_config(config, dev(x.view(np.int16)), dev(qw[0]), dev(qw[1]),
+                                  dev(np.array([qw[2]], np.float32)), c=c)
+        assert_ok(G.check(u16(c), *G.w4a16(x, *qw)), f"w4a16 {name} {m}x{n}x{k}")
+
+
+def test_w4a16_environment_override(gpu_lib, monkeypatch):
+    x, qw = _w4_case(3, 200, 1024, 77)
+    args = (dev(x.view(np.int16)), dev(qw[0]), dev(qw[1]), dev(np.array([qw[2]], np.float32)))
+    say("w4a16 environment override")
+    forced = u16(L.bsgemm_w4a16_run_config("mfma_m64_n16", *args))
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "mfma_m64_n16")
+    via_env = u16(L.bsgemm_w4a16_run(*args))
+    monkeypatch.delenv("BSGEMM_W4A16_FORCE_CONFIG")
+    auto = u16(L.bsgemm_w4a16_run(*args))
+    assert np.array_equal(forced, via_env)
+    assert_ok(G.check(auto, *G.w4a16(x, *qw)), "w4a16 selector")
+
+
 # ------------------------------------------------- all codes, all scales --
 
 @pytest.mark.parametrize("k", [128, 256, 512, 1024, 2048 + 256])
