@@ -22,6 +22,9 @@ The same JSON line carries:
     16 copies (cold cache), the three quantizers at 16384^2, and the
     256 x 256 x 128 NVFP4 GEMM latency.
 
+``--only big`` times the 64k^3 and 128k^3 NVFP4 GEMMs (about 60 GB of device
+memory, operands drawn as NVFP4 on the device; 16k^3 on the same kind of
+operands as the control) and prints their rows.
 ``--only headline`` runs just the headline GEMM (for profiler runs).  It adds
 a 1 GiB device copy (read 1 GiB, write 1 GiB) that calibrates HBM byte
 counters.
@@ -89,7 +92,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "headline"], default="all")
+    ap.add_argument("--only", choices=["all", "headline", "big"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -107,6 +110,23 @@ def main():
     L.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only == "big":
+        # 64k^3 and 128k^3 NVFP4 GEMMs (operands drawn as NVFP4 on the device),
+        # and 16k^3 on the same kind of operands as the control
+        out = {}
+        for size in (16384, 65536, 131072):
+            qa = synth.nvfp4_random_operand(size, size, synth.SEEDS["nvfp4_big.A"], dev)
+            qb = synth.nvfp4_random_operand(size, size, synth.SEEDS["nvfp4_big.B"], dev)
+            cbig = torch.empty((size, size), dtype=torch.int16, device=dev)
+            ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_NVFP4, *qa, *qb, size, c=cbig), {16384: 10, 65536: 3}.get(size, 2), 1)
+            tf = 2.0 * size ** 3 / (ms * 1e-3) / 1e12
+            out[f"nvfp4_gemm_{size}"] = {"ms": round(ms, 2), "tflops": round(tf, 1), "frac_f16_peak": round(tf / PEAK["f16"], 4)}
+            log(f"nvfp4 {size}^3: {ms:.1f} ms, {tf:.1f} TFLOPS")
+            del qa, qb, cbig
+            torch.cuda.empty_cache()
+        print(json.dumps(out))
+        return
 
     # ------------------------------------------------ headline: NVFP4 16k^3
     M = N = K = 16384

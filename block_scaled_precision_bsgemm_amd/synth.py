@@ -12,6 +12,12 @@ distributions are the library's stated synthetic recipe):
   (the 256 x 256 x 128 case of "Triton #11171 ...", section "The missing case
   was defined by shape, layout, and execution mode together").
 * ``mxfp8_4k``      -- MXFP8 x MXFP8, M=N=K=4096, ~ N(0, 1).
+* ``nvfp4_big``     -- NVFP4 x NVFP4 at 65536^3 and 131072^3 ("Together AI Ports
+  ThunderKittens ...", section "Building the GEMM": 64k and 128k square
+  GEMMs).  FP32 sources would take 16-64 GiB per operand, so the operands are
+  drawn directly as NVFP4 on the device: uniform random code bytes and E4M3
+  scale codes uniform in [0x30, 0x40) (2^-1 .. 2^1), tensor scale 1
+  (``nvfp4_random_operand``, torch's seeded device generator).
 * ``mxfp4``         -- MXFP4 x MXFP4, M=N=K=4096 or 16384, ~ N(0, 1) with 1% of
   the rows of A and of B multiplied by 100 (the 16k-square recipe of
   ``nvfp4_16k``, own seeds).
@@ -41,6 +47,7 @@ SEEDS = {
     "grouped.counts": 4000, "grouped.A": 4001, "grouped.W": 4002,
     "w4a16.X": 5001, "w4a16.W": 5002,
     "mxfp4.A": 6001, "mxfp4.B": 6002, "mxfp4.A.rows": 6011, "mxfp4.B.rows": 6012,
+    "nvfp4_big.A": 7001, "nvfp4_big.B": 7002,
 }
 
 SHAPES = {
@@ -120,6 +127,18 @@ def mxfp4_inputs(M=16384, N=16384, K=16384):
     a, ia = with_outlier_rows(normal_f32((M, K), SEEDS["mxfp4.A"]), SEEDS["mxfp4.A.rows"])
     b, ib = with_outlier_rows(normal_f32((N, K), SEEDS["mxfp4.B"]), SEEDS["mxfp4.B.rows"])
     return a, b, ia, ib
+
+
+def nvfp4_random_operand(rows, k, seed, device):
+    """NVFP4 operand drawn on `device`: (codes uint8 [rows, k/2] uniform
+    bytes, scales uint8 [rows, k/16] uniform in [0x30, 0x40), tensor scale
+    float32 [1] = 1), from torch's generator seeded with `seed`."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    codes = torch.randint(0, 256, (rows, k // 2), dtype=torch.uint8, device=device, generator=g)
+    scales = torch.randint(0x30, 0x40, (rows, k // 16), dtype=torch.uint8, device=device, generator=g)
+    return codes, scales, torch.ones(1, dtype=torch.float32, device=device)
 
 
 def grouped_inputs(G=32, M=16384, N=2048, K=7168, alpha=0.5):

@@ -331,6 +331,30 @@ def test_nvfp4_16k_config_sampled(gpu_lib):
     assert not torch.isnan(c.view(torch.bfloat16)).any().item()
 
 
+@pytest.mark.parametrize("size", [65536, 131072])
+def test_nvfp4_big_square_sampled(gpu_lib, size):
+    """64k^3 and 128k^3 NVFP4 GEMMs on operands drawn as NVFP4 on the device;
+    256 sampled rows x 256 sampled columns (plus the first and last of each)
+    against the oracle, and no unwritten element anywhere."""
+    dev0 = torch.device("cuda:0")
+    qa = synth.nvfp4_random_operand(size, size, synth.SEEDS["nvfp4_big.A"], dev0)
+    qb = synth.nvfp4_random_operand(size, size, synth.SEEDS["nvfp4_big.B"], dev0)
+    say("gemm nvfp4", f"{size}^3")
+    c = out_bf16(size, size)
+    L.bsgemm_run(L.BSGEMM_NVFP4, *qa, *qb, size, c=c)
+    rows = _sample(size, 256, 31)
+    cols = _sample(size, 256, 32)
+    ri, ci = torch.from_numpy(rows).cuda(), torch.from_numpy(cols).cuda()
+    got = u16(c[ri][:, ci])
+    nan_free = not torch.isnan(c.view(torch.bfloat16)).any().item()
+    ha = (qa[0][ri].cpu().numpy(), qa[1][ri].cpu().numpy(), np.float32(1))
+    hb = (qb[0][ci].cpu().numpy(), qb[1][ci].cpu().numpy(), np.float32(1))
+    del qa, qb, c
+    torch.cuda.empty_cache()
+    assert nan_free
+    assert_ok(G.check(got, *G.gemm_nvfp4(*ha, *hb)), f"nvfp4 {size}^3 sampled")
+
+
 # -------------------------------------------------------------- grouped --
 
 def _grouped_case(counts, n, k, seed):
