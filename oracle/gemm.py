@@ -182,6 +182,37 @@ def grouped_nvfp4_ex(a_codes, a_scales, a_ts, offsets, w_bits, w_dtype="bf16", b
     return c, t
 
 
+def grouped_kragged(a_codes, a_scales, a_ts, k_offsets, w_bits, w_dtype="bf16"):
+    """Inner-expert (K-ragged) grouped NVFP4 x dense GEMM: the groups split the
+    contraction dimension K instead of the rows ("Triton #11171 ...",
+    sections "Why `pad_a` represents the K-ragged boundary" (the activation's
+    ragged dimension is 1, i.e. K, with ragged padding on A) and "K-ragged
+    variants").
+
+        C[g][m, n] = s_t * sum_{off[g] <= k < off[g+1]} x_hat_A[m, k] * W[n, k]
+
+    A is NVFP4 [M, K], W holds BF16 or FP16 bit patterns [N, K]; each group's
+    K slice is padded in both (the padding elements take part in the sum like
+    any other element, so zero padding contributes nothing).  Returns
+    (C [G, M, N], T [G, M, N]), T the sum of |products| times |s_t|."""
+    off = np.asarray(k_offsets, dtype=np.int64)
+    G = len(off) - 1
+    w = np.asarray(w_bits)
+    decode = {"bf16": decode_bf16, "f16": decode_f16}[w_dtype]
+    xa = dequant_nvfp4(a_codes, a_scales, 1.0)
+    xw = decode(w)
+    assert off[0] == 0 and off[-1] == xa.shape[1] == xw.shape[1] and np.all(np.diff(off) >= 0)
+    M, N = xa.shape[0], xw.shape[0]
+    c = np.zeros((G, M, N))
+    t = np.zeros((G, M, N))
+    for g in range(G):
+        sl = slice(int(off[g]), int(off[g + 1]))
+        if off[g + 1] > off[g]:
+            cg, tg = _matmul_and_mag(xa[:, sl], xw[:, sl])
+            c[g], t[g] = cg * float(a_ts), tg * abs(float(a_ts))
+    return c, t
+
+
 def w4a16(x_bf16, w_codes, w_scales, w_ts):
     """BF16 activations X[M, K] x NVFP4 weights W[N, K]: C = X_hat @ W_hat^T
     ("Add sm121 (GB10) tier to the 4-bit GEMM dispatch heuristic", section

@@ -285,6 +285,34 @@ def test_grouped_ex_reductions():
     assert np.array_equal(c6, c7[rows])
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+def test_grouped_kragged_bruteforce_and_invariants(w_dtype):
+    M, N, K = 3, 4, 96
+    off = np.array([0, 32, 32, 96])                  # an empty group in the middle
+    x = synth.normal_f32((M, K), 95)
+    x[:, 40:56] *= np.float32(0.01)
+    a = Q.quantize_nvfp4(x)
+    wf = synth.normal_f32((N, K), 96, std=0.5)
+    w = synth.bf16_bits(wf) if w_dtype == "bf16" else wf.astype(np.float16).view(np.uint16)
+    c, t = G.grouped_kragged(*a, off, w, w_dtype)
+    assert c.shape == (3, M, N)
+    ea = _exact_nvfp4(*a)
+    dec = (lambda v: Fraction(float(F.decode_bf16(v)))) if w_dtype == "bf16" else _f16_frac
+    for g in range(3):
+        for m in range(M):
+            for n in range(N):
+                ex = sum((ea[m][k] * dec(w[n, k]) for k in range(off[g], off[g + 1])), Fraction(0))
+                assert abs(Fraction(float(c[g, m, n])) - ex) <= Fraction(1e-12) * (1 + abs(ex))
+    assert np.all(c[1] == 0) and np.all(t[1] == 0)
+    # the groups partition K: their sum is the one-group product over all of K
+    c1, t1 = G.grouped_kragged(*a, np.array([0, K]), w, w_dtype)
+    assert np.allclose(c.sum(axis=0), c1[0], rtol=0, atol=1e-12 * t1.max())
+    assert np.allclose(t.sum(axis=0), t1[0], rtol=1e-12)
+    # planted mistake: slices taken from the wrong end of K
+    cw, _ = G.grouped_kragged(*a, off, w[:, ::-1].copy(), w_dtype)
+    assert not np.allclose(cw, c, rtol=1e-9, atol=1e-9)
+
+
 def test_w4a16_equals_exact_bruteforce():
     M, N, K = 3, 4, 64
     x = synth.bf16_bits(synth.normal_f32((M, K), 71))
