@@ -18,7 +18,7 @@ The same JSON line carries:
     the MXFP8 GEMM at 16384^3 and 4096^3, the MXFP4 GEMM at 16384^3 (on
     the MXFP8 row's N(0, 1) inputs), the ragged grouped NVFP4 x BF16
     GEMM (and the same problem with FP16 weights and every routing and
-    epilogue variant), the W4A16 GEMM at M = 1, 16, 64, 256 with weights rotated through
+    epilogue variant, and its K-ragged weight-gradient form), the W4A16 GEMM at M = 1, 16, 64, 256 with weights rotated through
     16 copies (cold cache), the three quantizers at 16384^2, and the
     256 x 256 x 128 NVFP4 GEMM latency.
 
@@ -271,6 +271,26 @@ def main():
                                               "frac_f16_peak": round(tf / PEAK["f16"], 4),
                                               "variants": "gather + scatter + bias + gamma, FP16 W"}
     del qg, dw, doff, cg, dw16, vg, vs, vb, vgm
+
+    # inner-expert (K-ragged) grouped GEMM: the weight-gradient shape of the
+    # same problem (experts' token counts split K, each padded to 256),
+    # operands drawn on the device
+    kcounts = np.diff(off.astype(np.int64))
+    koff = np.concatenate([[0], np.cumsum([-(-int(c) // 256) * 256 for c in kcounts])]).astype(np.int32)
+    kk = int(koff[-1])
+    qk = synth.nvfp4_random_operand(7168, kk, synth.SEEDS["nvfp4_big.A"], dev)
+    gk = torch.Generator(device=dev)
+    gk.manual_seed(4400)
+    wk = (torch.randn((2048, kk), generator=gk, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+    ck = torch.empty((32, 7168, 2048), dtype=torch.int16, device=dev)
+    dkoff = torch.from_numpy(koff).to(dev)
+    ms = time_events(lambda i: L.bsgemm_grouped_kragged_run(*qk, dkoff, wk, kk, c=ck), 10, 3)
+    kflops = 2.0 * 7168 * 2048 * kk
+    tf = kflops / (ms * 1e-3) / 1e12
+    rows["grouped_kragged_nvfp4_bf16"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
+                                          "shape": f"32 groups, A 7168 x {kk} NVFP4, W 2048 x {kk} BF16, C 32 x 7168 x 2048",
+                                          "flops_counted": "2 * 7168 * 2048 * padded K"}
+    del qk, wk, ck, dkoff
 
     # --------------------------------------------------------------- W4A16
     Nw, Kw = 14336, 4096

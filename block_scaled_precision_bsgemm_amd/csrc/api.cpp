@@ -136,7 +136,7 @@ int check_limits(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k) {
 
 extern "C" {
 
-int bsgemm_version(void) { return 400; }   // 0.4.0: W4A16 configurations
+int bsgemm_version(void) { return 500; }   // 0.5.0: K-ragged grouped GEMM
 
 const char* bsgemm_status_string(int status) {
   switch (status) {
@@ -343,6 +343,44 @@ int bsgemm_grouped_run_ex(int num_groups, int64_t m_total, int64_t n, int64_t k,
     bsg::GroupedCall call{num_groups, m_total, a_rows, n, k, a, a_scales, a_tscale, group_offsets,
                           w, w_dtype == BSGEMM_W_F16, bias, gamma, gather_idx, scatter_idx, c_bf16};
     return finish_launch(fn, bsg::launch_grouped(call, st), st);
+  } catch (...) {
+    return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
+  }
+}
+
+int bsgemm_grouped_kragged_run(int num_groups, int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                               const uint8_t* a_scales, const float* a_tscale, const int32_t* k_offsets,
+                               int w_dtype, const uint16_t* w, uint16_t* c_bf16, void* stream) {
+  static const char* fn = "bsgemm_grouped_kragged_run";
+  try {
+    if (num_groups < 1) return fail(BSGEMM_ERR_INVALID_ARG, "%s: num_groups must be >= 1", fn);
+    if (m < 0 || n < 0 || k < 0) return fail(BSGEMM_ERR_INVALID_ARG, "%s: negative size", fn);
+    REQUIRE_PTR(a, m * k);
+    REQUIRE_PTR(a_scales, m * k);
+    REQUIRE_PTR(w, n * k);
+    REQUIRE_PTR(c_bf16, m * n);
+    if (a_tscale == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: a_tscale is NULL", fn);
+    if (k_offsets == nullptr) return fail(BSGEMM_ERR_INVALID_ARG, "%s: k_offsets is NULL", fn);
+    if (w_dtype != BSGEMM_W_BF16 && w_dtype != BSGEMM_W_F16)
+      return fail(BSGEMM_ERR_UNSUPPORTED, "%s: unknown w_dtype %d", fn, w_dtype);
+    if (k % 256 != 0)
+      return fail(BSGEMM_ERR_UNSUPPORTED, "%s: k = %lld is not a multiple of 256 (the K-slice padding)", fn,
+                  (long long)k);
+    REQUIRE_ALIGNED(a);
+    REQUIRE_ALIGNED(a_scales);
+    REQUIRE_ALIGNED(w);
+    REQUIRE_ALIGNED(c_bf16);
+    if ((reinterpret_cast<uintptr_t>(k_offsets) & 3u) != 0)
+      return fail(BSGEMM_ERR_BAD_ALIGNMENT, "%s: k_offsets is not 4-byte aligned", fn);
+    if (int s = check_limits(fn, m, n, k)) return s;
+    if ((int64_t)num_groups * ((m + 255) / 256) * ((n + 255) / 256) > MAX_ROWS)
+      return fail(BSGEMM_ERR_RESOURCE, "%s: too many tiles", fn);
+    int num_cus = 0;
+    if (int s = check_device(fn, &num_cus)) return s;
+    if (m == 0 || n == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bsg::KRaggedCall call{num_groups, m, n, k, a, a_scales, a_tscale, k_offsets, w, w_dtype == BSGEMM_W_F16, c_bf16};
+    return finish_launch(fn, bsg::launch_grouped_kragged(call, st), st);
   } catch (...) {
     return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);
   }

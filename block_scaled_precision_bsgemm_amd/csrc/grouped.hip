@@ -80,7 +80,8 @@ struct GArgs {
   const float* gamma;     // [M]
   const int32_t* gather;  // [M], rows of A
   const int32_t* scatter; // [M], rows of C
-  int G, M, a_rows, N, K, tiles_n;
+  const int32_t* koff;    // K-ragged mode: [G + 1] K offsets (multiples of 256); C is [G][M][N]
+  int G, M, a_rows, N, K, tiles_n, tiles_m;
 };
 
 // Operand type, exact dequantisation and MFMA of the two weight types.
@@ -337,38 +338,62 @@ struct GRingSmem {
   GEpi epi;
 };
 
-template <int SB, bool F16>
+// KRAG: the inner-expert (K-ragged) mode.  The groups split K instead of the
+// rows: workgroup (g, m tile, n tile) runs the K slice [koff[g], koff[g+1])
+// of the shared A and W and writes C[g].  Slices are multiples of 256, so
+// the 16-byte-scale ring serves every group; an empty slice writes zeros.
+template <int SB, bool F16, bool KRAG = false>
 __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   using GM = GMath<F16>;
   using VT = typename GM::vec;
   constexpr int U = SB / 4;                  // steps per scale load
   __shared__ GRingSmem<SB> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int M = p.M, N = p.N, K = p.K;
+  const int KH = K / 2, KB = K / 16;
   // n-tile-major order: consecutive tiles (kept on one XCD by xcd_remap) are
   // the m-tiles of one W column panel, so each group's W panel is fetched
   // from HBM about once and re-read from L2; A (small) is shared through the
   // infinity cache across panels.
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int mtiles = gridDim.x / p.tiles_n;
-  const int nt = t / mtiles, mt = t - nt * mtiles;
-  if (wave == 0) find_tile(p.off, p.G, mt, lane, sm.tile_info);
-  __syncthreads();
-  const int grp = sm.tile_info[0];
-  if (grp < 0) return;                      // uniform over the workgroup
-  const int M = p.M, N = p.N, K = p.K;
-  // Offsets are a documented precondition; clamping keeps even malformed
-  // ones inside the A and C buffers.
-  const int r0 = min(max(sm.tile_info[1], 0), M), r1 = min(max(sm.tile_info[2], r0), M);
+  int grp, r0, r1, nt, k0 = 0, k1 = K;
+  if constexpr (KRAG) {
+    const int per_g = p.tiles_m * p.tiles_n;
+    grp = t / per_g;
+    const int rem = t - grp * per_g;
+    nt = rem / p.tiles_m;
+    r0 = (rem - nt * p.tiles_m) * BM;
+    r1 = min(r0 + BM, M);
+    // offsets are a documented precondition; clamped and rounded down to
+    // multiples of 256, a malformed one still stays inside A and W
+    k0 = min(max(p.koff[grp], 0), K) & ~255;
+    k1 = min(max(p.koff[grp + 1], k0), K) & ~255;
+  } else {
+    const int mtiles = gridDim.x / p.tiles_n;
+    nt = t / mtiles;
+    const int mt = t - nt * mtiles;
+    if (wave == 0) find_tile(p.off, p.G, mt, lane, sm.tile_info);
+    __syncthreads();
+    grp = sm.tile_info[0];
+    if (grp < 0) return;                      // uniform over the workgroup
+    // Offsets are a documented precondition; clamping keeps even malformed
+    // ones inside the A and C buffers.
+    r0 = min(max(sm.tile_info[1], 0), M);
+    r1 = min(max(sm.tile_info[2], r0), M);
+  }
   const int n0 = nt * BN;
-  const int KT = K / BK;                    // a positive multiple of U
-  const int KH = K / 2, KB = K / 16;
+  const int KT = (k1 - k0) / BK;            // a multiple of U
   const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
   const bool gat = p.gather != nullptr;
   // With gather the A resources span all of A and rows are addressed by
-  // their source index; otherwise they span the tile's rows.
-  const rsrc4_t ra = make_rsrc4(gat ? p.A : p.A + (int64_t)r0 * KH, (gat ? p.a_rows : rows_a) * KH);
-  const rsrc4_t rsa = make_rsrc4(gat ? p.As : p.As + (int64_t)r0 * KB, (gat ? p.a_rows : rows_a) * KB);
-  const rsrc4_t rw = make_rsrc4(p.W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  // their source index; otherwise they span the tile's rows.  The K slice
+  // start is folded into the bases (k0 = 0 outside the K-ragged mode).
+  const rsrc4_t ra = make_rsrc4(gat ? p.A : p.A + (int64_t)r0 * KH + k0 / 2, (gat ? p.a_rows : rows_a) * KH - k0 / 2);
+  const rsrc4_t rsa = make_rsrc4(gat ? p.As : p.As + (int64_t)r0 * KB + k0 / 16,
+                                 (gat ? p.a_rows : rows_a) * KB - k0 / 16);
+  const rsrc4_t rw = make_rsrc4(p.W + (KRAG ? (int64_t)n0 * K : ((int64_t)grp * N + n0) * K) + k0,
+                                rows_w * K * 2 - k0 * 2);
+  uint16_t* const Cb = KRAG ? p.C + (int64_t)grp * M * N : p.C;
   fill_epi(p, r0, rows_a, tid, sm.epi);   // visible after the prologue's barrier
 
   // Load geometry.  A instruction u covers rows 32 (2 wave + u) .. +31 (two
@@ -557,7 +582,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   const float alpha = *p.Ats;
   const bool plain = !p.bias && !p.gamma && !p.scatter;
   if (plain && r0 + BM <= r1 && n0 + BN <= N) {
-    uint16_t* cw = p.C + (int64_t)(r0 + wave * 64 + g * 4) * N + n0 + r;
+    uint16_t* cw = Cb + (int64_t)(r0 + wave * 64 + g * 4) * N + n0 + r;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -580,7 +605,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
           float y = acc[i][j][v] * alpha;
           if (p.bias) y += b;
           if (p.gamma) y *= sm.epi.gamma[lr];
-          if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
+          if (dst >= 0 && col < N) Cb[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
         }
     }
   }
@@ -588,8 +613,22 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
 
 }  // namespace
 
+hipError_t launch_grouped_kragged(const KRaggedCall& c, hipStream_t stream) {
+  GArgs p{};
+  p.A = c.a; p.As = c.as; p.Ats = c.ats; p.W = c.w; p.C = c.c; p.koff = c.k_offsets;
+  p.G = c.num_groups; p.M = (int)c.m; p.a_rows = (int)c.m; p.N = (int)c.n; p.K = (int)c.k;
+  p.tiles_n = (int)ceil_div(c.n, BN);
+  p.tiles_m = (int)ceil_div(c.m, BM);
+  const dim3 grid((unsigned)((int64_t)c.num_groups * p.tiles_m * p.tiles_n));
+  if (c.w_f16)
+    hipLaunchKernelGGL((grouped_ring_kernel<16, true, true>), grid, dim3(NT), 0, stream, p);
+  else
+    hipLaunchKernelGGL((grouped_ring_kernel<16, false, true>), grid, dim3(NT), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_grouped(const GroupedCall& c, hipStream_t stream) {
-  GArgs p;
+  GArgs p{};
   p.A = c.a; p.As = c.as; p.Ats = c.ats; p.off = c.offsets; p.W = c.w; p.C = c.c;
   p.bias = c.bias; p.gamma = c.gamma; p.gather = c.gather; p.scatter = c.scatter;
   p.G = c.num_groups; p.M = (int)c.m_total; p.a_rows = (int)c.a_rows; p.N = (int)c.n; p.K = (int)c.k;

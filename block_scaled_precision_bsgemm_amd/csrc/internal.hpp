@@ -44,6 +44,21 @@ struct GroupedCall {
   uint16_t* c;
 };
 hipError_t launch_grouped(const GroupedCall& call, hipStream_t stream);
+
+// One K-ragged (inner-expert) grouped launch: k % 256 == 0; k_offsets on the
+// device; c is [num_groups][m][n].
+struct KRaggedCall {
+  int num_groups;
+  int64_t m, n, k;
+  const uint8_t* a;
+  const uint8_t* as;
+  const float* ats;
+  const int32_t* k_offsets;
+  const uint16_t* w;
+  bool w_f16;
+  uint16_t* c;
+};
+hipError_t launch_grouped_kragged(const KRaggedCall& call, hipStream_t stream);
 // W4A16 configurations: count, names, largest m each accepts, the selector,
 // and a launch of one configuration (config must be a valid id).
 int w4a16_num_configs();

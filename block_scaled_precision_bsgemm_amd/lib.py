@@ -38,6 +38,7 @@ SIGNATURES = {
     "bsgemm_grouped_run": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p, _p]),
     "bsgemm_grouped_run_ex": (_int, [_int, _i64, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _p, _p, _p,
                                      _p, _p]),
+    "bsgemm_grouped_kragged_run": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _int, _p, _p, _p]),
     "bsgemm_w4a16_run": (_int, [_i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "bsgemm_w4a16_run_config": (_int, [_int, _i64, _i64, _i64, _p, _p, _p, _p, _p, _p]),
     "bsgemm_w4a16_num_configs": (_int, []),
@@ -155,6 +156,18 @@ def bsgemm_grouped_run_ex(a, a_scales, a_tscale, group_offsets, w, k, w_dtype=BS
     _check(load().bsgemm_grouped_run_ex(G, m_total, n, k, a_rows, _ptr(a), _ptr(a_scales), _ptr(a_tscale),
                                         _ptr(group_offsets), w_dtype, _ptr(w), _ptr(bias), _ptr(gamma),
                                         _ptr(gather_idx), _ptr(scatter_idx), _ptr(c), _stream(stream)))
+    return c
+
+
+def bsgemm_grouped_kragged_run(a, a_scales, a_tscale, k_offsets, w, k, w_dtype=BSGEMM_W_BF16, c=None,
+                               stream=None):
+    """K-ragged grouped NVFP4 A [m, k] x dense W [n, k] (BF16 or FP16 bits), groups split K at
+    k_offsets [G + 1] -> C [G, m, n] (BF16 bits)."""
+    G = k_offsets.shape[0] - 1
+    m, n = a.shape[0], w.shape[0]
+    c = _empty((G, m, n), torch.int16, a) if c is None else c
+    _check(load().bsgemm_grouped_kragged_run(G, m, n, k, _ptr(a), _ptr(a_scales), _ptr(a_tscale),
+                                             _ptr(k_offsets), w_dtype, _ptr(w), _ptr(c), _stream(stream)))
     return c
 
 

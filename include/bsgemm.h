@@ -275,6 +275,38 @@ int bsgemm_grouped_run_ex(int num_groups, int64_t m_total, int64_t n, int64_t k,
                           const int32_t* scatter_idx, uint16_t* c_bf16, void* stream);
 
 /*
+ * Inner-expert (K-ragged) grouped GEMM: the groups split the contraction
+ * dimension K instead of the rows.  For each group g:
+ *   C[g][m][n] = bf16_RNE( s_t * sum_{k_offsets[g] <= k < k_offsets[g+1]}
+ *                                  (e2m1 * e4m3)(A)[m][k] * W[n][k] )
+ * with FP32 accumulation.  Each group's K slice is padded in A and W to a
+ * multiple of 256 elements (16 E4M3 scale bytes per row); the padding takes
+ * part in the sum like any other element, so zero padding (what quantizing
+ * zero-padded data gives) contributes nothing.  An empty slice gives C[g] = 0.
+ * Source: "Triton #11171 -- Why Two New NVFP4 Test Cases Produced Twelve
+ * Tensor-Memory Failures", sections "Why `pad_a` represents the K-ragged
+ * boundary" (the activation is ragged along dimension 1, K, with ragged
+ * padding on A) and "The skip logic is part of the regression contract"
+ * (a microscaled activation in inner-expert mode requires that padding).
+ *
+ * Arguments:
+ *   num_groups   G >= 1
+ *   a, a_scales, a_tscale  NVFP4 activations [m][k], one tensor scale
+ *   k_offsets    device int32[G+1]: k_offsets[0] = 0, k_offsets[G] = k,
+ *                non-decreasing multiples of 256.  Read on the device; an
+ *                offset that breaks this is clamped to [0, k] and rounded
+ *                down to a multiple of 256 (documented, not an error).
+ *   w_dtype      BSGEMM_W_BF16 or BSGEMM_W_F16
+ *   w            device uint16[n][k] (the dense operand, same K layout)
+ *   c_bf16       device uint16[G][m][n] (written)
+ * Sizes: m, n, k >= 0; k % 256 == 0 (else BSGEMM_ERR_UNSUPPORTED).
+ *   m == 0 or n == 0: BSGEMM_OK and nothing is launched.
+ */
+int bsgemm_grouped_kragged_run(int num_groups, int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                               const uint8_t* a_scales, const float* a_tscale, const int32_t* k_offsets,
+                               int w_dtype, const uint16_t* w, uint16_t* c_bf16, void* stream);
+
+/*
  * Small-M weight-only 4-bit GEMM: BF16 activations x NVFP4 weights.
  *   C[m][n] = bf16_RNE( s_tW * sum_k X[m][k] * (e2m1 * e4m3)(W)[n][k] )
  * Each weight byte is read from HBM once.  The kernel family is chosen by m:

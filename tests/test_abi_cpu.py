@@ -42,7 +42,7 @@ def test_status_strings_and_version(so):
                        (5, b"BSGEMM_ERR_RESOURCE"), (6, b"BSGEMM_ERR_LAUNCH")]:
         assert so.bsgemm_status_string(code) == name
     assert so.bsgemm_status_string(99) == b"unknown status"
-    assert so.bsgemm_version() == 400
+    assert so.bsgemm_version() == 500
 
 
 def run(so, fmt=L.BSGEMM_NVFP4, m=64, n=64, k=64, a=P, sa=P, ta=P, b=P, sb=P, tb=P, c=P):
@@ -184,6 +184,20 @@ def test_w4a16_forced_config_validation(so, monkeypatch):
     if not torch.cuda.is_available():
         monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "mfma_m32_n16")
         assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_DEVICE
+
+
+def test_grouped_kragged_validation(so):
+    def kr(G=2, m=64, n=64, k=512, a=P, sa=P, ta=P, off=P, wd=L.BSGEMM_W_BF16, w=P, c=P):
+        return so.bsgemm_grouped_kragged_run(G, m, n, k, a, sa, ta, off, wd, w, c, None)
+    assert kr(G=0) == L.BSGEMM_ERR_INVALID_ARG
+    assert kr(off=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert kr(ta=None) == L.BSGEMM_ERR_INVALID_ARG
+    assert kr(k=384) == L.BSGEMM_ERR_UNSUPPORTED                 # not a multiple of 256
+    assert b"multiple of 256" in so.bsgemm_last_error()
+    assert kr(wd=0) == L.BSGEMM_ERR_UNSUPPORTED
+    assert kr(c=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert kr(off=0x10002) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert kr(m=0, a=None, sa=None, c=None) in (L.BSGEMM_OK, L.BSGEMM_ERR_DEVICE)
 
 
 def test_last_error_is_per_thread(so):

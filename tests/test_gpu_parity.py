@@ -534,6 +534,74 @@ def test_grouped_ex_config_sampled(gpu_lib):
     assert not np.any(got == SENTINEL)
 
 
+# ------------------------------------------------ grouped: K-ragged mode --
+
+def _kragged_case(counts, m, n, seed, w_dtype):
+    """Groups split K: group g has counts[g] real K elements, padded with
+    zeros to a multiple of 256 in A (before quantization) and in W."""
+    pad = [-(-c // 256) * 256 for c in counts]
+    off = np.concatenate([[0], np.cumsum(pad)]).astype(np.int32)
+    k = int(off[-1])
+    x = np.zeros((m, k), np.float32)
+    wf = np.zeros((n, k), np.float32)
+    r = np.random.Generator(np.random.PCG64(seed))
+    for g, c in enumerate(counts):
+        x[:, off[g]:off[g] + c] = r.standard_normal((m, c), dtype=np.float32)
+        wf[:, off[g]:off[g] + c] = r.standard_normal((n, c), dtype=np.float32) * np.float32(0.02)
+    qa = Q.quantize_nvfp4(x)
+    w = synth.bf16_bits(wf) if w_dtype == "bf16" else wf.astype(np.float16).view(np.uint16)
+    return qa, off, w, k
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("counts,m,n", [
+    ([256], 256, 256),
+    ([100, 0, 700, 256], 300, 260),        # an empty group, ragged m and n tails
+    ([1, 255, 257, 1024], 64, 520),
+])
+def test_grouped_kragged_shapes(gpu_lib, w_dtype, counts, m, n):
+    qa, off, w, k = _kragged_case(counts, m, n, sum(counts) + m, w_dtype)
+    say("grouped K-ragged", w_dtype, counts, m, n, k)
+    c = torch.full((len(counts), m, n), SENTINEL, dtype=torch.int16, device="cuda")
+    L.bsgemm_grouped_kragged_run(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)), dev(off), dev(w), k,
+                                 w_dtype=L.BSGEMM_W_F16 if w_dtype == "f16" else L.BSGEMM_W_BF16, c=c)
+    got = u16(c)
+    cref, t = G.grouped_kragged(*qa, off, w, w_dtype)
+    for g in range(len(counts)):
+        assert_ok(G.check(got[g], cref[g], t[g]), f"K-ragged group {g} of {counts} {w_dtype}")
+
+
+def test_grouped_kragged_config_sampled(gpu_lib):
+    """Weight-gradient shape of the grouped config: 32 experts' token counts
+    (the Dirichlet draw over 16384 tokens) split K, each padded to 256;
+    A = 7168 x K NVFP4, W = 2048 x K BF16, C = 32 x 7168 x 2048; sampled
+    (group, row) pairs, all columns."""
+    counts = synth.group_counts(32, 16384, 0.5, synth.SEEDS["grouped.counts"])
+    m, n = 7168, 2048
+    pad = [-(-int(c) // 256) * 256 for c in counts]
+    off = np.concatenate([[0], np.cumsum(pad)]).astype(np.int32)
+    k = int(off[-1])
+    x = synth.normal_f32((m, k), 4301)
+    wf = synth.normal_f32((n, k), 4302, std=0.02)
+    for g, c in enumerate(counts):   # zero padding in both operands
+        x[:, off[g] + int(c):off[g + 1]] = 0
+        wf[:, off[g] + int(c):off[g + 1]] = 0
+    w = synth.bf16_bits(wf)
+    del wf
+    rows = _sample(m, 24, 41)
+    ca, sa, ta = _check_nvfp4_quant(x, "K-ragged A (sampled rows)", rows)
+    del x
+    say("grouped K-ragged 32 x (7168 x 2048), k =", k)
+    c = out_bf16(32 * m, n).view(32, m, n)
+    L.bsgemm_grouped_kragged_run(ca, sa, ta, dev(off), dev(w), k, c=c)
+    assert not torch.isnan(c.view(torch.bfloat16)).any().item()
+    got = u16(c[:, torch.from_numpy(rows).cuda()])
+    qa = (ca.cpu().numpy()[rows], sa.cpu().numpy()[rows], np.float32(ta.item()))
+    cref, t = G.grouped_kragged(*qa, off, w, "bf16")
+    for g in range(32):
+        assert_ok(G.check(got[g], cref[g], t[g]), f"K-ragged config group {g}")
+
+
 # ---------------------------------------------------------------- W4A16 --
 
 def _gpu_w4a16(x, qw, m):
