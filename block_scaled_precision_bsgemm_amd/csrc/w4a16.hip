@@ -389,8 +389,9 @@ namespace {
 
 struct W4Config {
   const char* name;
-  int mt;   // 0: vector-ALU gemv (one X row per grid row); else the MFMA kernel's m tile
-  int nb;   // W rows per workgroup; 0 = the fit width (w4a16_fit_nb)
+  int mt;     // 0: vector-ALU gemv (one X row per grid row); else the MFMA kernel's m tile
+  int nb;     // W rows per workgroup; 0 = the fit width (w4a16_fit_nb)
+  int ring;   // W register ring depth in stages; 0 = the m tile's default (16, 32: 1; 64: 4)
 };
 
 constexpr W4Config kW4Configs[] = {
@@ -398,6 +399,9 @@ constexpr W4Config kW4Configs[] = {
     {"mfma_m16_nfit", 16, 0}, {"mfma_m16_n16", 16, 16}, {"mfma_m16_n32", 16, 32}, {"mfma_m16_n64", 16, 64},
     {"mfma_m32_nfit", 32, 0}, {"mfma_m32_n16", 32, 16}, {"mfma_m32_n32", 32, 32}, {"mfma_m32_n64", 32, 64},
     {"mfma_m64_nfit", 64, 0}, {"mfma_m64_n16", 64, 16}, {"mfma_m64_n32", 64, 32}, {"mfma_m64_n64", 64, 64},
+    {"mfma_m16_nfit_r2", 16, 0, 2}, {"mfma_m16_nfit_r4", 16, 0, 4},
+    {"mfma_m32_nfit_r2", 32, 0, 2}, {"mfma_m32_nfit_r4", 32, 0, 4},
+    {"mfma_m64_nfit_r2", 64, 0, 2},
 };
 constexpr int kW4NumConfigs = sizeof(kW4Configs) / sizeof(kW4Configs[0]);
 
@@ -436,11 +440,16 @@ int w4a16_config_id(int mt, int nb) {
   return base + (nb == 0 ? 0 : nb == 16 ? 1 : nb == 32 ? 2 : 3);
 }
 
+//   - W register ring depth: the 64-row m tile keeps 4 stages (rechecked
+//     +3.7% over 2 at k = 4096 and 14336); the 16- and 32-row tiles keep 4
+//     for k >= 8192 (+3.5-8% at k = 14336) and 1 below (4 lost at k = 4096).
 int w4a16_select(int64_t m, int64_t n, int64_t k) {
-  (void)k;
   if (m <= 2 || (m <= 8 && m * n <= 24576)) return 0;   // valu_gemv
   for (int mt : {16, 32, 64})
-    if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) return w4a16_config_id(mt, 0);
+    if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) {
+      if (k >= 8192 && mt < 64) return mt == 16 ? 14 : 16;   // mfma_m{16,32}_nfit_r4
+      return w4a16_config_id(mt, 0);
+    }
   int best = 64;
   double best_cost = 0;
   for (int mt : {64, 32, 16}) {
@@ -461,11 +470,16 @@ hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint1
     hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)ceil_div(n, GV_ROWS * GV_WAVES), (unsigned)m), dim3(64 * GV_WAVES),
                        0, stream, x, w, ws, wts, c, (int)n, (int)k);
   } else if (cf.mt == 16) {
-    launch_skinny<16, 2, 8, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 4) launch_skinny<16, 2, 8, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    else if (cf.ring == 2) launch_skinny<16, 2, 8, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    else launch_skinny<16, 2, 8, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else if (cf.mt == 32) {
-    launch_skinny<32, 2, 4, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 4) launch_skinny<32, 2, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    else if (cf.ring == 2) launch_skinny<32, 2, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    else launch_skinny<32, 2, 4, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else {
-    launch_skinny<64, 4, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 2) launch_skinny<64, 4, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    else launch_skinny<64, 4, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   }
   return hipGetLastError();
 }

@@ -134,7 +134,7 @@ def test_grouped_ex_validation(so):
 def test_w4a16_configs_and_exhaustive_selector(so):
     n_cfg = so.bsgemm_w4a16_num_configs()
     names = [so.bsgemm_w4a16_config_name(i).decode() for i in range(n_cfg)]
-    assert n_cfg == 13 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
+    assert n_cfg == 18 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
     assert so.bsgemm_w4a16_config_name(n_cfg) is None and so.bsgemm_w4a16_config_name(-1) is None
     tile = {nm: (0 if nm == "valu_gemv" else int(nm.split("_")[1][1:])) for nm in names}
 
@@ -147,7 +147,8 @@ def test_w4a16_configs_and_exhaustive_selector(so):
     # properties: the vector ALU exactly for m <= 2, or m <= 8 with
     # m * n <= 24576; an MFMA pick with the fit width has an m tile whose
     # grid fits one wave of 256 workgroups with 64-row slabs, and no smaller
-    # tile does; otherwise no tile fits and the pick uses 64-row slabs.
+    # tile does (16/32-row tiles: 4-stage W ring from k = 8192); otherwise no tile fits and the
+    # pick uses 64-row slabs.
     decisions = 0
     for n in (1, 64, 896, 1536, 3072, 4096, 5120, 8192, 10240, 14336, 65536):
         for k in (32, 4096, 14336):
@@ -161,7 +162,7 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                     continue
                 fits = [t for t in (16, 32, 64) if grid(m, n, t, 64) <= 256]
                 if fits:
-                    assert nm == f"mfma_m{fits[0]}_nfit", (m, n, nm)
+                    assert nm == f"mfma_m{fits[0]}_nfit" + ("_r4" if k >= 8192 and fits[0] < 64 else ""), (m, n, k, nm)
                 else:
                     assert nm.endswith("_n64"), (m, n, nm)
     assert decisions == 11 * 3 * 135
@@ -178,7 +179,7 @@ def test_w4a16_forced_config_validation(so, monkeypatch):
     monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "no_such_tile")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert b"FORCE_CONFIG" in so.bsgemm_last_error()
-    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "13")
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "18")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     import torch
     if not torch.cuda.is_available():
