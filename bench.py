@@ -18,10 +18,13 @@ The same JSON line carries:
     the MXFP8 GEMM at 16384^3 and 4096^3, the MXFP4 GEMM at 16384^3 (on
     the MXFP8 row's N(0, 1) inputs), the ragged grouped NVFP4 x BF16
     GEMM (and the same problem with FP16 weights and every routing and
-    epilogue variant, and its K-ragged weight-gradient form), the W4A16 GEMM at M = 1, 16, 64, 256 with weights rotated through
-    16 copies (cold cache), the three quantizers at 16384^2, and the
-    256 x 256 x 128 NVFP4 GEMM latency.
+    epilogue variant, and its K-ragged weight-gradient form), the W4A16
+    GEMM at M = 1, 16, 64, 256 with weights rotated through 16 copies (cold
+    cache; back-to-back launches, and the same launches replayed from a HIP
+    graph), the three quantizers at 16384^2, and the 256 x 256 x 128 NVFP4
+    GEMM latency.
 
+``--only w4a16`` runs just the W4A16 rows (for profiler runs).
 ``--only big`` times the 64k^3 and 128k^3 NVFP4 GEMMs (about 60 GB of device
 memory, operands drawn as NVFP4 on the device; 16k^3 on the same kind of
 operands as the control) and prints their rows.
@@ -92,7 +95,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "headline", "big"], default="all")
+    ap.add_argument("--only", choices=["all", "headline", "big", "w4a16"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -110,6 +113,10 @@ def main():
     L.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only == "w4a16":
+        print(json.dumps(w4a16_rows(L, synth, dev)))
+        return
 
     if args.only == "big":
         # 64k^3 and 128k^3 NVFP4 GEMMs (operands drawn as NVFP4 on the device),
@@ -293,23 +300,7 @@ def main():
     del qk, wk, ck, dkoff
 
     # --------------------------------------------------------------- W4A16
-    Nw, Kw = 14336, 4096
-    _, wf = synth.w4a16_inputs(1)
-    qw = L.bsgemm_quantize_nvfp4(torch.from_numpy(wf).to(dev))
-    copies = 16   # 16 x 33 MB > 256 MB Infinity Cache: every launch reads cold weights
-    wc = [qw[0].clone() for _ in range(copies)]
-    ws = [qw[1].clone() for _ in range(copies)]
-    for m in (1, 16, 64, 256):
-        x = synth.bf16_bits(synth.normal_f32((m, Kw), synth.SEEDS["w4a16.X"]))
-        dx = torch.from_numpy(x.view(np.int16)).to(dev)
-        cw = torch.empty((m, Nw), dtype=torch.int16, device=dev)
-        ms = time_events(lambda i: L.bsgemm_w4a16_run(dx, wc[i % copies], ws[i % copies], qw[2], c=cw), 64, 16)
-        nbytes = Nw * Kw // 2 + Nw * Kw // 16 + 4 + 2 * m * Kw + 2 * m * Nw
-        gbps = nbytes / (ms * 1e-3) / 1e9
-        tf = 2.0 * m * Nw * Kw / (ms * 1e-3) / 1e12
-        rows[f"w4a16_m{m}"] = {"us": round(ms * 1e3, 2), "gbps": round(gbps, 1), "frac_hbm": round(gbps / PEAK["hbm_gbps"], 4),
-                               "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4)}
-    del wc, ws, qw
+    rows.update(w4a16_rows(L, synth, dev))
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOPS", "n_gpus": 1,
@@ -322,6 +313,69 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "rows": rows,
     }
     print(json.dumps(out))
+
+
+def time_graph(fn, launches, replays):
+    """Average ms per call with `launches` calls captured in one HIP graph and
+    the graph replayed `replays` times (launch overhead amortised)."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(launches):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(replays):
+        g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (replays * launches), g
+
+
+def w4a16_rows(L, synth, dev):
+    """W4A16 at M = 1, 16, 64, 256 on the 14336 x 4096 NVFP4 weight, rotated
+    through 16 copies (cold weights): back-to-back launches timed with events,
+    and the same launches captured in a HIP graph (the graph's last output is
+    checked bit for bit against an eager launch first)."""
+    import numpy as np
+    import torch
+    rows = {}
+    Nw, Kw = 14336, 4096
+    _, wf = synth.w4a16_inputs(1)
+    qw = L.bsgemm_quantize_nvfp4(torch.from_numpy(wf).to(dev))
+    copies = 16   # 16 x 33 MB > 256 MB Infinity Cache: every launch reads cold weights
+    wc = [qw[0].clone() for _ in range(copies)]
+    ws = [qw[1].clone() for _ in range(copies)]
+    for m in (1, 16, 64, 256):
+        x = synth.bf16_bits(synth.normal_f32((m, Kw), synth.SEEDS["w4a16.X"]))
+        dx = torch.from_numpy(x.view(np.int16)).to(dev)
+        cw = torch.empty((m, Nw), dtype=torch.int16, device=dev)
+        call = lambda i: L.bsgemm_w4a16_run(dx, wc[i % copies], ws[i % copies], qw[2], c=cw)  # noqa: E731
+        ms = time_events(call, 64, 16)
+        eager = L.bsgemm_w4a16_run(dx, wc[0], ws[0], qw[2]).clone()
+        ms_graph, graph = time_graph(call, 64, 8)
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_ok = bool(torch.equal(cw, eager))
+        del graph
+        nbytes = Nw * Kw // 2 + Nw * Kw // 16 + 4 + 2 * m * Kw + 2 * m * Nw
+        row = {"config": L.w4a16_configs()[L.bsgemm_w4a16_select(m, Nw, Kw)]}
+        for tag, t in (("", ms), ("_graph", ms_graph)):
+            gbps = nbytes / (t * 1e-3) / 1e9
+            tf = 2.0 * m * Nw * Kw / (t * 1e-3) / 1e12
+            row.update({f"us{tag}": round(t * 1e3, 2), f"gbps{tag}": round(gbps, 1),
+                        f"frac_hbm{tag}": round(gbps / 8000.0, 4), f"tflops{tag}": round(tf, 2)})
+        row["graph_output_matches_eager"] = graph_ok
+        rows[f"w4a16_m{m}"] = row
+    return rows
 
 
 def cpu_baseline(ca, sa, ta, cb, sb, tb, K):
