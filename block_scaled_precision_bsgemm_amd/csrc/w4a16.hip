@@ -25,14 +25,14 @@ typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 // ------------------------------------------------------------------ m == 1
 // (one X row per blockIdx.y)
 //
-// Wave = GV_ROWS weight rows.  In each 4096-element chunk of K, lane l owns K
+// Wave = R weight rows.  In each 4096-element chunk of K, lane l owns K
 // [32 l, 32 l + 32) and [2048 + 32 l, 2048 + 32 l + 32): one 16-byte code
 // load per row and half, so every load instruction reads 1 KB of one row.
 // All loads of a chunk are issued before any arithmetic.  Each 16-element
 // block's dot product is taken on the unscaled E2M1 values (exact in BF16,
 // via fdot2); the block's full E4M3 scale is applied once, in FP32.
 
-constexpr int GV_ROWS = 4, GV_WAVES = 4;
+constexpr int GV_WAVES = 4;   // waves per workgroup; the rows per wave are a template parameter
 
 template <int J>
 __device__ __forceinline__ float dot_e2m1_pair(uint32_t codes, uint32_t xpair, float acc) {
@@ -94,10 +94,10 @@ __device__ __forceinline__ int rows_lane(int lane) {
   return r;
 }
 
+template <int R>
 __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
     const float* __restrict__ Wts, uint16_t* __restrict__ C, int N, int K) {
-  constexpr int R = GV_ROWS;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // row blockIdx.y of X and C (the vector-ALU path forced on m > 1 re-reads
   // W once per row)
@@ -390,7 +390,8 @@ namespace {
 struct W4Config {
   const char* name;
   int mt;     // 0: vector-ALU gemv (one X row per grid row); else the MFMA kernel's m tile
-  int nb;     // W rows per workgroup; 0 = the fit width (w4a16_fit_nb)
+  int nb;     // MFMA: W rows per workgroup, 0 = the fit width (w4a16_fit_nb);
+              // vector ALU: W rows per wave, 0 = 4
   int ring;   // W register ring depth in stages; 0 = the m tile's default (16, 32: 1; 64: 4)
 };
 
@@ -402,6 +403,7 @@ constexpr W4Config kW4Configs[] = {
     {"mfma_m16_nfit_r2", 16, 0, 2}, {"mfma_m16_nfit_r4", 16, 0, 4},
     {"mfma_m32_nfit_r2", 32, 0, 2}, {"mfma_m32_nfit_r4", 32, 0, 4},
     {"mfma_m64_nfit_r2", 64, 0, 2},
+    {"valu_gemv_w2", 0, 2}, {"valu_gemv_w8", 0, 8},
 };
 constexpr int kW4NumConfigs = sizeof(kW4Configs) / sizeof(kW4Configs[0]);
 
@@ -441,13 +443,24 @@ int w4a16_config_id(int mt, int nb) {
 }
 
 //   - W register ring depth: the 64-row m tile keeps 4 stages (rechecked
-//     +3.7% over 2 at k = 4096 and 14336); the 16- and 32-row tiles keep 4
-//     for k >= 8192 (+3.5-8% at k = 14336) and 1 below (4 lost at k = 4096).
+//     +3.7% over 2 at k = 4096 and 14336); the 32-row tile keeps 4 for
+//     k >= 7168 (+3.5-8% at k = 14336) and 1 below (4 lost at k = 4096); the
+//     16-row tile likewise, but only while it spans at most 3 m tiles (+5.5%
+//     rechecked at k = 7168; 2-4% slower in the screen at 4 or more tiles).
+//   - For n <= 1024 the MFMA kernel fills at most 64 workgroups, so the
+//     vector-ALU kernel also takes m up to 16 there.
+//   - The vector-ALU kernel takes 2 W rows per wave instead of 4 where 4 rows
+//     leave fewer than about 3 waves per CU per X row (m = 1 at n <= 4096,
+//     m <= 4 at n <= 2560, any m at n <= 1024): rechecked +7-12% at
+//     2560 x 10240 and 1536 x 8960; at larger m or n the extra waves re-read
+//     X and lose (-9-16% rechecked at m = 2-8, n = 1536-4096).
 int w4a16_select(int64_t m, int64_t n, int64_t k) {
-  if (m <= 2 || (m <= 8 && m * n <= 24576)) return 0;   // valu_gemv
+  if (m <= 2 || (m <= 8 && m * n <= 24576) || (m <= 16 && n <= 1024))
+    return ((m <= 1 && n <= 4096) || (m <= 4 && n <= 2560) || n <= 1024) ? 18 : 0;   // valu_gemv_w2 / valu_gemv
   for (int mt : {16, 32, 64})
     if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) {
-      if (k >= 8192 && mt < 64) return mt == 16 ? 14 : 16;   // mfma_m{16,32}_nfit_r4
+      if (k >= 7168 && mt == 32) return 16;              // mfma_m32_nfit_r4
+      if (k >= 7168 && mt == 16 && m <= 48) return 14;   // mfma_m16_nfit_r4
       return w4a16_config_id(mt, 0);
     }
   int best = 64;
@@ -467,8 +480,14 @@ hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint1
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream) {
   const W4Config& cf = kW4Configs[config];
   if (cf.mt == 0) {
-    hipLaunchKernelGGL(gemv_kernel, dim3((unsigned)ceil_div(n, GV_ROWS * GV_WAVES), (unsigned)m), dim3(64 * GV_WAVES),
-                       0, stream, x, w, ws, wts, c, (int)n, (int)k);
+    const int rows = cf.nb > 0 ? cf.nb : 4;   // W rows per wave
+    const dim3 grid((unsigned)ceil_div(n, rows * GV_WAVES), (unsigned)m);
+    if (rows == 8)
+      hipLaunchKernelGGL(gemv_kernel<8>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
+    else if (rows == 2)
+      hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
+    else
+      hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
   } else if (cf.mt == 16) {
     if (cf.ring == 4) launch_skinny<16, 2, 8, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
     else if (cf.ring == 2) launch_skinny<16, 2, 8, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);

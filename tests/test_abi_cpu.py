@@ -134,9 +134,9 @@ def test_grouped_ex_validation(so):
 def test_w4a16_configs_and_exhaustive_selector(so):
     n_cfg = so.bsgemm_w4a16_num_configs()
     names = [so.bsgemm_w4a16_config_name(i).decode() for i in range(n_cfg)]
-    assert n_cfg == 18 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
+    assert n_cfg == 20 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
     assert so.bsgemm_w4a16_config_name(n_cfg) is None and so.bsgemm_w4a16_config_name(-1) is None
-    tile = {nm: (0 if nm == "valu_gemv" else int(nm.split("_")[1][1:])) for nm in names}
+    tile = {nm: (0 if nm.startswith("valu_gemv") else int(nm.split("_")[1][1:])) for nm in names}
 
     def mtile(nm):
         return int(nm.split("_")[1][1:])
@@ -144,28 +144,34 @@ def test_w4a16_configs_and_exhaustive_selector(so):
     def grid(m, n, mt, nb):
         return -(-n // nb) * -(-m // mt)
     # Exhaustive over the grid, checking the selector's stated rule by its
-    # properties: the vector ALU exactly for m <= 2, or m <= 8 with
-    # m * n <= 24576; an MFMA pick with the fit width has an m tile whose
-    # grid fits one wave of 256 workgroups with 64-row slabs, and no smaller
-    # tile does (16/32-row tiles: 4-stage W ring from k = 8192); otherwise no tile fits and the
+    # properties: the vector ALU exactly for m <= 2, m <= 8 with
+    # m * n <= 24576, or m <= 16 with n <= 1024 (2 W rows per wave where 4
+    # would leave few waves); an MFMA pick with the fit width has an m tile
+    # whose grid fits one wave of 256 workgroups with 64-row slabs, and no
+    # smaller tile does (4-stage W ring from k = 7168 for the 32-row tile, and
+    # for the 16-row tile up to 3 m tiles); otherwise no tile fits and the
     # pick uses 64-row slabs.
     decisions = 0
     for n in (1, 64, 896, 1536, 3072, 4096, 5120, 8192, 10240, 14336, 65536):
-        for k in (32, 4096, 14336):
+        for k in (32, 4096, 7168, 14336):
             for m in list(range(0, 130)) + [192, 256, 384, 1024, 1 << 20]:
                 c = so.bsgemm_w4a16_select(m, n, k)
                 decisions += 1
                 assert 0 <= c < n_cfg
                 nm = names[c]
-                assert (nm == "valu_gemv") == (m <= 2 or (m <= 8 and m * n <= 24576)), (m, n, nm)
-                if nm == "valu_gemv":
+                valu = m <= 2 or (m <= 8 and m * n <= 24576) or (m <= 16 and n <= 1024)
+                assert nm.startswith("valu_gemv") == valu, (m, n, nm)
+                if valu:
+                    w2 = (m <= 1 and n <= 4096) or (m <= 4 and n <= 2560) or n <= 1024
+                    assert nm == ("valu_gemv_w2" if w2 else "valu_gemv"), (m, n, nm)
                     continue
                 fits = [t for t in (16, 32, 64) if grid(m, n, t, 64) <= 256]
                 if fits:
-                    assert nm == f"mfma_m{fits[0]}_nfit" + ("_r4" if k >= 8192 and fits[0] < 64 else ""), (m, n, k, nm)
+                    r4 = k >= 7168 and (fits[0] == 32 or (fits[0] == 16 and m <= 48))
+                    assert nm == f"mfma_m{fits[0]}_nfit" + ("_r4" if r4 else ""), (m, n, k, nm)
                 else:
                     assert nm.endswith("_n64"), (m, n, nm)
-    assert decisions == 11 * 3 * 135
+    assert decisions == 11 * 4 * 135
     assert so.bsgemm_w4a16_select(4, 64, 48) == -1 and so.bsgemm_w4a16_select(-1, 64, 64) == -1
 
 
@@ -179,7 +185,7 @@ def test_w4a16_forced_config_validation(so, monkeypatch):
     monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "no_such_tile")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert b"FORCE_CONFIG" in so.bsgemm_last_error()
-    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "18")
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "20")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     import torch
     if not torch.cuda.is_available():
