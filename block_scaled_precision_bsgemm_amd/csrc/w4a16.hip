@@ -152,12 +152,14 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 // ------------------------------------------------------------------ m >= 2
 //
 // Workgroup = SK_CONS consumer waves + SK_PROD producer waves.  It owns W rows
-// [n0, n0 + nb) (nb <= 64: four 16-row MFMA tiles; rows past nb are masked)
-// and X rows [m0, m0 + MT), over all of K.
+// [n0, n0 + nb) (nb <= 16 TP NT: TP NT 16-row MFMA tiles; rows past nb are
+// masked) and X rows [m0, m0 + MT), over all of K.
 //
-// K is cut into 128-element blocks; stage s holds KS consecutive blocks.
-// Consumer c = (tile group g = c % TP, K split h = c / TP) owns the NT = 4/TP
-// W tiles of group g and, in stage s, block KS s + h.  It loads its W codes
+// K is cut into 128-element blocks; stage s holds KS = SK_CONS / TP
+// consecutive blocks.  Consumer c = (tile group g = c % TP, K split h = c / TP)
+// owns the NT W tiles of group g and, in stage s, block KS s + h.  With one
+// tile (TP = NT = 1, nb = 16) all eight consumers split K, so a narrow slab
+// still has eight waves streaming W.  It loads its W codes
 // straight from HBM into registers, RING stages ahead, dequantises them exactly
 // to BF16 (dequant2_bf16) and runs 16x16x32 BF16 MFMAs against X fragments
 // from LDS.
@@ -219,12 +221,12 @@ __device__ __forceinline__ void sk_produce(SkStage<MT, KS>* st, const uint16_t* 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
 }
 
-template <int MT, int TP, int NSLOT, int RING, bool SDMA>
+template <int MT, int TP, int NT, int NSLOT, int RING, bool SDMA>
 __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
     const float* __restrict__ Wts, uint16_t* __restrict__ C, int M, int N, int K, int nb, int m_tiles) {
-  constexpr int NJ = MT / 16, KS = SK_CONS / TP, NT = 4 / TP;
-  static_assert(KS % 2 == 0 && NT * TP == 4, "consumer split");
+  constexpr int NJ = MT / 16, KS = SK_CONS / TP, NTILE = TP * NT;
+  static_assert(KS % 2 == 0 && NTILE <= 4, "consumer split");
   __shared__ SkStage<MT, KS> st[NSLOT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // consecutive workgroups (the m tiles of one W slab) share an XCD's L2
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
     });
   }
 
-  // ---- sum the K splits through LDS; consumer i (< 4) finishes W tile i
+  // ---- sum the K splits through LDS; consumer i (< NTILE) finishes W tile i
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   v4f* red = reinterpret_cast<v4f*>(&st[0]);   // [consumer][il][j][lane]
   static_assert(SK_CONS * NT * NJ * 64 * sizeof(v4f) <= sizeof(st), "reduction space");
@@ -329,7 +331,7 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) red[((wave * NT + il) * NJ + j) * 64 + lane] = acc[il][j];
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  if (wave >= 4) return;
+  if (wave >= NTILE) return;
   const float ts = *Wts;
   const int i = wave, gi = i / NT, il = i % NT;
 #pragma unroll
@@ -357,19 +359,21 @@ int64_t w4a16_fit_nb(int64_t m, int64_t n, int mt) {
   return std::min<int64_t>(64, std::max<int64_t>(16, ceil_div(n, per_mtile)));
 }
 
-template <int MT, int TP, int NSLOT, int RING>
-void launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w, const uint8_t* ws,
-                   const float* wts, uint16_t* c, int nb_forced, hipStream_t stream) {
+template <int MT, int TP, int NT, int NSLOT, int RING>
+hipError_t launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w, const uint8_t* ws,
+                         const float* wts, uint16_t* c, int nb_forced, hipStream_t stream) {
   // W rows per workgroup (the tile width along N): forced, or the fit width
   const int nb = nb_forced > 0 ? nb_forced : (int)w4a16_fit_nb(m, n, MT);
+  if (nb > 16 * TP * NT) return hipErrorInvalidValue;   // the table pairs slab widths with tilings
   const int n_tiles = (int)ceil_div(n, nb), m_tiles = (int)ceil_div(m, MT);
   const dim3 grid((unsigned)(n_tiles * m_tiles));
   if (k % 256 == 0)
-    hipLaunchKernelGGL((skinny_kernel<MT, TP, NSLOT, RING, true>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
+    hipLaunchKernelGGL((skinny_kernel<MT, TP, NT, NSLOT, RING, true>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
                        wts, c, (int)m, (int)n, (int)k, nb, m_tiles);
   else
-    hipLaunchKernelGGL((skinny_kernel<MT, TP, NSLOT, RING, false>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
+    hipLaunchKernelGGL((skinny_kernel<MT, TP, NT, NSLOT, RING, false>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
                        wts, c, (int)m, (int)n, (int)k, nb, m_tiles);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -393,6 +397,7 @@ struct W4Config {
   int nb;     // MFMA: W rows per workgroup, 0 = the fit width (w4a16_fit_nb);
               // vector ALU: W rows per wave, 0 = 4
   int ring;   // W register ring depth in stages; 0 = the m tile's default (16, 32: 1; 64: 4)
+  bool ksplit = false;   // MFMA: one 16-row W tile per workgroup, K split over all 8 consumers
 };
 
 constexpr W4Config kW4Configs[] = {
@@ -404,6 +409,8 @@ constexpr W4Config kW4Configs[] = {
     {"mfma_m32_nfit_r2", 32, 0, 2}, {"mfma_m32_nfit_r4", 32, 0, 4},
     {"mfma_m64_nfit_r2", 64, 0, 2},
     {"valu_gemv_w2", 0, 2}, {"valu_gemv_w8", 0, 8},
+    {"mfma_m16_n16_ks8", 16, 16, 8, true}, {"mfma_m16_n16_ks8_r4", 16, 16, 4, true},
+    {"mfma_m32_n16_ks8", 32, 16, 8, true},
 };
 constexpr int kW4NumConfigs = sizeof(kW4Configs) / sizeof(kW4Configs[0]);
 
@@ -419,22 +426,31 @@ int w4a16_config_max_m(int config) { return kW4Configs[config].mt == 0 ? 65535 :
 
 // The selector, fitted to rechecked calibration measurements (N x K in
 // {14336 x 4096, 4096 x 14336, 4096 x 4096, 1536 x 8960}) and checked on
-// held-out shapes (2048 x 8192, 3072 x 4096, 5120 x 4096, 8192 x 2048,
-// 896 x 4864, 6144 x 4096, 10240 x 2560, 2560 x 10240, 1024 x 1024), M from 1
-// to 256.  One rule with a physical reason:
-//   - vector ALU for m <= 2, or m <= 8 with m * n <= 24576: it re-reads W
-//     once per row (from the infinity cache) but has no fixed MFMA-pipeline
-//     cost;
-//   - otherwise the MFMA kernel, whose workgroups each hold a whole CU.
-//     While the grid fits in one wave of workgroups (one per CU), time
-//     follows the work per workgroup: take the smallest m tile whose grid
-//     fits with 64-row W slabs, then the narrowest slab that still fits (the
-//     fit width), which fills the wave.
+// further shapes (2048 x 8192, 3072 x 4096, 5120 x 4096, 8192 x 2048,
+// 896 x 4864, 6144 x 4096, 10240 x 2560, 2560 x 10240, 1024 x 1024,
+// 768 x 3072, 1280 x 5120, 3584 x 7168, 2048 x 2048, 12288 x 3072,
+// 2048 x 6144, 1792 x 7168, 2304 x 9216, 3328 x 5120, 7168 x 7168), M from 1
+// to 256.  Rules, each with a physical reason:
+//   - vector ALU for m <= 2: no fixed MFMA-pipeline cost, and at two rows
+//     the second pass over W comes from the infinity cache;
+//   - 16-row W slabs with K split over all eight consumer waves while that
+//     grid fits one wave of workgroups (m tile 16, else 32), or two waves
+//     for k >= 7168 with the 16-row tile: every consumer streams W, and the
+//     W slab is read once per 16 or 32 rows of X.  Rechecked 2-2.3x faster
+//     than the four-tile kernel at n = 1536-4096 (whose 16-row slabs left six
+//     of eight consumers streaming nothing) and 1.1-3x faster than the vector
+//     ALU from m = 3;
+//   - vector ALU for m <= 8 with m * n <= 24576;
+//   - otherwise the four-tile MFMA kernel, whose workgroups each hold a
+//     whole CU.  While the grid fits in one wave of workgroups (one per CU),
+//     time follows the work per workgroup: take the smallest m tile whose
+//     grid fits with 64-row W slabs, then the narrowest slab that still fits
+//     (the fit width), which fills the wave.
 //   - If no m tile fits, 64-row slabs and the m tile with the fewest
 //     weighted waves: a wave of 16-, 32- and 64-row tiles costs about 0.8,
 //     1 and 1.5 (measured: workgroup time is mostly the W stream, not the
 //     MFMA work); ties go to the larger tile.
-// The previous rule (m tile by m alone, slab width from n alone) was within
+// The first rule (m tile by m alone, slab width from n alone) was within
 // 3% only for n >= 12288; at n = 4096 its 16-row slabs re-read X for little W
 // and ran up to 3.4x slower.
 int w4a16_config_id(int mt, int nb) {
@@ -447,16 +463,21 @@ int w4a16_config_id(int mt, int nb) {
 //     k >= 7168 (+3.5-8% at k = 14336) and 1 below (4 lost at k = 4096); the
 //     16-row tile likewise, but only while it spans at most 3 m tiles (+5.5%
 //     rechecked at k = 7168; 2-4% slower in the screen at 4 or more tiles).
-//   - For n <= 1024 the MFMA kernel fills at most 64 workgroups, so the
-//     vector-ALU kernel also takes m up to 16 there.
 //   - The vector-ALU kernel takes 2 W rows per wave instead of 4 where 4 rows
-//     leave fewer than about 3 waves per CU per X row (m = 1 at n <= 4096,
-//     m <= 4 at n <= 2560, any m at n <= 1024): rechecked +7-12% at
-//     2560 x 10240 and 1536 x 8960; at larger m or n the extra waves re-read
-//     X and lose (-9-16% rechecked at m = 2-8, n = 1536-4096).
+//     leave fewer than about 3 waves per CU per X row (n <= 2560, or m = 1
+//     at n <= 4096): rechecked +7-12% at 2560 x 10240 and 1536 x 8960; at
+//     larger m or n the extra waves re-read X and lose (-9-16% rechecked at
+//     m = 2-8, n = 1536-4096).
+//   - The K-split kernel keeps a 4-stage W ring: against 8 stages the median
+//     ratio over 180 cells was within 2.5% at every K but 8960 (4.6%).
 int w4a16_select(int64_t m, int64_t n, int64_t k) {
-  if (m <= 2 || (m <= 8 && m * n <= 24576) || (m <= 16 && n <= 1024))
-    return ((m <= 1 && n <= 4096) || (m <= 4 && n <= 2560) || n <= 1024) ? 18 : 0;   // valu_gemv_w2 / valu_gemv
+  const int gemv = (n <= 2560 || (m <= 1 && n <= 4096)) ? 18 : 0;   // valu_gemv_w2 / valu_gemv
+  if (m <= 2) return gemv;
+  const int64_t slabs = ceil_div(n, 16);
+  if (slabs * ceil_div(m, 16) <= kW4Workgroups) return 21;                   // mfma_m16_n16_ks8_r4
+  if (slabs * ceil_div(m, 32) <= kW4Workgroups) return 22;                   // mfma_m32_n16_ks8
+  if (k >= 7168 && slabs * ceil_div(m, 16) <= 2 * kW4Workgroups) return 21;
+  if (m <= 8 && m * n <= 24576) return gemv;
   for (int mt : {16, 32, 64})
     if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) {
       if (k >= 7168 && mt == 32) return 16;              // mfma_m32_nfit_r4
@@ -488,17 +509,21 @@ hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint1
       hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
     else
       hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
+  } else if (cf.ksplit) {
+    if (cf.mt == 32) return launch_skinny<32, 1, 1, 2, 8>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 4) return launch_skinny<16, 1, 1, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    return launch_skinny<16, 1, 1, 4, 8>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else if (cf.mt == 16) {
-    if (cf.ring == 4) launch_skinny<16, 2, 8, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
-    else if (cf.ring == 2) launch_skinny<16, 2, 8, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
-    else launch_skinny<16, 2, 8, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 4) return launch_skinny<16, 2, 2, 8, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 2) return launch_skinny<16, 2, 2, 8, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    return launch_skinny<16, 2, 2, 8, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else if (cf.mt == 32) {
-    if (cf.ring == 4) launch_skinny<32, 2, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
-    else if (cf.ring == 2) launch_skinny<32, 2, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
-    else launch_skinny<32, 2, 4, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 4) return launch_skinny<32, 2, 2, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 2) return launch_skinny<32, 2, 2, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    return launch_skinny<32, 2, 2, 4, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else {
-    if (cf.ring == 2) launch_skinny<64, 4, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
-    else launch_skinny<64, 4, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.ring == 2) return launch_skinny<64, 4, 1, 4, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    return launch_skinny<64, 4, 1, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   }
   return hipGetLastError();
 }

@@ -644,12 +644,14 @@ def _w4_case(m, n, k, seed):
     return x, qw
 
 
-@pytest.mark.parametrize("config", range(20))
+@pytest.mark.parametrize("config", range(23))
 def test_w4a16_every_config(gpu_lib, config):
     """Each configuration, forced, on shapes it would never be chosen for:
-    ragged m, n and K tails (K % 256 != 0 uses per-lane scale loads)."""
+    ragged m, n and K tails (K % 256 != 0 uses per-lane scale loads), and a
+    K long enough to wrap the deepest W register ring (8 stages of 1024)."""
     name = L.w4a16_configs()[config]
-    for (m, n, k) in [(1, 300, 1024), (5, 72, 2048 + 96), (33, 129, 512), (70, 260, 4096 + 256)]:
+    for (m, n, k) in [(1, 300, 1024), (5, 72, 2048 + 96), (33, 129, 512), (70, 260, 4096 + 256),
+                      (9, 40, 9216 + 32)]:
         x, qw = _w4_case(m, n, k, 1000 * config + m)
         say("w4a16 forced", name, m, n, k)
         c = out_bf16(m, n)
