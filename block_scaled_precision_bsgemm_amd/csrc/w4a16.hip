@@ -155,11 +155,13 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 // [n0, n0 + nb) (nb <= 16 TP NT: TP NT 16-row MFMA tiles; rows past nb are
 // masked) and X rows [m0, m0 + MT), over all of K.
 //
-// K is cut into 128-element blocks; stage s holds KS = SK_CONS / TP
-// consecutive blocks.  Consumer c = (tile group g = c % TP, K split h = c / TP)
-// owns the NT W tiles of group g and, in stage s, block KS s + h.  With one
-// tile (TP = NT = 1, nb = 16) all eight consumers split K, so a narrow slab
-// still has eight waves streaming W.  It loads its W codes
+// K is cut into 128-element blocks; stage s holds SB = KS BPS consecutive
+// blocks, KS = SK_CONS / TP.  Consumer c = (tile group g = c % TP, K split
+// h = c / TP) owns the NT W tiles of group g and, in stage s, blocks
+// SB s + KS b + h for b < BPS.  With one tile (TP = NT = 1, nb = 16) all
+// eight consumers split K, so a narrow slab still has eight waves streaming
+// W.  More blocks per stage (BPS > 1) mean fewer workgroup barriers, each of
+// which holds all ten waves to the slowest one.  A consumer loads its W codes
 // straight from HBM into registers, RING stages ahead, dequantises them exactly
 // to BF16 (dequant2_bf16) and runs 16x16x32 BF16 MFMAs against X fragments
 // from LDS.
@@ -177,25 +179,25 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 
 constexpr int SK_CONS = 8, SK_PROD = 2, SK_THREADS = 64 * (SK_CONS + SK_PROD);
 
-template <int MT, int KS>
+template <int MT, int SB>
 struct SkStage {
-  uint4 x[KS][MT * 16];    // [block][row m: 16 chunks of 16 B; chunk c at c ^ (m & 15)]
-  uint4 s[64 * KS / 2];    // W scales of the stage: row r at bytes [8 KS r, 8 KS r + 8 KS)
+  uint4 x[SB][MT * 16];    // [block][row m: 16 chunks of 16 B; chunk c at c ^ (m & 15)]
+  uint4 s[64 * SB / 2];    // W scales of the stage: row r at bytes [8 SB r, 8 SB r + 8 SB)
 };
 
-template <int MT, int KS, int NSLOT, bool SDMA, int P>
-__device__ __forceinline__ void sk_produce(SkStage<MT, KS>* st, const uint16_t* X, const uint8_t* Ws, int m0,
+template <int MT, int SB, int NSLOT, bool SDMA, int P>
+__device__ __forceinline__ void sk_produce(SkStage<MT, SB>* st, const uint16_t* X, const uint8_t* Ws, int m0,
                                            int n0, int rows_x, int rows_w, int K, int S, int lane) {
-  constexpr int XD = KS * MT / 4;             // X loads per stage (1 KB each)
-  constexpr int SD = SDMA ? KS / 2 : 0;       // scale loads per stage (1 KB each)
+  constexpr int XD = SB * MT / 4;             // X loads per stage (1 KB each)
+  constexpr int SD = SDMA ? SB / 2 : 0;       // scale loads per stage (1 KB each)
   constexpr int CNT = (XD + SK_PROD - 1 - P) / SK_PROD + (SD + SK_PROD - 1 - P) / SK_PROD;
   static_assert(CNT * (NSLOT - 2) < 64, "outstanding loads exceed the vmcnt range");
   const int KB = K / 16;
   const auto x_rsrc = make_rsrc4(X + (int64_t)m0 * K, rows_x * K * 2);
   const auto s_rsrc = make_rsrc4(Ws + (int64_t)n0 * KB, rows_w * KB);
   auto issue = [&](int s) {
-    SkStage<MT, KS>& t = st[s % NSLOT];
-    const int kst = s * 128 * KS;
+    SkStage<MT, SB>& t = st[s % NSLOT];
+    const int kst = s * 128 * SB;
 #pragma unroll
     for (int i = P; i < XD; i += SK_PROD) {
       // 4 rows of block j: lane -> (row m, LDS chunk lane & 15)
@@ -206,8 +208,8 @@ __device__ __forceinline__ void sk_produce(SkStage<MT, KS>* st, const uint16_t* 
     }
 #pragma unroll
     for (int i = P; i < SD; i += SK_PROD) {
-      const int e = 64 * i + lane;                      // 16-byte piece: row e / (KS/2)
-      const int r = e / (KS / 2), b = kst / 16 + 16 * (e % (KS / 2));
+      const int e = 64 * i + lane;                      // 16-byte piece: row e / (SB/2)
+      const int r = e / (SB / 2), b = kst / 16 + 16 * (e % (SB / 2));
       dma_x4(s_rsrc, lds_addr(&t.s[64 * i]), b < KB ? r * KB + b : OOB);
     }
   };
@@ -221,49 +223,53 @@ __device__ __forceinline__ void sk_produce(SkStage<MT, KS>* st, const uint16_t* 
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier\n\ts_barrier" ::: "memory");
 }
 
-template <int MT, int TP, int NT, int NSLOT, int RING, bool SDMA>
+template <int MT, int TP, int NT, int NSLOT, int RING, int BPS, bool SDMA>
 __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
     const float* __restrict__ Wts, uint16_t* __restrict__ C, int M, int N, int K, int nb, int m_tiles) {
-  constexpr int NJ = MT / 16, KS = SK_CONS / TP, NTILE = TP * NT;
+  constexpr int NJ = MT / 16, KS = SK_CONS / TP, NTILE = TP * NT, SB = KS * BPS;
   static_assert(KS % 2 == 0 && NTILE <= 4, "consumer split");
-  __shared__ SkStage<MT, KS> st[NSLOT];
+  __shared__ SkStage<MT, SB> st[NSLOT];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // consecutive workgroups (the m tiles of one W slab) share an XCD's L2
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int n0 = (lin / m_tiles) * nb, m0 = (lin % m_tiles) * MT;
   const int KH = K / 2, KB = K / 16;
   const int rows_w = max(0, min(nb, N - n0)), rows_x = max(0, min(MT, M - m0));
-  const int S = (K + 128 * KS - 1) / (128 * KS);
+  const int S = (K + 128 * SB - 1) / (128 * SB);
 
   if (wave >= SK_CONS) {
-    if (wave == SK_CONS) sk_produce<MT, KS, NSLOT, SDMA, 0>(st, X, Ws, m0, n0, rows_x, rows_w, K, S, lane);
-    else sk_produce<MT, KS, NSLOT, SDMA, 1>(st, X, Ws, m0, n0, rows_x, rows_w, K, S, lane);
+    if (wave == SK_CONS) sk_produce<MT, SB, NSLOT, SDMA, 0>(st, X, Ws, m0, n0, rows_x, rows_w, K, S, lane);
+    else sk_produce<MT, SB, NSLOT, SDMA, 1>(st, X, Ws, m0, n0, rows_x, rows_w, K, S, lane);
     return;
   }
 
   // ------------------------------------------------------------ consumers
+  // In stage s consumer h takes the stage's blocks KS b + h, b < BPS (block
+  // SB s + KS b + h of K).
   const int g = wave % TP, h = wave / TP;
   const int r = lane & 15, q = lane >> 4;
   const auto c_rsrc = make_rsrc(Wc + (int64_t)n0 * KH, rows_w * KH);
   const auto s_rsrc = make_rsrc(Ws + (int64_t)n0 * KB, rows_w * KB);
   auto wrow = [&](int il) { return 16 * (g * NT + il) + r; };
-  auto wload = [&](int s, int il) -> uint4 {
-    const int t = KS * s + h, k = 128 * t + 32 * q;
+  auto wload = [&](int s, int b, int il) -> uint4 {
+    const int t = SB * s + KS * b + h, k = 128 * t + 32 * q;
     return buffer_load_x4(c_rsrc, (s < S && k < K) ? wrow(il) * KH + 64 * t + 16 * q : OOB);
   };
-  auto sload = [&](int s, int il) -> uint32_t {   // scales of blocks 8t + 2q, 8t + 2q + 1
-    const int t = KS * s + h, k = 128 * t + 32 * q;
+  auto sload = [&](int s, int b, int il) -> uint32_t {   // scales of blocks 8t + 2q, 8t + 2q + 1
+    const int t = SB * s + KS * b + h, k = 128 * t + 32 * q;
     return SDMA ? 0u : buffer_load_u16(s_rsrc, (s < S && k < K) ? wrow(il) * KB + 8 * t + 2 * q : OOB);
   };
-  uint4 wr[RING][NT];
-  uint32_t sr[RING][NT];
+  uint4 wr[RING][BPS][NT];
+  uint32_t sr[RING][BPS][NT];
   static_for<0, RING>([&](auto B) {
 #pragma unroll
-    for (int il = 0; il < NT; ++il) {
-      wr[B][il] = wload(B, il);
-      sr[B][il] = sload(B, il);
-    }
+    for (int b = 0; b < BPS; ++b)
+#pragma unroll
+      for (int il = 0; il < NT; ++il) {
+        wr[B][b][il] = wload(B, b, il);
+        sr[B][b][il] = sload(B, b, il);
+      }
   });
   v4f acc[NT][NJ];
 #pragma unroll
@@ -271,56 +277,73 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[il][j] = v4f{};
 
-  for (int s0 = 0; s0 < S; s0 += RING) {
-    static_for<0, RING>([&](auto B) {
-      const int s = s0 + B;
-      if (s < S) {
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage s published
-        const SkStage<MT, KS>& t = st[s % NSLOT];
-        float sc[NT][2], mn[NT][2];
+  // One stage: ring slot B holds stage s's W codes.
+  auto stage = [&](const int s, auto B) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // stage s published
+    const SkStage<MT, SB>& t = st[s % NSLOT];
+    static_for<0, BPS>([&](auto b) {
+      const int jb = KS * b + h;   // the block's index in the stage
+      // every LDS read of the block (X fragments, scales) is issued before
+      // any arithmetic, so their latency overlaps the dequantisation
+      // instead of stalling each MFMA on its own read
+      uint4 xf[4][NJ];
+      uint32_t w16s[NT];
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) xf[sp][j] = t.x[jb][(16 * j + r) * 16 + ((4 * q + sp) ^ r)];
+#pragma unroll
+      for (int il = 0; il < NT; ++il)
+        w16s[il] = SDMA ? *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(t.s) +
+                                                             wrow(il) * 8 * SB + 8 * jb + 2 * q)
+                        : sr[B][b][il];
+      __builtin_amdgcn_sched_barrier(0);
+      float sc[NT][2], mn[NT][2];
+#pragma unroll
+      for (int il = 0; il < NT; ++il) {
+        const uint32_t w16 = w16s[il];
+        sc[il][0] = e4m3_scale_value(w16 & 0xFFu);
+        sc[il][1] = e4m3_scale_value(w16 >> 8);
+        mn[il][0] = scale_mantissa_f32(sc[il][0]);
+        mn[il][1] = scale_mantissa_f32(sc[il][1]);
+      }
+#pragma unroll
+      for (int sp = 0; sp < 4; ++sp) {
+        v8bf_t wv[NT];
 #pragma unroll
         for (int il = 0; il < NT; ++il) {
-          uint32_t w16;
-          if (SDMA)
-            w16 = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(t.s) +
-                                                     wrow(il) * 8 * KS + 8 * h + 2 * q);
-          else
-            w16 = sr[B][il];
-          sc[il][0] = e4m3_scale_value(w16 & 0xFFu);
-          sc[il][1] = e4m3_scale_value(w16 >> 8);
-          mn[il][0] = scale_mantissa_f32(sc[il][0]);
-          mn[il][1] = scale_mantissa_f32(sc[il][1]);
+          const uint4& wq = wr[B][b][il];
+          const uint32_t d = sp == 0 ? wq.x : sp == 1 ? wq.y : sp == 2 ? wq.z : wq.w;
+          const float sv = sc[il][sp >> 1], mv = mn[il][sp >> 1];
+          const uint32_t w4[4] = {dequant2_bf16<0>(d, sv, mv), dequant2_bf16<1>(d, sv, mv),
+                                  dequant2_bf16<2>(d, sv, mv), dequant2_bf16<3>(d, sv, mv)};
+          __builtin_memcpy(&wv[il], w4, 16);
         }
 #pragma unroll
-        for (int sp = 0; sp < 4; ++sp) {
-          v8bf_t wv[NT];
+        for (int j = 0; j < NJ; ++j) {
+          v8bf_t x8;
+          __builtin_memcpy(&x8, &xf[sp][j], 16);
 #pragma unroll
-          for (int il = 0; il < NT; ++il) {
-            const uint32_t d = sp == 0 ? wr[B][il].x : sp == 1 ? wr[B][il].y : sp == 2 ? wr[B][il].z : wr[B][il].w;
-            const float sv = sc[il][sp >> 1], mv = mn[il][sp >> 1];
-            const uint32_t w4[4] = {dequant2_bf16<0>(d, sv, mv), dequant2_bf16<1>(d, sv, mv),
-                                    dequant2_bf16<2>(d, sv, mv), dequant2_bf16<3>(d, sv, mv)};
-            __builtin_memcpy(&wv[il], w4, 16);
-          }
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const uint4 xv = t.x[h][(16 * j + r) * 16 + ((4 * q + sp) ^ r)];
-            v8bf_t x8;
-            __builtin_memcpy(&x8, &xv, 16);
-#pragma unroll
-            for (int il = 0; il < NT; ++il)
-              acc[il][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[il], x8, acc[il][j], 0, 0, 0);
-          }
-        }
-        // refill this ring slot with the block RING stages ahead
-#pragma unroll
-        for (int il = 0; il < NT; ++il) {
-          wr[B][il] = wload(s + RING, il);
-          sr[B][il] = sload(s + RING, il);
+          for (int il = 0; il < NT; ++il)
+            acc[il][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[il], x8, acc[il][j], 0, 0, 0);
         }
       }
+      // refill this ring slot with the block RING stages ahead
+#pragma unroll
+      for (int il = 0; il < NT; ++il) {
+        wr[B][b][il] = wload(s + RING, b, il);
+        sr[B][b][il] = sload(s + RING, b, il);
+      }
     });
-  }
+  };
+  // Whole rounds of RING stages run without a branch around any load, so the
+  // compiler's load counting waits only for the slot each stage consumes;
+  // the last partial round checks each stage.
+  int s0 = 0;
+  for (; s0 + RING <= S; s0 += RING) static_for<0, RING>([&](auto B) { stage(s0 + B, B); });
+  static_for<0, RING>([&](auto B) {
+    if (s0 + B < S) stage(s0 + B, B);
+  });
 
   // ---- sum the K splits through LDS; consumer i (< NTILE) finishes W tile i
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -359,7 +382,7 @@ int64_t w4a16_fit_nb(int64_t m, int64_t n, int mt) {
   return std::min<int64_t>(64, std::max<int64_t>(16, ceil_div(n, per_mtile)));
 }
 
-template <int MT, int TP, int NT, int NSLOT, int RING>
+template <int MT, int TP, int NT, int NSLOT, int RING, int BPS = 1>
 hipError_t launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w, const uint8_t* ws,
                          const float* wts, uint16_t* c, int nb_forced, hipStream_t stream) {
   // W rows per workgroup (the tile width along N): forced, or the fit width
@@ -368,10 +391,10 @@ hipError_t launch_skinny(int64_t m, int64_t n, int64_t k, const uint16_t* x, con
   const int n_tiles = (int)ceil_div(n, nb), m_tiles = (int)ceil_div(m, MT);
   const dim3 grid((unsigned)(n_tiles * m_tiles));
   if (k % 256 == 0)
-    hipLaunchKernelGGL((skinny_kernel<MT, TP, NT, NSLOT, RING, true>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
+    hipLaunchKernelGGL((skinny_kernel<MT, TP, NT, NSLOT, RING, BPS, true>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
                        wts, c, (int)m, (int)n, (int)k, nb, m_tiles);
   else
-    hipLaunchKernelGGL((skinny_kernel<MT, TP, NT, NSLOT, RING, false>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
+    hipLaunchKernelGGL((skinny_kernel<MT, TP, NT, NSLOT, RING, BPS, false>), grid, dim3(SK_THREADS), 0, stream, x, w, ws,
                        wts, c, (int)m, (int)n, (int)k, nb, m_tiles);
   return hipGetLastError();
 }
@@ -398,6 +421,8 @@ struct W4Config {
               // vector ALU: W rows per wave, 0 = 4
   int ring;   // W register ring depth in stages; 0 = the m tile's default (16, 32: 1; 64: 4)
   bool ksplit = false;   // MFMA: one 16-row W tile per workgroup, K split over all 8 consumers
+  int bps = 1;           // MFMA: K blocks per consumer per stage (one workgroup barrier each)
+  int tp = 0;            // MFMA, 64-row m tile: tile groups (0: 4 groups of one tile; 2: 2 groups of two)
 };
 
 constexpr W4Config kW4Configs[] = {
@@ -411,6 +436,10 @@ constexpr W4Config kW4Configs[] = {
     {"valu_gemv_w2", 0, 2}, {"valu_gemv_w8", 0, 8},
     {"mfma_m16_n16_ks8", 16, 16, 8, true}, {"mfma_m16_n16_ks8_r4", 16, 16, 4, true},
     {"mfma_m32_n16_ks8", 32, 16, 8, true},
+    {"mfma_m16_nfit_b2", 16, 0, 1, false, 2}, {"mfma_m16_nfit_b4", 16, 0, 1, false, 4},
+    {"mfma_m32_nfit_b2", 32, 0, 1, false, 2}, {"mfma_m64_nfit_b2", 64, 0, 2, false, 2},
+    {"mfma_m64_n64_b2", 64, 64, 2, false, 2}, {"mfma_m16_n16_ks8_b2", 16, 16, 2, true, 2},
+    {"mfma_m64_nfit_t2", 64, 0, 2, false, 1, 2}, {"mfma_m64_n64_t2", 64, 64, 2, false, 1, 2},
 };
 constexpr int kW4NumConfigs = sizeof(kW4Configs) / sizeof(kW4Configs[0]);
 
@@ -431,15 +460,15 @@ int w4a16_config_max_m(int config) { return kW4Configs[config].mt == 0 ? 65535 :
 // 768 x 3072, 1280 x 5120, 3584 x 7168, 2048 x 2048, 12288 x 3072,
 // 2048 x 6144, 1792 x 7168, 2304 x 9216, 3328 x 5120, 7168 x 7168), M from 1
 // to 256.  Rules, each with a physical reason:
-//   - vector ALU for m <= 2: no fixed MFMA-pipeline cost, and at two rows
-//     the second pass over W comes from the infinity cache;
+//   - vector ALU for m <= 2, or m <= 4 at n <= 2048: no fixed MFMA-pipeline
+//     cost, and the second to fourth passes over W come from the caches;
 //   - 16-row W slabs with K split over all eight consumer waves while that
 //     grid fits one wave of workgroups (m tile 16, else 32), or two waves
 //     for k >= 7168 with the 16-row tile: every consumer streams W, and the
 //     W slab is read once per 16 or 32 rows of X.  Rechecked 2-2.3x faster
 //     than the four-tile kernel at n = 1536-4096 (whose 16-row slabs left six
 //     of eight consumers streaming nothing) and 1.1-3x faster than the vector
-//     ALU from m = 3;
+//     ALU from m = 3 where n > 2048;
 //   - vector ALU for m <= 8 with m * n <= 24576;
 //   - otherwise the four-tile MFMA kernel, whose workgroups each hold a
 //     whole CU.  While the grid fits in one wave of workgroups (one per CU),
@@ -450,6 +479,13 @@ int w4a16_config_max_m(int config) { return kW4Configs[config].mt == 0 ? 65535 :
 //     weighted waves: a wave of 16-, 32- and 64-row tiles costs about 0.8,
 //     1 and 1.5 (measured: workgroup time is mostly the W stream, not the
 //     MFMA work); ties go to the larger tile.
+//   - Four-tile variant per m tile, from the screen medians of every
+//     variant over all cells relative to the best of them (max loss of the
+//     pick in brackets): 16 rows: 2-stage W ring below k = 7168 (3.2%), 2
+//     blocks per stage from there (3.2%); 32 rows: 2 blocks per stage from
+//     k = 4096 (0%), 1 ring stage below (1.2%); 64 rows: two tile groups of
+//     two tiles (2.4%), which halves the LDS reads of X, against 10-16% for
+//     the four-group tiling.
 // The first rule (m tile by m alone, slab width from n alone) was within
 // 3% only for n >= 12288; at n = 4096 its 16-row slabs re-read X for little W
 // and ran up to 3.4x slower.
@@ -458,11 +494,6 @@ int w4a16_config_id(int mt, int nb) {
   return base + (nb == 0 ? 0 : nb == 16 ? 1 : nb == 32 ? 2 : 3);
 }
 
-//   - W register ring depth: the 64-row m tile keeps 4 stages (rechecked
-//     +3.7% over 2 at k = 4096 and 14336); the 32-row tile keeps 4 for
-//     k >= 7168 (+3.5-8% at k = 14336) and 1 below (4 lost at k = 4096); the
-//     16-row tile likewise, but only while it spans at most 3 m tiles (+5.5%
-//     rechecked at k = 7168; 2-4% slower in the screen at 4 or more tiles).
 //   - The vector-ALU kernel takes 2 W rows per wave instead of 4 where 4 rows
 //     leave fewer than about 3 waves per CU per X row (n <= 2560, or m = 1
 //     at n <= 4096): rechecked +7-12% at 2560 x 10240 and 1536 x 8960; at
@@ -472,7 +503,7 @@ int w4a16_config_id(int mt, int nb) {
 //     ratio over 180 cells was within 2.5% at every K but 8960 (4.6%).
 int w4a16_select(int64_t m, int64_t n, int64_t k) {
   const int gemv = (n <= 2560 || (m <= 1 && n <= 4096)) ? 18 : 0;   // valu_gemv_w2 / valu_gemv
-  if (m <= 2) return gemv;
+  if (m <= 2 || (m <= 4 && n <= 2048)) return gemv;
   const int64_t slabs = ceil_div(n, 16);
   if (slabs * ceil_div(m, 16) <= kW4Workgroups) return 21;                   // mfma_m16_n16_ks8_r4
   if (slabs * ceil_div(m, 32) <= kW4Workgroups) return 22;                   // mfma_m32_n16_ks8
@@ -480,9 +511,9 @@ int w4a16_select(int64_t m, int64_t n, int64_t k) {
   if (m <= 8 && m * n <= 24576) return gemv;
   for (int mt : {16, 32, 64})
     if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) {
-      if (k >= 7168 && mt == 32) return 16;              // mfma_m32_nfit_r4
-      if (k >= 7168 && mt == 16 && m <= 48) return 14;   // mfma_m16_nfit_r4
-      return w4a16_config_id(mt, 0);
+      if (mt == 64) return 29;                           // mfma_m64_nfit_t2
+      if (mt == 32) return k >= 4096 ? 25 : 5;           // mfma_m32_nfit_b2 / mfma_m32_nfit
+      return k >= 7168 ? 23 : 13;                        // mfma_m16_nfit_b2 / mfma_m16_nfit_r2
     }
   int best = 64;
   double best_cost = 0;
@@ -494,7 +525,7 @@ int w4a16_select(int64_t m, int64_t n, int64_t k) {
       best_cost = cost;
     }
   }
-  return w4a16_config_id(best, 64);
+  return best == 64 ? 30 : w4a16_config_id(best, 64);   // mfma_m64_n64_t2
 }
 
 hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
@@ -509,6 +540,14 @@ hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint1
       hipLaunchKernelGGL(gemv_kernel<2>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
     else
       hipLaunchKernelGGL(gemv_kernel<4>, grid, dim3(64 * GV_WAVES), 0, stream, x, w, ws, wts, c, (int)n, (int)k);
+  } else if (cf.tp == 2 && cf.mt == 64) {
+    return launch_skinny<64, 2, 2, 2, 2, 1>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+  } else if (cf.bps > 1) {
+    if (cf.ksplit) return launch_skinny<16, 1, 1, 2, 2, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.mt == 16 && cf.bps == 4) return launch_skinny<16, 2, 2, 2, 1, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.mt == 16) return launch_skinny<16, 2, 2, 4, 1, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    if (cf.mt == 32) return launch_skinny<32, 2, 2, 2, 1, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
+    return launch_skinny<64, 4, 1, 2, 2, 2>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
   } else if (cf.ksplit) {
     if (cf.mt == 32) return launch_skinny<32, 1, 1, 2, 8>(m, n, k, x, w, ws, wts, c, cf.nb, stream);
     if (cf.ring == 4) return launch_skinny<16, 1, 1, 4, 4>(m, n, k, x, w, ws, wts, c, cf.nb, stream);

@@ -134,7 +134,7 @@ def test_grouped_ex_validation(so):
 def test_w4a16_configs_and_exhaustive_selector(so):
     n_cfg = so.bsgemm_w4a16_num_configs()
     names = [so.bsgemm_w4a16_config_name(i).decode() for i in range(n_cfg)]
-    assert n_cfg == 23 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
+    assert n_cfg == 31 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
     assert so.bsgemm_w4a16_config_name(n_cfg) is None and so.bsgemm_w4a16_config_name(-1) is None
     tile = {nm: (0 if nm.startswith("valu_gemv") else int(nm.split("_")[1][1:])) for nm in names}
 
@@ -144,15 +144,14 @@ def test_w4a16_configs_and_exhaustive_selector(so):
     def grid(m, n, mt, nb):
         return -(-n // nb) * -(-m // mt)
     # Exhaustive over the grid, checking the selector's stated rule by its
-    # properties: the vector ALU for m <= 2 (2 W rows per wave where 4 would
-    # leave few waves); then 16-row W slabs with an 8-way K split while that
-    # grid fits one wave of 256 workgroups (m tile 16, else 32), or two waves
-    # with the 16-row tile at k >= 7168; then the vector ALU for m <= 8 with
-    # m * n <= 24576; then an MFMA pick with the fit width has an m tile
-    # whose grid fits one wave with 64-row slabs, and no smaller tile does
-    # (4-stage W ring from k = 7168 for the 32-row tile, and for the 16-row
-    # tile up to 3 m tiles); otherwise no tile fits and the pick uses 64-row
-    # slabs.
+    # properties: the vector ALU for m <= 2 or m <= 4 with n <= 2048 (2 W
+    # rows per wave where 4 would leave few waves); then 16-row W slabs with
+    # an 8-way K split while that grid fits one wave of 256 workgroups (m
+    # tile 16, else 32), or two waves with the 16-row tile at k >= 7168; then
+    # the vector ALU for m <= 8 with m * n <= 24576; then a four-tile pick
+    # with the fit width has an m tile whose grid fits one wave with 64-row
+    # slabs, and no smaller tile does (variant by m tile and K); otherwise
+    # no tile fits and the pick uses 64-row slabs.
     decisions = 0
     for n in (1, 64, 896, 1536, 3072, 4096, 4112, 5120, 7168, 8192, 10240, 14336, 65536):
         for k in (32, 4096, 7168, 8192, 14336):
@@ -162,7 +161,7 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                 assert 0 <= c < n_cfg
                 nm = names[c]
                 slabs = -(-n // 16)
-                if m <= 2:
+                if m <= 2 or (m <= 4 and n <= 2048):
                     ks = None
                 elif slabs * -(-m // 16) <= 256:
                     ks = "mfma_m16_n16_ks8_r4"
@@ -172,7 +171,7 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                     ks = "mfma_m16_n16_ks8_r4"
                 else:
                     ks = None
-                valu = m <= 2 or (ks is None and m <= 8 and m * n <= 24576)
+                valu = m <= 2 or (m <= 4 and n <= 2048) or (ks is None and m <= 8 and m * n <= 24576)
                 assert nm.startswith("valu_gemv") == valu, (m, n, nm)
                 if valu:
                     w2 = n <= 2560 or (m <= 1 and n <= 4096)
@@ -183,10 +182,10 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                     continue
                 fits = [t for t in (16, 32, 64) if grid(m, n, t, 64) <= 256]
                 if fits:
-                    r4 = k >= 7168 and (fits[0] == 32 or (fits[0] == 16 and m <= 48))
-                    assert nm == f"mfma_m{fits[0]}_nfit" + ("_r4" if r4 else ""), (m, n, k, nm)
+                    sfx = {16: "_b2" if k >= 7168 else "_r2", 32: "_b2" if k >= 4096 else "", 64: "_t2"}[fits[0]]
+                    assert nm == f"mfma_m{fits[0]}_nfit" + sfx, (m, n, k, nm)
                 else:
-                    assert nm.endswith("_n64"), (m, n, nm)
+                    assert nm.endswith("_n64") or nm == "mfma_m64_n64_t2", (m, n, nm)
     assert decisions == 13 * 5 * 135
     assert so.bsgemm_w4a16_select(4, 64, 48) == -1 and so.bsgemm_w4a16_select(-1, 64, 64) == -1
 
@@ -201,7 +200,7 @@ def test_w4a16_forced_config_validation(so, monkeypatch):
     monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "no_such_tile")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert b"FORCE_CONFIG" in so.bsgemm_last_error()
-    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "23")
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "31")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     import torch
     if not torch.cuda.is_available():

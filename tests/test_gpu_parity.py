@@ -644,7 +644,7 @@ def _w4_case(m, n, k, seed):
     return x, qw
 
 
-@pytest.mark.parametrize("config", range(23))
+@pytest.mark.parametrize("config", range(31))
 def test_w4a16_every_config(gpu_lib, config):
     """Each configuration, forced, on shapes it would never be chosen for:
     ragged m, n and K tails (K % 256 != 0 uses per-lane scale loads), and a
