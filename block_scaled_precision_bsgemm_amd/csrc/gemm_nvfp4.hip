@@ -313,6 +313,7 @@ struct NDec {
   Scales2 a[4], b[4];
 };
 
+template <bool IL = true>
 __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
@@ -342,22 +343,29 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   }
   const int scale_off = (64 * wave + lane) * KB;
 
-  // Stage st (past-the-end stages load zeros from an out-of-range offset).
-  auto issue = [&](int st, auto WITH_SCALES) {
+  // Stage st (past-the-end stages load zeros from an out-of-range offset):
+  // code load u (A rows for u < 4, B rows for u >= 4) and the scale loads.
+  auto issue_code = [&](int st, int u) {
     const int slot = st % NR_NS;
-    const bool live = st < KT;
+    const int off = st < KT ? code_off[u & 3] + st * ROWB : OOB;
+    if (u < 4)
+      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
+    else
+      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + (u & 3))]), off);
+  };
+  auto issue_scales = [&](int st) {
+    const int sbuf = (st / 2) % NR_SBUF;
+    const int soff = st < KT ? scale_off + (st / 2) * 16 : OOB;
+    dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+    dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
+  };
+  auto issue = [&](int st, auto WITH_SCALES) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int off = live ? code_off[u] + st * ROWB : OOB;
-      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
-      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + u)]), off);
+      issue_code(st, u);
+      issue_code(st, 4 + u);
     }
-    if (decltype(WITH_SCALES)::value) {
-      const int sbuf = (st / 2) % NR_SBUF;
-      const int soff = live ? scale_off + (st / 2) * 16 : OOB;
-      dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
-      dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
-    }
+    if (decltype(WITH_SCALES)::value) issue_scales(st);
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -455,7 +463,9 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   // conversions under the first 8 MFMAs (with `first`), multiplies under the
   // last 8 (with `second`).  Scheduling regions end at the sched_barriers.
   auto sub = [&](const v8h* ca, const v8h* cb, const NHalf& x, const NDec& d, int sp, v8h* na, v8h* nb,
-                 auto first, auto second, auto NV1, auto NV2, auto NL2) {
+                 auto first, auto second, auto NV1, auto NV2, auto NL2, auto pre) {
+    pre();   // direct loads placed ahead of the sub-step's scheduling region
+    __builtin_amdgcn_sched_barrier(0);
     mfma_half(ca, cb, 0);
     convert(x, d, sp, na, nb);
     first();
@@ -475,24 +485,49 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     constexpr int PAR = decltype(PARC)::value;
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
-    // stage kt+2 carries a scale super-stage when it is even, i.e. PAR == 0
-    issue(kt + 2, std::integral_constant<bool, PAR == 0>{});
-    __builtin_amdgcn_sched_barrier(0);
-    sub(av[0], bv[0], x0, d0, 1, av[1], bv[1], none, [&] { read_half(kt, PARC, H1{}, x1); }, N4{}, N4{}, N2{});
+    // stage kt+2 carries a scale super-stage when it is even, i.e. PAR == 0.
+    // IL: its loads go out two per sub-step over the first four sub-steps
+    // (a burst of ten direct loads holds up the wave's MFMA issue while the
+    // memory queue drains: measured +2.7% at 16384^3, +4-5% at 4096 x 4096 x
+    // 16384, bit-identical output; one load per sub-step over all eight was
+    // 1% slower at 16384^3); otherwise all at the head of the step.
+    auto loads = [&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      return [&, q] {
+        if constexpr (IL) {
+          if (q == 0 && PAR == 0) issue_scales(kt + 2);
+          if (q < 4) {
+            issue_code(kt + 2, q);
+            issue_code(kt + 2, 4 + q);
+          }
+        } else if (q == 0) {
+          issue(kt + 2, std::integral_constant<bool, PAR == 0>{});
+        }
+      };
+    };
+    // all of stage kt+2's loads are issued before the mid-step wait
+    constexpr int EARLY = NR_CODE_LOADS + (PAR == 0 ? 2 : 0);
+    sub(av[0], bv[0], x0, d0, 1, av[1], bv[1], none, [&] { read_half(kt, PARC, H1{}, x1); }, N4{}, N4{}, N2{},
+        loads(std::integral_constant<int, 0>{}));
     sub(av[1], bv[1], x0, d0, 2, av[0], bv[0], [&] { decode_part(x1, d1, std::integral_constant<int, 0>{}); },
-        [&] { decode_part(x1, d1, std::integral_constant<int, 1>{}); }, N6{}, N6{}, N0{});
+        [&] { decode_part(x1, d1, std::integral_constant<int, 1>{}); }, N6{}, N6{}, N0{},
+        loads(std::integral_constant<int, 1>{}));
     sub(av[0], bv[0], x0, d0, 3, av[1], bv[1], [&] { decode_part(x1, d1, std::integral_constant<int, 2>{}); },
-        [&] { decode_part(x1, d1, std::integral_constant<int, 3>{}); }, N6{}, N6{}, N0{});
-    sub(av[1], bv[1], x1, d1, 0, av[0], bv[0], none, none, N4{}, N4{}, N0{});
+        [&] { decode_part(x1, d1, std::integral_constant<int, 3>{}); }, N6{}, N6{}, N0{},
+        loads(std::integral_constant<int, 2>{}));
+    sub(av[1], bv[1], x1, d1, 0, av[0], bv[0], none, none, N4{}, N4{}, N0{}, loads(std::integral_constant<int, 3>{}));
     // stage kt+1 landed (stage kt+2 stays in flight)
-    wait_vm_barrier<NR_CODE_LOADS + (PAR == 0 ? 2 : 0)>();
+    wait_vm_barrier<EARLY>();
     sub(av[0], bv[0], x1, d1, 1, av[1], bv[1], none,
-        [&] { read_half(kt + 1, std::integral_constant<int, PAR ^ 1>{}, H0{}, x0); }, N4{}, N4{}, N2{});
+        [&] { read_half(kt + 1, std::integral_constant<int, PAR ^ 1>{}, H0{}, x0); }, N4{}, N4{}, N2{},
+        loads(std::integral_constant<int, 4>{}));
     sub(av[1], bv[1], x1, d1, 2, av[0], bv[0], [&] { decode_part(x0, d0, std::integral_constant<int, 0>{}); },
-        [&] { decode_part(x0, d0, std::integral_constant<int, 1>{}); }, N6{}, N6{}, N0{});
+        [&] { decode_part(x0, d0, std::integral_constant<int, 1>{}); }, N6{}, N6{}, N0{},
+        loads(std::integral_constant<int, 5>{}));
     sub(av[0], bv[0], x1, d1, 3, av[1], bv[1], [&] { decode_part(x0, d0, std::integral_constant<int, 2>{}); },
-        [&] { decode_part(x0, d0, std::integral_constant<int, 3>{}); }, N6{}, N6{}, N0{});
-    sub(av[1], bv[1], x0, d0, 0, av[0], bv[0], none, none, N4{}, N4{}, N0{});
+        [&] { decode_part(x0, d0, std::integral_constant<int, 3>{}); }, N6{}, N6{}, N0{},
+        loads(std::integral_constant<int, 6>{}));
+    sub(av[1], bv[1], x0, d0, 0, av[0], bv[0], none, none, N4{}, N4{}, N0{}, loads(std::integral_constant<int, 7>{}));
   };
 
   // prologue: stages 0 (with the first scale super-stage) and 1
@@ -532,7 +567,7 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
   if (k % 256 == 0 && k > 0)
-    hipLaunchKernelGGL(nvfp4_gemm_ring_kernel, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+    hipLaunchKernelGGL(nvfp4_gemm_ring_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else if (k % 128 == 0)
     hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
