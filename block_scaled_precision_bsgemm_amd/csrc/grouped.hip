@@ -342,7 +342,7 @@ struct GRingSmem {
 // rows: workgroup (g, m tile, n tile) runs the K slice [koff[g], koff[g+1])
 // of the shared A and W and writes C[g].  Slices are multiples of 256, so
 // the 16-byte-scale ring serves every group; an empty slice writes zeros.
-template <int SB, bool F16, bool KRAG = false>
+template <int SB, bool F16, bool KRAG = false, bool IL = true>
 __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   using GM = GMath<F16>;
   using VT = typename GM::vec;
@@ -419,23 +419,32 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   const bool s_ok = s_src >= 0;
   const int s_off = s_src * KB;
 
-  auto issue = [&](int st, auto WITH_SCALES) {
+  // Part `part` of stage st's loads (IL spreads them over three sub-steps):
+  // 0: the scales (when the stage starts a super-stage), A and W loads 0-1;
+  // 1: W loads 2-4; 2: W loads 5-7.  part < 0: all of them.
+  auto issue_part = [&](int st, int part, bool with_scales) {
     const int slot = st % GR_NS;
     const bool live = st < KT;
+    if (part <= 0) {
+      if (with_scales) {
+        const int sbuf = (st / U) % GR_SBUF;
+        const int soff = (live && s_ok) ? s_off + (st / U) * SB : OOB;
+        if (SB == 16) dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
+        else dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+      }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
-      dma_x4(ra, lds_addr(&sm.a[slot][64 * (2 * wave + u)]), (live && a_ok[u]) ? a_off[u] + st * AROWB : OOB);
+      for (int u = 0; u < 2; ++u)
+        dma_x4(ra, lds_addr(&sm.a[slot][64 * (2 * wave + u)]), (live && a_ok[u]) ? a_off[u] + st * AROWB : OOB);
+    }
+    const int u0 = part < 0 ? 0 : part == 0 ? 0 : part == 1 ? 2 : 5;
+    const int u1 = part < 0 ? 8 : part == 0 ? 2 : part == 1 ? 5 : 8;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      dma_x4(rw, lds_addr(&sm.w[slot][64 * (8 * wave + u)]),
-             live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
-    if (decltype(WITH_SCALES)::value) {
-      const int sbuf = (st / U) % GR_SBUF;
-      const int soff = (live && s_ok) ? s_off + (st / U) * SB : OOB;
-      if (SB == 16) dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
-      else dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
-    }
+      if (u >= u0 && u < u1)
+        dma_x4(rw, lds_addr(&sm.w[slot][64 * (8 * wave + u)]),
+               live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
   };
+  auto issue = [&](int st, auto WITH_SCALES) { issue_part(st, -1, decltype(WITH_SCALES)::value); };
 
   // Wave w computes rows [64 w, 64 w + 64) x all 256 columns: 2 x 8 MFMA
   // tiles.  Each A row is then dequantised by exactly one wave (the BF16
@@ -513,16 +522,27 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
     constexpr int IN = decltype(INC)::value;
     constexpr int CUR = IN & 1;
     constexpr int AFTER = loads_of((IN + 2) % U);   // stage kt+2 stays in flight
-    issue(kt + 2, std::integral_constant<bool, ((IN + 2) % U) == 0>{});
+    constexpr bool WS = ((IN + 2) % U) == 0;
+    // IL: stage kt+2's loads over the first three sub-steps (one burst at
+    // the head of the step holds up the wave's MFMA issue)
+    issue_part(kt + 2, IL ? 0 : -1, WS);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(av[0], bv[0]);
     read_w(kt, 1, bv[1]);
     dequant(fa[CUR], 1, av[1]);
     interleave();
+    if constexpr (IL) {
+      issue_part(kt + 2, 1, WS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mfmas(av[1], bv[1]);
     read_w(kt, 2, bv[0]);
     dequant(fa[CUR], 2, av[0]);
     interleave();
+    if constexpr (IL) {
+      issue_part(kt + 2, 2, WS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     mfmas(av[0], bv[0]);
     read_w(kt, 3, bv[1]);
     dequant(fa[CUR], 3, av[1]);
@@ -548,16 +568,24 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
       step(kt, std::integral_constant<int, 0>{});
       // second step of the pair: same code with the buffers swapped
       constexpr int IN = 1;
-      issue(kt + 3, std::true_type{});
+      issue_part(kt + 3, IL ? 0 : -1, true);
       __builtin_amdgcn_sched_barrier(0);
       mfmas(av[0], bv[0]);
       read_w(kt + 1, 1, bv[1]);
       dequant(fa[1], 1, av[1]);
       interleave();
+      if constexpr (IL) {
+        issue_part(kt + 3, 1, true);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       mfmas(av[1], bv[1]);
       read_w(kt + 1, 2, bv[0]);
       dequant(fa[1], 2, av[0]);
       interleave();
+      if constexpr (IL) {
+        issue_part(kt + 3, 2, true);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       mfmas(av[0], bv[0]);
       read_w(kt + 1, 3, bv[1]);
       dequant(fa[1], 3, av[1]);
