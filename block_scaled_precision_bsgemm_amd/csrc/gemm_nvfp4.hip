@@ -268,16 +268,16 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
 
 // ---------------------------------------------------------------------------
 // Ring kernel (K % 256 == 0).  The operands stream HBM -> LDS by direct loads
-// through a 3-stage ring of 128-element K steps; two steps are in flight
-// while one is computed (a step is ~4096 MFMA cycles, so this covers the
-// memory latency).
+// through a 4-stage ring of 128-element K steps; three steps are in flight
+// while one is computed (a step is ~4096 MFMA cycles; the fourth stage
+// measured +3% over three at 16384^3, bit-identical, and fills 152 KiB of LDS).
 //
 // Per stage and operand, codes are [256][64] bytes, 16-byte chunk c of row r
 // at c ^ ((r >> 2) & 3).  Each wave issues 8 code loads per stage (1 KiB =
 // 16 rows each).  Scales come in batches of 16 bytes per row (two stages of
 // eight 16-element blocks): one load per operand per wave every two stages,
 // with one lane per row.  There are 3 super-stage buffers, so a buffer is
-// rewritten only two barriers after its last read.
+// rewritten only after the barrier that follows its last read.
 //
 // A step is 8 sub-steps of 16 MFMAs (K16 each); sub-step t uses half t/4 of
 // the step's K range and dword t%4 of the lane's code chunk.  Software
@@ -292,12 +292,13 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
 //     the barrier; the next stage's half-0 data is read during sub-step 4,
 //     decoded over sub-steps 5 and 6, and prepared for its sub-step 0 during
 //     sub-step 7.
-constexpr int NR_NS = 3, NR_ROW = ROWB / 16, NR_SBUF = 3;
+constexpr int NR_NS = 4, NR_ROW = ROWB / 16, NR_SBUF = 3;
 constexpr int NR_CODE_LOADS = 8;
 
+template <int NS>
 struct NRingSmem {
-  uint4 a[NR_NS][BM * NR_ROW];
-  uint4 b[NR_NS][BN * NR_ROW];
+  uint4 a[NS][BM * NR_ROW];
+  uint4 b[NS][BN * NR_ROW];
   uint4 as[NR_SBUF][BM];          // 16 scale bytes per row: stage 2q then 2q+1
   uint4 bs[NR_SBUF][BN];
 };
@@ -313,12 +314,12 @@ struct NDec {
   Scales2 a[4], b[4];
 };
 
-template <bool IL = true>
+template <bool IL = true, int NS = NR_NS>
 __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
     uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ NRingSmem sm;
+  __shared__ NRingSmem<NS> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tm, tn;
   if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   // Stage st (past-the-end stages load zeros from an out-of-range offset):
   // code load u (A rows for u < 4, B rows for u >= 4) and the scale loads.
   auto issue_code = [&](int st, int u) {
-    const int slot = st % NR_NS;
+    const int slot = st % NS;
     const int off = st < KT ? code_off[u & 3] + st * ROWB : OOB;
     if (u < 4)
       dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   // 16-byte super-stage entry (static).
   auto read_half = [&](int st, auto PARC, auto HC, NHalf& x) {
     constexpr int par = decltype(PARC)::value, h = decltype(HC)::value;
-    const int slot = st % NR_NS, sbuf = (st / 2) % NR_SBUF;
+    const int slot = st % NS, sbuf = (st / 2) % NR_SBUF;
     // lane g's two scale bytes: the 16-bit half g of the half step's dword
     const uint16_t* sa16 = reinterpret_cast<const uint16_t*>(&sm.as[sbuf][0]);
     const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(&sm.bs[sbuf][0]);
@@ -491,22 +492,25 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     // memory queue drains: measured +2.7% at 16384^3, +4-5% at 4096 x 4096 x
     // 16384, bit-identical output; one load per sub-step over all eight was
     // 1% slower at 16384^3); otherwise all at the head of the step.
+    constexpr bool NEW_SC = ((PAR + NS - 1) & 1) == 0;   // stage kt+NS-1 is even
     auto loads = [&](auto Q) {
       constexpr int q = decltype(Q)::value;
       return [&, q] {
         if constexpr (IL) {
-          if (q == 0 && PAR == 0) issue_scales(kt + 2);
+          if (q == 0 && NEW_SC) issue_scales(kt + NS - 1);
           if (q < 4) {
-            issue_code(kt + 2, q);
-            issue_code(kt + 2, 4 + q);
+            issue_code(kt + NS - 1, q);
+            issue_code(kt + NS - 1, 4 + q);
           }
         } else if (q == 0) {
-          issue(kt + 2, std::integral_constant<bool, PAR == 0>{});
+          issue(kt + NS - 1, std::integral_constant<bool, NEW_SC>{});
         }
       };
     };
-    // all of stage kt+2's loads are issued before the mid-step wait
-    constexpr int EARLY = NR_CODE_LOADS + (PAR == 0 ? 2 : 0);
+    // stages kt+2 .. kt+NS-1 stay in flight at the mid-step wait (all of
+    // stage kt+NS-1's loads are issued before it); an even stage brings the
+    // scales of its super-stage
+    constexpr int EARLY = NR_CODE_LOADS * (NS - 2) + 2 * ((NS - 2 + (PAR == 0 ? 1 : 0)) / 2);
     sub(av[0], bv[0], x0, d0, 1, av[1], bv[1], none, [&] { read_half(kt, PARC, H1{}, x1); }, N4{}, N4{}, N2{},
         loads(std::integral_constant<int, 0>{}));
     sub(av[1], bv[1], x0, d0, 2, av[0], bv[0], [&] { decode_part(x1, d1, std::integral_constant<int, 0>{}); },
@@ -531,9 +535,13 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   };
 
   // prologue: stages 0 (with the first scale super-stage) and 1
-  issue(0, std::true_type{});
-  issue(1, std::false_type{});
-  wait_vm_barrier<NR_CODE_LOADS>();
+  // prologue: stages 0 .. NS-2 (even ones with their scale super-stage);
+  // wait for stage 0
+  static_for<0, NS - 1>([&](auto SC) {
+    constexpr int st = decltype(SC)::value;
+    issue(st, std::integral_constant<bool, (st & 1) == 0>{});
+  });
+  wait_vm_barrier<NR_CODE_LOADS * (NS - 2) + 2 * ((NS - 2) / 2)>();
   read_half(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, x0);
   decode(x0, d0);
   dequant(x0, d0, 0, av[0], bv[0]);
@@ -567,7 +575,7 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
   if (k % 256 == 0 && k > 0)
-    hipLaunchKernelGGL(nvfp4_gemm_ring_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+    hipLaunchKernelGGL((nvfp4_gemm_ring_kernel<true, NR_NS>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else if (k % 128 == 0)
     hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
