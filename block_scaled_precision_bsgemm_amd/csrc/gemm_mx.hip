@@ -282,7 +282,7 @@ template <> struct Frags<true> {
   int sa[4], sb[4];
 };
 
-template <int SB, bool FP4, bool IL = true>
+template <int SB, bool FP4, int IL = 2>
 __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
@@ -454,13 +454,27 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
     constexpr int IN = decltype(INC)::value;
     constexpr int CUR = decltype(CURC)::value;
     constexpr int ISSUE_MOD = (IN + RB_NS - 1) % U;   // stage kt+3 within its super-stage
-    constexpr int AFTER = loads_of((IN + 2) % U) + loads_of((IN + 3) % U);
+    // Direct loads of stage kt+3 (a burst of 8 at the head of the step, IL
+    // == 0, fills the wave's memory queue and holds up its MFMA issue):
+    //   IL == 1: interleaved with the first half's MFMAs (+11% at 16384^3
+    //            for MXFP8 and MXFP4 over IL == 0);
+    //   IL == 2: the A half interleaved with the first half's MFMAs, the B
+    //            half right after the mid-step barrier, so the wait leaves
+    //            fewer loads outstanding (+1.3% MXFP8, +3.4% MXFP4 at 16384^3
+    //            over IL == 1).  All three give bit-identical output.
+    constexpr int LATE = IL == 2 ? 4 : 0;
+    constexpr int AFTER = loads_of((IN + 2) % U) + loads_of((IN + 3) % U) - LATE;
     constexpr auto SEL = std::integral_constant<int, 2 * (IN % 2)>{};
-    if constexpr (IL) {
-      // the step's 8 code loads interleaved with the first half's MFMAs
-      // (a burst of 8 direct loads fills the wave's memory queue and holds
-      // up its MFMA issue: measured +11% at 16384^3 for MXFP8 and MXFP4,
-      // bit-identical output); the scale loads first
+    if constexpr (IL == 2) {
+      if constexpr (ISSUE_MOD == 0) issue_scales(kt + RB_NS - 1);
+      static_for<0, 8 * per_byte<FP4>()>([&](auto IX) {
+        constexpr int ix = decltype(IX)::value, t = ix % 8;
+        if (ix % (2 * per_byte<FP4>()) == 0) issue_code(kt + RB_NS - 1, ix / (2 * per_byte<FP4>()));
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_one(f[CUR], t >> 2, t & 3, SEL, std::integral_constant<int, ix / 8>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else if constexpr (IL == 1) {
       if constexpr (ISSUE_MOD == 0) issue_scales(kt + RB_NS - 1);
       // FP4: the 8 tiles' first K64 halves, then their second halves (two
       // MFMAs into one accumulator stay 7 issues apart)
@@ -479,6 +493,11 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
       mfma_rows(f[CUR], 0, SEL);
     }
     wait_vm_barrier<AFTER>();        // stage kt+1 landed; kt+2, kt+3 in flight
+    if constexpr (IL == 2) {
+#pragma unroll
+      for (int u = 4; u < 8; ++u) issue_code(kt + RB_NS - 1, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, f[CUR ^ 1]);
     mfma_rows(f[CUR], 2, SEL);
     // 8 MFMAs (FP8) or 16 (FP4) interleaved with the 24 LDS reads
