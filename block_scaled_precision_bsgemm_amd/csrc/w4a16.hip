@@ -28,7 +28,8 @@ typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
 // Wave = R weight rows.  In each 4096-element chunk of K, lane l owns K
 // [32 l, 32 l + 32) and [2048 + 32 l, 2048 + 32 l + 32): one 16-byte code
 // load per row and half, so every load instruction reads 1 KB of one row.
-// All loads of a chunk are issued before any arithmetic.  Each 16-element
+// The chunk of X is loaded once per workgroup and shared through LDS.  All
+// loads of a chunk are issued before any arithmetic.  Each 16-element
 // block's dot product is taken on the unscaled E2M1 values (exact in BF16,
 // via fdot2); the block's full E4M3 scale is applied once, in FP32.
 
@@ -98,29 +99,37 @@ template <int R>
 __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
     const float* __restrict__ Wts, uint16_t* __restrict__ C, int N, int K) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave and rows are wave-uniform; readfirstlane tells the compiler so,
+  // otherwise it builds the W buffer resources in vector registers and wraps
+  // every W load in a waterfall loop
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // row blockIdx.y of X and C (the vector-ALU path forced on m > 1 re-reads
   // W once per row)
   X += (int64_t)blockIdx.y * K;
   C += (int64_t)blockIdx.y * N;
   const int n0 = (blockIdx.x * GV_WAVES + wave) * R;
   const int KH = K / 2, KB = K / 16;
-  const int rows = max(0, min(N - n0, R));
+  const int rows = __builtin_amdgcn_readfirstlane(max(0, min(N - n0, R)));
   const auto c_rsrc = make_rsrc(Wc + (int64_t)n0 * KH, rows * KH);
   const auto s_rsrc = make_rsrc(Ws + (int64_t)n0 * KB, rows * KB);
   const auto x_rsrc = make_rsrc(X, K * 2);
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  __shared__ uint4 xs[512];   // one 4096-element chunk of X
   for (int kc = 0; kc < K; kc += 4096) {
     // K % 32 == 0, so each lane's 32-element group is wholly in or out of K
     const int g0 = kc + 32 * lane, g1 = kc + 2048 + 32 * lane;
     const bool in0 = g0 < K, in1 = g1 < K;
-    uint4 x0[4], x1[4];
+    // The workgroup loads the chunk of X once (16 bytes per thread and half)
+    // and shares it through LDS: loaded by every wave, X took as many
+    // L2-to-CU bytes as the W stream itself.  It goes out ahead of the W
+    // loads, so waiting for it leaves W in flight.
+    uint4 xl[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      x0[q] = buffer_load_x4(x_rsrc, in0 ? (g0 + 8 * q) * 2 : OOB);
-      x1[q] = buffer_load_x4(x_rsrc, in1 ? (g1 + 8 * q) * 2 : OOB);
+    for (int h = 0; h < 2; ++h) {
+      const int e = kc + 8 * (threadIdx.x + 256 * h);
+      xl[h] = buffer_load_x4(x_rsrc, e < K ? e * 2 : OOB);
     }
     uint4 c0[R], c1[R];
     uint32_t s0[R], s1[R];
@@ -133,6 +142,16 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
     for (int r = 0; r < R; ++r) {
       c1[r] = buffer_load_x4(c_rsrc, in1 ? r * KH + g1 / 2 : OOB);
       s1[r] = buffer_load_u16(s_rsrc, in1 ? r * KB + g1 / 16 : OOB);
+    }
+    if (kc > 0) __syncthreads();   // the previous chunk's reads are done
+    xs[threadIdx.x] = xl[0];
+    xs[threadIdx.x + 256] = xl[1];
+    __syncthreads();
+    uint4 x0[4], x1[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x0[q] = xs[4 * lane + q];        // K g0 .. g0 + 31
+      x1[q] = xs[256 + 4 * lane + q];  // K g1 .. g1 + 31
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -235,7 +254,11 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int n0 = (lin / m_tiles) * nb, m0 = (lin % m_tiles) * MT;
   const int KH = K / 2, KB = K / 16;
-  const int rows_w = max(0, min(nb, N - n0)), rows_x = max(0, min(MT, M - m0));
+  // wave-uniform (readfirstlane): a min/max evaluated in vector registers
+  // would put the W and X buffer resources there and wrap every load in a
+  // waterfall loop
+  const int rows_w = __builtin_amdgcn_readfirstlane(max(0, min(nb, N - n0)));
+  const int rows_x = __builtin_amdgcn_readfirstlane(max(0, min(MT, M - m0)));
   const int S = (K + 128 * SB - 1) / (128 * SB);
 
   if (wave >= SK_CONS) {
