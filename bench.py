@@ -25,6 +25,8 @@ The same JSON line carries:
     GEMM latency.
 
 ``--only w4a16`` runs just the W4A16 rows (for profiler runs).
+``--only mx`` runs just the MX GEMM rows and a 1 GiB device copy (for profiler
+runs: kernel traces and HBM byte counters of the MX GEMMs).
 ``--only big`` times the 64k^3 and 128k^3 NVFP4 GEMMs (about 60 GB of device
 memory, operands drawn as NVFP4 on the device; 16k^3 on the same kind of
 operands as the control) and prints their rows.
@@ -95,7 +97,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "headline", "big", "w4a16"], default="all")
+    ap.add_argument("--only", choices=["all", "headline", "big", "w4a16", "mx"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +118,18 @@ def main():
 
     if args.only == "w4a16":
         print(json.dumps(w4a16_rows(L, synth, dev)))
+        return
+
+    if args.only == "mx":
+        out = mx_rows(L, synth, dev, args.steps)
+        # HBM counter calibration: a plain 1 GiB device-to-device copy.
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_bytes"] = 1 << 30
+        print(json.dumps(out))
         return
 
     if args.only == "big":
@@ -200,43 +214,8 @@ def main():
     ms = time_events(lambda i: L.bsgemm_quantize_nvfp4(da, ca, sa, ta), 5, 2)
     rows["quantize_nvfp4_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (8 + 0.5625) / (ms * 1e-3) / 1e9, 1),
                                           "bytes_model": "2 reads of FP32 + codes + scales"}
-    del ca, sa, ta, cb, sb, tb, c
-    mx_a = synth.normal_f32((M, K), synth.SEEDS["mxfp8_4k.A"])
-    mx_b = synth.normal_f32((N, K), synth.SEEDS["mxfp8_4k.B"])
-    dma, dmb = torch.from_numpy(mx_a).to(dev), torch.from_numpy(mx_b).to(dev)
-    del mx_a, mx_b, da, db
-    c8a, s8a = L.bsgemm_quantize_mxfp8(dma)
-    c8b, s8b = L.bsgemm_quantize_mxfp8(dmb)
-    ms = time_events(lambda i: L.bsgemm_quantize_mxfp8(dma, c8a, s8a), 5, 2)
-    rows["quantize_mxfp8_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (4 + 1.03125) / (ms * 1e-3) / 1e9, 1)}
-    # MXFP4 from the same N(0, 1) 16k inputs
-    c4a, s4a = L.bsgemm_quantize_mxfp4(dma)
-    c4b, s4b = L.bsgemm_quantize_mxfp4(dmb)
-    ms = time_events(lambda i: L.bsgemm_quantize_mxfp4(dma, c4a, s4a), 5, 2)
-    rows["quantize_mxfp4_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (4 + 0.53125) / (ms * 1e-3) / 1e9, 1)}
-    del dma, dmb
-    c16 = torch.empty((M, N), dtype=torch.int16, device=dev)
-    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP4, c4a, s4a, None, c4b, s4b, None, K, c=c16),
-                     max(3, args.steps // 2), 2)
-    tf = flops / (ms * 1e-3) / 1e12
-    rows["mxfp4_gemm_16384"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp4_peak": round(tf / PEAK["fp4"], 4)}
-    del c4a, s4a, c4b, s4b, c16
-
-    # --------------------------------------------------- MXFP8 16k^3 and 4k^3
-    c16 = torch.empty((M, N), dtype=torch.int16, device=dev)
-    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP8, c8a, s8a, None, c8b, s8b, None, K, c=c16),
-                     max(3, args.steps // 2), 2)
-    tf = flops / (ms * 1e-3) / 1e12
-    rows["mxfp8_gemm_16384"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
-    del c8a, s8a, c8b, s8b, c16
-    a4, b4 = synth.mxfp8_inputs()
-    q4a = L.bsgemm_quantize_mxfp8(torch.from_numpy(a4).to(dev))
-    q4b = L.bsgemm_quantize_mxfp8(torch.from_numpy(b4).to(dev))
-    c4 = torch.empty((4096, 4096), dtype=torch.int16, device=dev)
-    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP8, q4a[0], q4a[1], None, q4b[0], q4b[1], None, 4096, c=c4), 50, 10)
-    tf = 2.0 * 4096 ** 3 / (ms * 1e-3) / 1e12
-    rows["mxfp8_gemm_4096"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
-    del q4a, q4b, c4
+    del ca, sa, ta, cb, sb, tb, c, da, db
+    rows.update(mx_rows(L, synth, dev, args.steps, time_quantizers=True))
 
     # --------------------------------------------------- NVFP4 256x256x128
     sa0, sb0 = synth.nvfp4_small_inputs()
@@ -313,6 +292,51 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "rows": rows,
     }
     print(json.dumps(out))
+
+
+def mx_rows(L, synth, dev, steps, time_quantizers=False):
+    """MXFP4 and MXFP8 GEMMs at 16384^3 on N(0, 1) inputs, MXFP8 at 4096^3
+    (and, with time_quantizers, the MXFP8 and MXFP4 quantizers at 16384^2)."""
+    import torch
+    rows = {}
+    M = N = K = 16384
+    n_el, flops = M * K, 2.0 * M * N * K
+    mx_a = synth.normal_f32((M, K), synth.SEEDS["mxfp8_4k.A"])
+    mx_b = synth.normal_f32((N, K), synth.SEEDS["mxfp8_4k.B"])
+    dma, dmb = torch.from_numpy(mx_a).to(dev), torch.from_numpy(mx_b).to(dev)
+    del mx_a, mx_b
+    c8a, s8a = L.bsgemm_quantize_mxfp8(dma)
+    c8b, s8b = L.bsgemm_quantize_mxfp8(dmb)
+    if time_quantizers:
+        ms = time_events(lambda i: L.bsgemm_quantize_mxfp8(dma, c8a, s8a), 5, 2)
+        rows["quantize_mxfp8_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (4 + 1.03125) / (ms * 1e-3) / 1e9, 1)}
+    # MXFP4 from the same N(0, 1) 16k inputs
+    c4a, s4a = L.bsgemm_quantize_mxfp4(dma)
+    c4b, s4b = L.bsgemm_quantize_mxfp4(dmb)
+    if time_quantizers:
+        ms = time_events(lambda i: L.bsgemm_quantize_mxfp4(dma, c4a, s4a), 5, 2)
+        rows["quantize_mxfp4_16384x16384"] = {"ms": round(ms, 4), "gbps": round(n_el * (4 + 0.53125) / (ms * 1e-3) / 1e9, 1)}
+    del dma, dmb
+    c16 = torch.empty((M, N), dtype=torch.int16, device=dev)
+    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP4, c4a, s4a, None, c4b, s4b, None, K, c=c16),
+                     max(3, steps // 2), 2)
+    tf = flops / (ms * 1e-3) / 1e12
+    rows["mxfp4_gemm_16384"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp4_peak": round(tf / PEAK["fp4"], 4)}
+    del c4a, s4a, c4b, s4b
+
+    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP8, c8a, s8a, None, c8b, s8b, None, K, c=c16),
+                     max(3, steps // 2), 2)
+    tf = flops / (ms * 1e-3) / 1e12
+    rows["mxfp8_gemm_16384"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+    del c8a, s8a, c8b, s8b, c16
+    a4, b4 = synth.mxfp8_inputs()
+    q4a = L.bsgemm_quantize_mxfp8(torch.from_numpy(a4).to(dev))
+    q4b = L.bsgemm_quantize_mxfp8(torch.from_numpy(b4).to(dev))
+    c4 = torch.empty((4096, 4096), dtype=torch.int16, device=dev)
+    ms = time_events(lambda i: L.bsgemm_run(L.BSGEMM_MXFP8, q4a[0], q4a[1], None, q4b[0], q4b[1], None, 4096, c=c4), 50, 10)
+    tf = 2.0 * 4096 ** 3 / (ms * 1e-3) / 1e12
+    rows["mxfp8_gemm_4096"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_fp8_peak": round(tf / PEAK["fp8"], 4)}
+    return rows
 
 
 def time_graph(fn, launches, replays):
