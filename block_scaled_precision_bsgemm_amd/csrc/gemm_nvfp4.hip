@@ -567,6 +567,82 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Small-problem kernel: 64 x 64 output tiles, one 32 x 32 FP16 MFMA tile per
+// wave, operands straight from global memory (L2) into registers.  It serves
+// grids that would leave most CUs idle with 256 x 256 tiles: the
+// 256 x 256 x 128 GEMM is one such tile, and one workgroup would then run
+// every load, MFMA and store of the problem in series (14 us).
+//
+// K runs in chunks of 128 elements.  In a chunk, lane (r = l % 32,
+// g = l / 32) supplies A row r (and B row r) at K [64 g, 64 g + 64): 32
+// contiguous code bytes and the 4 scale bytes of their blocks.  MFMA t
+// (0..7) takes K positions 64 g + 8 t .. + 7 from each lane half, so A and B
+// pair the same K positions in every product and each position is used once.
+// Codes are dequantised exactly to FP16 as in the other kernels.
+constexpr int SMALL_T = 64;
+// Grids of fewer 256 x 256 tiles than this run the small kernel (measured:
+// 2.4-2.9x faster up to 25 tiles, equal at 32, 8% slower at 36).
+constexpr int NV_SMALL_TILES = 32;
+
+__global__ __launch_bounds__(256) void nvfp4_small_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
+    uint16_t* __restrict__ C, int M, int N, int K, int tiles_n) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int m0 = tm * SMALL_T + 32 * (wave & 1), n0 = tn * SMALL_T + 32 * (wave >> 1);
+  const int KH = K / 2, KB = K / 16;
+  // wave-uniform (readfirstlane), so the buffer resources stay scalar
+  const int rows_a = __builtin_amdgcn_readfirstlane(max(0, min(32, M - m0)));
+  const int rows_b = __builtin_amdgcn_readfirstlane(max(0, min(32, N - n0)));
+  const auto ca = make_rsrc(A + (int64_t)max(0, min(m0, M)) * KH, rows_a * KH);
+  const auto cb = make_rsrc(B + (int64_t)max(0, min(n0, N)) * KH, rows_b * KH);
+  const auto sa = make_rsrc(As + (int64_t)max(0, min(m0, M)) * KB, rows_a * KB);
+  const auto sb = make_rsrc(Bs + (int64_t)max(0, min(n0, N)) * KB, rows_b * KB);
+  const int r = lane & 31, g = lane >> 5;
+  v16f acc = v16f{};
+  for (int kc = 0; kc < K; kc += 128) {
+    // K % 32 == 0: each 32-element half of the lane's range is wholly in or out of K
+    const int k0 = kc + 64 * g;
+    const bool in0 = k0 < K, in1 = k0 + 32 < K;
+    const uint4 a0 = buffer_load_x4(ca, in0 ? r * KH + k0 / 2 : OOB);
+    const uint4 a1 = buffer_load_x4(ca, in1 ? r * KH + k0 / 2 + 16 : OOB);
+    const uint4 b0 = buffer_load_x4(cb, in0 ? r * KH + k0 / 2 : OOB);
+    const uint4 b1 = buffer_load_x4(cb, in1 ? r * KH + k0 / 2 + 16 : OOB);
+    // the scale row pitch K / 16 is only 2-byte aligned: 16-bit loads
+    const uint32_t sa0 = buffer_load_u16(sa, in0 ? r * KB + k0 / 16 : OOB);
+    const uint32_t sa1 = buffer_load_u16(sa, in1 ? r * KB + k0 / 16 + 2 : OOB);
+    const uint32_t sb0 = buffer_load_u16(sb, in0 ? r * KB + k0 / 16 : OOB);
+    const uint32_t sb1 = buffer_load_u16(sb, in1 ? r * KB + k0 / 16 + 2 : OOB);
+    float xs[4], ys[4];
+    uint32_t xm[4], ym[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t wa = b < 2 ? sa0 : sa1, wb = b < 2 ? sb0 : sb1;
+      xs[b] = e4m3_scale_value((wa >> (8 * (b & 1))) & 0xFFu);
+      ys[b] = e4m3_scale_value((wb >> (8 * (b & 1))) & 0xFFu);
+      xm[b] = scale_mantissa_f16x2(xs[b]);
+      ym[b] = scale_mantissa_f16x2(ys[b]);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t da = t < 4 ? dword_of(a0, t) : dword_of(a1, t - 4);
+      const uint32_t db = t < 4 ? dword_of(b0, t) : dword_of(b1, t - 4);
+      const v8h av = dequant8_f16(da, xs[t / 2], xm[t / 2]);
+      const v8h bv = dequant8_f16(db, ys[t / 2], ym[t / 2]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
+    }
+  }
+  const float alpha = __fmul_rn(*Ats, *Bts);
+  const int col = n0 + r;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int row = m0 + (v >> 2) * 8 + g * 4 + (v & 3);
+    if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[v] * alpha);
+  }
+}
 }  // namespace
 
 hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
@@ -574,7 +650,11 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* bs, const float* bts, uint16_t* c,
                              hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
-  if (k % 256 == 0 && k > 0)
+  if (tiles_m * tiles_n < NV_SMALL_TILES) {
+    const int sm = (int)ceil_div(m, SMALL_T), sn = (int)ceil_div(n, SMALL_T);
+    hipLaunchKernelGGL(nvfp4_small_kernel, dim3(sm * sn), dim3(256), 0, stream, a, as, ats, b, bs, bts, c, (int)m,
+                       (int)n, (int)k, sn);
+  } else if (k % 256 == 0 && k > 0)
     hipLaunchKernelGGL((nvfp4_gemm_ring_kernel<true, NR_NS>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else if (k % 128 == 0)

@@ -235,6 +235,21 @@ def test_gemm_shapes(gpu_lib, fmt, m, n, k):
     assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("m,n,k", [(1536, 1400, 512), (1536, 1400, 640), (1300, 1600, 544), (1300, 1600, 2048)])
+def test_gemm_nvfp4_large_grid_paths(gpu_lib, m, n, k):
+    """Grids of at least 32 tiles of 256 x 256 (below that the small-problem
+    kernel runs): the ring kernel (K % 256 == 0) and the register-staged
+    kernel with K % 128 == 0 and K % 128 != 0, with ragged edges in M and N."""
+    r = np.random.Generator(np.random.PCG64(m * 7919 + n * 31 + k))
+    xa = r.standard_normal((m, k)).astype(np.float32)
+    xb = r.standard_normal((n, k)).astype(np.float32)
+    xa[:: 97] *= np.float32(50.0)                      # mixed block scales
+    qa, qb = _quant(L.BSGEMM_NVFP4, xa), _quant(L.BSGEMM_NVFP4, xb)
+    say("gemm nvfp4 large grid", m, n, k)
+    c = _gpu_gemm(L.BSGEMM_NVFP4, qa, qb, k)
+    assert_ok(G.check(c, *_ref(L.BSGEMM_NVFP4, qa, qb)), f"nvfp4 {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 def test_gemm_zero_rows_and_k0(gpu_lib, fmt):
     f = FMTS[fmt]
@@ -675,13 +690,14 @@ def test_w4a16_environment_override(gpu_lib, monkeypatch):
 
 # ------------------------------------------------- all codes, all scales --
 
-@pytest.mark.parametrize("k", [128, 256, 512, 1024, 2048 + 256])
-def test_gemm_nvfp4_every_scale_code(gpu_lib, k):
+@pytest.mark.parametrize("m,n,k", [(300, 260, 128), (300, 260, 256), (300, 260, 512), (300, 260, 1024),
+                                   (300, 260, 2048 + 256), (1600, 1400, 256 + 128), (1600, 1400, 1024)])
+def test_gemm_nvfp4_every_scale_code(gpu_lib, m, n, k):
     """Random E2M1 codes with E4M3 scale codes drawn uniformly from all 127
-    finite non-negative codes (zero and subnormals included), on the ring
-    (K % 256 == 0) and register-staged paths."""
-    r = np.random.Generator(np.random.PCG64(k))
-    m, n = 300, 260
+    finite non-negative codes (zero and subnormals included): 300 x 260 runs
+    the small-problem kernel; 1600 x 1400 (42 tiles of 256 x 256) the
+    register-staged (K % 256 != 0) and ring (K % 256 == 0) kernels."""
+    r = np.random.Generator(np.random.PCG64(k + m))
     qa = (r.integers(0, 256, (m, k // 2)).astype(np.uint8),
           r.integers(0, 0x7F, (m, k // 16)).astype(np.uint8), np.float32(0.75))
     qb = (r.integers(0, 256, (n, k // 2)).astype(np.uint8),
