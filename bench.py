@@ -27,6 +27,8 @@ The same JSON line carries:
 ``--only w4a16`` runs just the W4A16 rows (for profiler runs).
 ``--only mx`` runs just the MX GEMM rows and a 1 GiB device copy (for profiler
 runs: kernel traces and HBM byte counters of the MX GEMMs).
+``--only grouped`` runs just the grouped rows and the same 1 GiB device copy (for
+profiler runs).
 ``--only big`` times the 64k^3 and 128k^3 NVFP4 GEMMs (about 60 GB of device
 memory, operands drawn as NVFP4 on the device; 16k^3 on the same kind of
 operands as the control) and prints their rows.
@@ -92,12 +94,74 @@ def time_events(fn, steps, warmup):
     return s.elapsed_time(e) / steps
 
 
+def grouped_rows(L, synth, dev):
+    """The grouped rows: the 32-group NVFP4 x BF16 problem, the same problem with FP16 weights
+    and every routing and epilogue variant, and its K-ragged weight-gradient form."""
+    import numpy as np
+    import torch
+
+    rows = {}
+    # ------------------------------------------------------------- grouped
+    log("generating grouped inputs")
+    gx, off, gw = synth.grouped_inputs()
+    qg = L.bsgemm_quantize_nvfp4(torch.from_numpy(gx).to(dev))
+    dw = torch.from_numpy(gw.view(np.int16)).to(dev)
+    doff = torch.from_numpy(off).to(dev)
+    del gx, gw
+    cg = torch.empty((16384, 2048), dtype=torch.int16, device=dev)
+    ms = time_events(lambda i: L.bsgemm_grouped_run(*qg, doff, dw, 7168, c=cg), 10, 3)
+    gflops = 2.0 * 16384 * 2048 * 7168
+    counts = np.diff(off.astype(np.int64))
+    gbytes = 16384 * 7168 * 0.5625 + int((counts > 0).sum()) * 2048 * 7168 * 2 + 16384 * 2048 * 2
+    tf = gflops / (ms * 1e-3) / 1e12
+    rows["grouped_nvfp4_bf16"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
+                                  "gbps_algorithmic": round(gbytes / (ms * 1e-3) / 1e9, 1),
+                                  "groups_nonempty": int((counts > 0).sum()), "max_group_rows": int(counts.max())}
+    # the same problem through the variant entry point: FP16 weights (the BF16
+    # weights converted to FP16 on the device), gather over all rows, a
+    # scatter permutation, bias and gamma
+    rng = np.random.Generator(np.random.PCG64(4200))
+    dw16 = dw.view(torch.bfloat16).to(torch.float16).view(torch.int16)
+    vg = torch.from_numpy(rng.integers(0, 16384, 16384).astype(np.int32)).to(dev)
+    vs = torch.from_numpy(rng.permutation(16384).astype(np.int32)).to(dev)
+    vb = torch.from_numpy((rng.standard_normal((32, 2048)) * 0.1).astype(np.float32)).to(dev)
+    vgm = torch.from_numpy(rng.uniform(-2, 2, 16384).astype(np.float32)).to(dev)
+    ms = time_events(lambda i: L.bsgemm_grouped_run_ex(*qg, doff, dw16, 7168, w_dtype=L.BSGEMM_W_F16, bias=vb,
+                                                       gamma=vgm, gather_idx=vg, scatter_idx=vs, c=cg), 10, 3)
+    tf = gflops / (ms * 1e-3) / 1e12
+    rows["grouped_nvfp4_f16_all_variants"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
+                                              "frac_f16_peak": round(tf / PEAK["f16"], 4),
+                                              "variants": "gather + scatter + bias + gamma, FP16 W"}
+    del qg, dw, doff, cg, dw16, vg, vs, vb, vgm
+
+    # inner-expert (K-ragged) grouped GEMM: the weight-gradient shape of the
+    # same problem (experts' token counts split K, each padded to 256),
+    # operands drawn on the device
+    kcounts = np.diff(off.astype(np.int64))
+    koff = np.concatenate([[0], np.cumsum([-(-int(c) // 256) * 256 for c in kcounts])]).astype(np.int32)
+    kk = int(koff[-1])
+    qk = synth.nvfp4_random_operand(7168, kk, synth.SEEDS["nvfp4_big.A"], dev)
+    gk = torch.Generator(device=dev)
+    gk.manual_seed(4400)
+    wk = (torch.randn((2048, kk), generator=gk, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
+    ck = torch.empty((32, 7168, 2048), dtype=torch.int16, device=dev)
+    dkoff = torch.from_numpy(koff).to(dev)
+    ms = time_events(lambda i: L.bsgemm_grouped_kragged_run(*qk, dkoff, wk, kk, c=ck), 10, 3)
+    kflops = 2.0 * 7168 * 2048 * kk
+    tf = kflops / (ms * 1e-3) / 1e12
+    rows["grouped_kragged_nvfp4_bf16"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
+                                          "shape": f"32 groups, A 7168 x {kk} NVFP4, W 2048 x {kk} BF16, C 32 x 7168 x 2048",
+                                          "flops_counted": "2 * 7168 * 2048 * padded K"}
+    del qk, wk, ck, dkoff
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["all", "headline", "big", "w4a16", "mx"], default="all")
+    ap.add_argument("--only", choices=["all", "headline", "big", "w4a16", "mx", "grouped"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -118,6 +182,18 @@ def main():
 
     if args.only == "w4a16":
         print(json.dumps(w4a16_rows(L, synth, dev)))
+        return
+
+    if args.only == "grouped":
+        out = grouped_rows(L, synth, dev)
+        # HBM counter calibration: a plain 1 GiB device-to-device copy.
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_bytes"] = 1 << 30
+        print(json.dumps(out))
         return
 
     if args.only == "mx":
@@ -230,58 +306,7 @@ def main():
                                       "note": "eager launches through the Python binding are bound by the "
                                               "host; the graph replay gives the GPU time per launch"}
 
-    # ------------------------------------------------------------- grouped
-    log("generating grouped inputs")
-    gx, off, gw = synth.grouped_inputs()
-    qg = L.bsgemm_quantize_nvfp4(torch.from_numpy(gx).to(dev))
-    dw = torch.from_numpy(gw.view(np.int16)).to(dev)
-    doff = torch.from_numpy(off).to(dev)
-    del gx, gw
-    cg = torch.empty((16384, 2048), dtype=torch.int16, device=dev)
-    ms = time_events(lambda i: L.bsgemm_grouped_run(*qg, doff, dw, 7168, c=cg), 10, 3)
-    gflops = 2.0 * 16384 * 2048 * 7168
-    counts = np.diff(off.astype(np.int64))
-    gbytes = 16384 * 7168 * 0.5625 + int((counts > 0).sum()) * 2048 * 7168 * 2 + 16384 * 2048 * 2
-    tf = gflops / (ms * 1e-3) / 1e12
-    rows["grouped_nvfp4_bf16"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
-                                  "gbps_algorithmic": round(gbytes / (ms * 1e-3) / 1e9, 1),
-                                  "groups_nonempty": int((counts > 0).sum()), "max_group_rows": int(counts.max())}
-    # the same problem through the variant entry point: FP16 weights (the BF16
-    # weights converted to FP16 on the device), gather over all rows, a
-    # scatter permutation, bias and gamma
-    rng = np.random.Generator(np.random.PCG64(4200))
-    dw16 = dw.view(torch.bfloat16).to(torch.float16).view(torch.int16)
-    vg = torch.from_numpy(rng.integers(0, 16384, 16384).astype(np.int32)).to(dev)
-    vs = torch.from_numpy(rng.permutation(16384).astype(np.int32)).to(dev)
-    vb = torch.from_numpy((rng.standard_normal((32, 2048)) * 0.1).astype(np.float32)).to(dev)
-    vgm = torch.from_numpy(rng.uniform(-2, 2, 16384).astype(np.float32)).to(dev)
-    ms = time_events(lambda i: L.bsgemm_grouped_run_ex(*qg, doff, dw16, 7168, w_dtype=L.BSGEMM_W_F16, bias=vb,
-                                                       gamma=vgm, gather_idx=vg, scatter_idx=vs, c=cg), 10, 3)
-    tf = gflops / (ms * 1e-3) / 1e12
-    rows["grouped_nvfp4_f16_all_variants"] = {"ms": round(ms, 4), "tflops": round(tf, 2),
-                                              "frac_f16_peak": round(tf / PEAK["f16"], 4),
-                                              "variants": "gather + scatter + bias + gamma, FP16 W"}
-    del qg, dw, doff, cg, dw16, vg, vs, vb, vgm
-
-    # inner-expert (K-ragged) grouped GEMM: the weight-gradient shape of the
-    # same problem (experts' token counts split K, each padded to 256),
-    # operands drawn on the device
-    kcounts = np.diff(off.astype(np.int64))
-    koff = np.concatenate([[0], np.cumsum([-(-int(c) // 256) * 256 for c in kcounts])]).astype(np.int32)
-    kk = int(koff[-1])
-    qk = synth.nvfp4_random_operand(7168, kk, synth.SEEDS["nvfp4_big.A"], dev)
-    gk = torch.Generator(device=dev)
-    gk.manual_seed(4400)
-    wk = (torch.randn((2048, kk), generator=gk, device=dev) * 0.02).to(torch.bfloat16).view(torch.int16)
-    ck = torch.empty((32, 7168, 2048), dtype=torch.int16, device=dev)
-    dkoff = torch.from_numpy(koff).to(dev)
-    ms = time_events(lambda i: L.bsgemm_grouped_kragged_run(*qk, dkoff, wk, kk, c=ck), 10, 3)
-    kflops = 2.0 * 7168 * 2048 * kk
-    tf = kflops / (ms * 1e-3) / 1e12
-    rows["grouped_kragged_nvfp4_bf16"] = {"ms": round(ms, 4), "tflops": round(tf, 2), "frac_bf16_peak": round(tf / PEAK["bf16"], 4),
-                                          "shape": f"32 groups, A 7168 x {kk} NVFP4, W 2048 x {kk} BF16, C 32 x 7168 x 2048",
-                                          "flops_counted": "2 * 7168 * 2048 * padded K"}
-    del qk, wk, ck, dkoff
+    rows.update(grouped_rows(L, synth, dev))
 
     # --------------------------------------------------------------- W4A16
     rows.update(w4a16_rows(L, synth, dev))

@@ -639,6 +639,248 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   }
 }
 
+// Ping-pong form of the ring kernel for K % 256 == 0: eight waves, two per
+// SIMD (waves w and w + 4 share SIMD w % 4), in two groups that take turns.
+// While group 0 runs the MFMAs of step k, group 1 issues its loads for stage
+// k + 2, reads stage k's A codes, scales and W fragments from LDS and
+// expands A; then the roles swap.  The matrix core of each SIMD is fed from
+// one wave while the other wave's memory and VALU work overlaps it.
+//
+// Wave (pg, wq) computes rows [64 wq, 64 wq + 64) x columns
+// [128 pg, 128 pg + 128): 2 x 4 MFMA tiles, 128 accumulator registers.  The
+// MFMAs run in the same K order as in the ring kernel, so the two give
+// identical results.
+//
+// Ring: 3 stages, loads two stages ahead.  B_a(k) is the barrier at which
+// group 0 enters the MFMA phase of step k, B_b(k) the one at which group 1
+// does.  Each group issues the loads of stage k + 2 at the start of its
+// MFMA phase of step k (after B_a(k), resp. B_b(k)); every read of stage
+// k - 1, whose slot they overwrite, ends by B_a(k).  That leaves the MFMA
+// phase free to read W fragments of the current stage too.
+struct GPPSmem {
+  uint4 a[GR_NS][BM * ARC];
+  uint4 w[GR_NS][BN * WRC];
+  uint32_t as[GR_SBUF][BM * 4];
+  int tile_info[4];
+  GEpi epi;
+};
+
+template <bool F16, int PRIO>
+__global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
+  using GM = GMath<F16>;
+  using VT = typename GM::vec;
+  constexpr int U = 4;                       // steps per 16-byte scale load
+  __shared__ GPPSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pg = wave >> 2, wq = wave & 3;
+  const int M = p.M, N = p.N, K = p.K;
+  const int KH = K / 2, KB = K / 16;
+  // tile order as in the ring kernel (n-major, XCD-contiguous)
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int mtiles = gridDim.x / p.tiles_n;
+  const int nt = t / mtiles;
+  const int mt = t - nt * mtiles;
+  if (wave == 0) find_tile(p.off, p.G, mt, lane, sm.tile_info);
+  __syncthreads();
+  const int grp = sm.tile_info[0];
+  if (grp < 0) return;                        // uniform over the workgroup
+  const int r0 = min(max(sm.tile_info[1], 0), M);
+  const int r1 = min(max(sm.tile_info[2], r0), M);
+  const int n0 = nt * BN;
+  const int KT = K / BK;                      // a multiple of U
+  const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
+  const bool gat = p.gather != nullptr;
+  const rsrc4_t ra = make_rsrc4(gat ? p.A : p.A + (int64_t)r0 * KH, (gat ? p.a_rows : rows_a) * KH);
+  const rsrc4_t rsa = make_rsrc4(gat ? p.As : p.As + (int64_t)r0 * KB, (gat ? p.a_rows : rows_a) * KB);
+  const rsrc4_t rw = make_rsrc4(p.W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  fill_epi(p, r0, rows_a, tid, sm.epi);   // visible after the prologue's barrier
+
+  // Load geometry.  Wave w's A load covers rows 32 w .. +31 (two lanes per
+  // row); its W load u (0..3) covers rows 8 (4 w + u) .. +7 (eight lanes per
+  // row); group 0's waves also load the scales of rows 64 wq .. +63.
+  const int arow = 32 * wave + (lane >> 1);
+  const int asrc = gat ? gather_row(p, r0, rows_a, arow) : arow;
+  const int a_off = asrc >= 0 ? asrc * KH + (((lane & 1) ^ ((arow >> 3) & 1)) * 16) : -1;
+  int w_off[2];   // loads u and u + 2 differ by 16 rows and share the swizzle
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 8 * (4 * wave + u) + (lane >> 3);
+    w_off[u] = row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
+  }
+  const int s_src = gat ? gather_row(p, r0, rows_a, 64 * wq + lane) : 64 * wq + lane;
+  const int s_off = s_src >= 0 ? s_src * KB : -1;
+
+  auto issue = [&](int st, auto PG, auto WITH_SCALES) {
+    const int slot = st % GR_NS;
+    const bool live = st < KT;
+    if constexpr (decltype(PG)::value == 0 && decltype(WITH_SCALES)::value) {
+      const int sbuf = (st / U) % GR_SBUF;
+      dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wq * 4]), (live && s_off >= 0) ? s_off + (st / U) * 16 : OOB);
+    }
+    dma_x4(ra, lds_addr(&sm.a[slot][64 * wave]), (live && a_off >= 0) ? a_off + st * AROWB : OOB);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      dma_x4(rw, lds_addr(&sm.w[slot][64 * (4 * wave + u)]),
+             live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
+  };
+  // loads per wave for stage st (st % U == s_mod): the scale load joins
+  // group 0's A and W loads at the start of each 4-step scale batch
+  auto loads_of = [](int pg_, int s_mod) { return 5 + ((pg_ == 0 && s_mod == 0) ? 1 : 0); };
+
+  const int r = lane & 31, g = lane >> 5;
+  VT av[4][2];
+  // This wave's 2 A row fragments of stage st (st % U == IN), expanded for
+  // all four K16 sub-steps.  Sub-step sp pairs lane half g with K
+  // 32 g + 8 sp .. + 7, whose scale is byte 2 g + sp / 2 of the row's 4 scale
+  // bytes for the step.
+  auto read_a = [&](int st, auto INC) {
+    constexpr int IN = decltype(INC)::value;
+    const int slot = st % GR_NS, sbuf = (st / U) % GR_SBUF;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = wq * 64 + i * 32 + r;
+      const uint4 c = sm.a[slot][aswz(row, g)];
+      const uint32_t word = sm.as[sbuf][row * 4 + IN] >> (16 * g);
+      const v2f sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);   // exact E4M3
+      const uint32_t m0 = GM::mant(sv[0]), m1 = GM::mant(sv[1]);
+      av[0][i] = GM::dq8(c.x, sv[0], m0);
+      av[1][i] = GM::dq8(c.y, sv[0], m0);
+      av[2][i] = GM::dq8(c.z, sv[1], m1);
+      av[3][i] = GM::dq8(c.w, sv[1], m1);
+    }
+  };
+  // This wave's 4 W fragments of sub-step sp of stage st.
+  auto read_w = [&](int st, int sp, VT* bv) {
+    const int slot = st % GR_NS;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 q = sm.w[slot][wswz(pg * 128 + j * 32 + r, 4 * g + sp)];
+      __builtin_memcpy(&bv[j], &q, 16);
+    }
+  };
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  auto mfmas = [&](const VT* a, const VT* b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = GM::mfma(a[i], b[j], acc[i][j]);
+  };
+
+  VT bv0[4], bv1[4], bv2[4], bv3[4];
+  // Memory phase of step k: A expanded for the whole step, W of sub-steps 0-1.
+  auto mem_phase = [&](int k, auto INC) {
+    read_a(k, INC);
+    read_w(k, 0, bv0);
+    read_w(k, 1, bv1);
+  };
+  // MFMA phase of step k: the loads of stage k + 2, then the 32 MFMAs, with
+  // the W fragments of sub-steps 2-3 read under those of sub-steps 0-1.
+  auto mfma_phase = [&](int k, auto PG, auto WS) {
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
+    issue(k + 2, PG, WS);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(av[0], bv0);
+    read_w(k, 2, bv2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(av[1], bv1);
+    read_w(k, 3, bv3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(av[2], bv2);
+    mfmas(av[3], bv3);
+    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
+  };
+
+  using Z = std::integral_constant<int, 0>;
+  using O = std::integral_constant<int, 1>;
+  // Prologue: stages 0 and 1; stage 0 complete everywhere before the first read.
+  if (pg == 0) {
+    issue(0, Z{}, std::true_type{});
+    issue(1, Z{}, std::false_type{});
+    wait_vm_barrier<loads_of(0, 1)>();
+  } else {
+    issue(0, O{}, std::true_type{});
+    issue(1, O{}, std::false_type{});
+    wait_vm_barrier<loads_of(1, 1)>();
+  }
+  // Group 0: [mem k] B_a(k) [MFMA k] B_b(k).
+  // Group 1: B_a(0), then [mem k] B_b(k) [MFMA k] B_a(k+1).
+  // At B_b(k) every wave's stage k + 1 loads have landed (group 0 may still
+  // have stage k + 2 in flight; group 1 issues it after B_b(k)), so group 0's
+  // reads of stage k + 1 after B_b(k), and group 1's after B_a(k + 1), see
+  // the whole stage.
+  if (pg == 0) {
+    for (int kt = 0; kt < KT; kt += U) {
+      static_for<0, U>([&](auto IC) {
+        constexpr int IN = decltype(IC)::value;
+        const int k = kt + IN;
+        mem_phase(k, IC);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_phase(k, Z{}, std::integral_constant<bool, ((IN + 2) % U) == 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm_barrier<loads_of(0, (IN + 2) % U)>();
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    asm volatile("s_barrier" ::: "memory");
+  } else {
+    asm volatile("s_barrier" ::: "memory");
+    for (int kt = 0; kt < KT; kt += U) {
+      static_for<0, U>([&](auto IC) {
+        constexpr int IN = decltype(IC)::value;
+        const int k = kt + IN;
+        mem_phase(k, IC);
+        wait_vm_barrier<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_phase(k, O{}, std::integral_constant<bool, ((IN + 2) % U) == 0>{});
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
+
+  // Epilogue as in the ring kernel, for this wave's 64 x 128 block.
+  const float alpha = *p.Ats;
+  const bool plain = !p.bias && !p.gamma && !p.scatter;
+  const int cn0 = n0 + pg * 128;
+  if (plain && r0 + BM <= r1 && n0 + BN <= N) {
+    uint16_t* cw = p.C + (int64_t)(r0 + wq * 64 + g * 4) * N + cn0 + r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] =
+              (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = cn0 + j * 32 + r;
+      const float b = (p.bias && col < N) ? p.bias[(int64_t)grp * N + col] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int lr = wq * 64 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          const int dst = sm.epi.dst[lr];
+          float y = acc[i][j][v] * alpha;
+          if (p.bias) y += b;
+          if (p.gamma) y *= sm.epi.gamma[lr];
+          if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_grouped_kragged(const KRaggedCall& c, hipStream_t stream) {
@@ -666,14 +908,14 @@ hipError_t launch_grouped(const GroupedCall& c, hipStream_t stream) {
   const int64_t k = c.k;
   if (c.w_f16) {
     if (k % 256 == 0 && k > 0)
-      hipLaunchKernelGGL((grouped_ring_kernel<16, true>), grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((grouped_pp_kernel<true, 0>), grid, dim3(512), 0, stream, p);
     else if (k % 64 == 0 && k > 0)
       hipLaunchKernelGGL((grouped_ring_kernel<4, true>), grid, dim3(NT), 0, stream, p);
     else
       hipLaunchKernelGGL(grouped_kernel<true>, grid, dim3(NT), 0, stream, p);
   } else {
     if (k % 256 == 0 && k > 0)
-      hipLaunchKernelGGL((grouped_ring_kernel<16, false>), grid, dim3(NT), 0, stream, p);
+      hipLaunchKernelGGL((grouped_pp_kernel<false, 0>), grid, dim3(512), 0, stream, p);
     else if (k % 64 == 0 && k > 0)
       hipLaunchKernelGGL((grouped_ring_kernel<4, false>), grid, dim3(NT), 0, stream, p);
     else
