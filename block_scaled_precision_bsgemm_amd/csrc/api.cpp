@@ -373,7 +373,8 @@ int bsgemm_grouped_kragged_run(int num_groups, int64_t m, int64_t n, int64_t k, 
     if ((reinterpret_cast<uintptr_t>(k_offsets) & 3u) != 0)
       return fail(BSGEMM_ERR_BAD_ALIGNMENT, "%s: k_offsets is not 4-byte aligned", fn);
     if (int s = check_limits(fn, m, n, k)) return s;
-    if ((int64_t)num_groups * ((m + 255) / 256) * ((n + 255) / 256) > MAX_ROWS)
+    // the launch pads the (group, n tile) units to a multiple of 8
+    if (((int64_t)num_groups * ((n + 255) / 256) + 7) / 8 * 8 * ((m + 255) / 256) > MAX_ROWS)
       return fail(BSGEMM_ERR_RESOURCE, "%s: too many tiles", fn);
     int num_cus = 0;
     if (int s = check_device(fn, &num_cus)) return s;

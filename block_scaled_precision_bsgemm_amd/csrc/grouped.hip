@@ -351,24 +351,32 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int M = p.M, N = p.N, K = p.K;
   const int KH = K / 2, KB = K / 16;
-  // n-tile-major order: consecutive tiles (kept on one XCD by xcd_remap) are
-  // the m-tiles of one W column panel, so each group's W panel is fetched
-  // from HBM about once and re-read from L2; A (small) is shared through the
-  // infinity cache across panels.
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
   int grp, r0, r1, nt, k0 = 0, k1 = K;
   if constexpr (KRAG) {
-    const int per_g = p.tiles_m * p.tiles_n;
-    grp = t / per_g;
-    const int rem = t - grp * per_g;
-    nt = rem / p.tiles_m;
-    r0 = (rem - nt * p.tiles_m) * BM;
+    // Unit u = (group, n tile): its tiles_m m-tiles run back to back on one
+    // XCD and share the unit's W slice through L2.  Units go round-robin over
+    // the 8 XCDs (workgroup b runs on XCD b % 8), so each XCD gets every
+    // group's n-tiles in turn: with contiguous blocks of units, the XCD that
+    // drew the longest K slices set the kernel time (up to 2.7x its share
+    // for Dirichlet-sized experts).  The grid is padded to whole rounds of 8
+    // units; padding workgroups exit here.
+    const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+    const int u = (i / p.tiles_m) * 8 + x;
+    if (u >= p.G * p.tiles_n) return;        // uniform over the workgroup
+    grp = u / p.tiles_n;
+    nt = u - grp * p.tiles_n;
+    r0 = (i % p.tiles_m) * BM;
     r1 = min(r0 + BM, M);
     // offsets are a documented precondition; clamped and rounded down to
     // multiples of 256, a malformed one still stays inside A and W
     k0 = min(max(p.koff[grp], 0), K) & ~255;
     k1 = min(max(p.koff[grp + 1], k0), K) & ~255;
   } else {
+    // n-tile-major order: consecutive tiles (kept on one XCD by xcd_remap)
+    // are the m-tiles of one W column panel, so each group's W panel is
+    // fetched from HBM about once and re-read from L2; A (small) is shared
+    // through the infinity cache across panels.
+    const int t = xcd_remap(blockIdx.x, gridDim.x);
     const int mtiles = gridDim.x / p.tiles_n;
     nt = t / mtiles;
     const int mt = t - nt * mtiles;
@@ -889,7 +897,8 @@ hipError_t launch_grouped_kragged(const KRaggedCall& c, hipStream_t stream) {
   p.G = c.num_groups; p.M = (int)c.m; p.a_rows = (int)c.m; p.N = (int)c.n; p.K = (int)c.k;
   p.tiles_n = (int)ceil_div(c.n, BN);
   p.tiles_m = (int)ceil_div(c.m, BM);
-  const dim3 grid((unsigned)((int64_t)c.num_groups * p.tiles_m * p.tiles_n));
+  const int64_t units = (int64_t)c.num_groups * p.tiles_n;   // padded to whole rounds of 8 (one per XCD)
+  const dim3 grid((unsigned)(ceil_div(units, 8) * 8 * p.tiles_m));
   if (c.w_f16)
     hipLaunchKernelGGL((grouped_ring_kernel<16, true, true>), grid, dim3(NT), 0, stream, p);
   else
