@@ -397,6 +397,8 @@ def _gpu_grouped(qa, off, w, k):
     ([600, 0, 0, 900], 512, 256),
     ([77, 256], 260, 320),                 # odd number of 64-element K steps
     ([512, 256, 0, 300], 512, 1280),       # whole 256-row tiles; 16-byte scale batches
+    ([300, 0, 257], 258, 256),             # n % 4 != 0: 2-byte stores on the ping-pong path
+    ([77, 256], 262, 320),                 # n % 4 != 0 on the 4-byte-scale ring
 ])
 def test_grouped_shapes(gpu_lib, counts, n, k):
     qa, off, w = _grouped_case(counts, n, k, sum(counts) + n + k)
@@ -464,17 +466,18 @@ ALL = ("bias", "gamma", "gather", "scatter")
 
 
 @pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
-@pytest.mark.parametrize("k", [96, 320, 512])
-def test_grouped_ex_all_variants(gpu_lib, w_dtype, k):
+@pytest.mark.parametrize("k,n", [(96, 260), (320, 260), (512, 260), (512, 254)])
+def test_grouped_ex_all_variants(gpu_lib, w_dtype, k, n):
     """bias + gamma + gather (from fewer A rows than m, with repeats) + scatter,
     on the register-staged (K = 96), 4-byte-scale ring (K % 64) and
-    16-byte-scale ring (K % 256) kernels, BF16 and FP16 weights."""
-    counts, n = [77, 256, 0, 300], 260
+    ping-pong (K % 256) kernels, BF16 and FP16 weights; n = 254 takes the
+    2-byte stores of the scattered epilogue."""
+    counts = [77, 256, 0, 300]
     m = sum(counts)
     qa, off, w, v = _variant_case(counts, n, k, 700 + k, w_dtype, a_rows=500)
     say("grouped_ex all variants", w_dtype, counts, n, k)
     c = _gpu_grouped_ex(qa, off, w, k, w_dtype, v, ALL, m)
-    assert_ok(G.check(c, *_ref_ex(qa, off, w, w_dtype, v, ALL)), f"grouped_ex {w_dtype} k={k}")
+    assert_ok(G.check(c, *_ref_ex(qa, off, w, w_dtype, v, ALL)), f"grouped_ex {w_dtype} k={k} n={n}")
     assert not np.any(c == SENTINEL)
 
 
@@ -573,6 +576,7 @@ def _kragged_case(counts, m, n, seed, w_dtype):
     ([256], 256, 256),
     ([100, 0, 700, 256], 300, 260),        # an empty group, ragged m and n tails
     ([1, 255, 257, 1024], 64, 520),
+    ([100, 300], 270, 258),                # n % 4 != 0: 2-byte stores
 ])
 def test_grouped_kragged_shapes(gpu_lib, w_dtype, counts, m, n):
     qa, off, w, k = _kragged_case(counts, m, n, sum(counts) + m, w_dtype)
