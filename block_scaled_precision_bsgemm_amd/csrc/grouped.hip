@@ -648,11 +648,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
 }
 
 // Ping-pong form of the ring kernel for K % 256 == 0: eight waves, two per
-// SIMD (waves w and w + 4 share SIMD w % 4), in two groups that take turns.
-// While group 0 runs the MFMAs of step k, group 1 issues its loads for stage
-// k + 2, reads stage k's A codes, scales and W fragments from LDS and
+// SIMD (waves w and w + 4 share SIMD w % 4 under the round-robin placement),
+// in two groups that take turns.  While group 0 runs the MFMAs of step k,
+// group 1 reads stage k's A codes, scales and W fragments from LDS and
 // expands A; then the roles swap.  The matrix core of each SIMD is fed from
-// one wave while the other wave's memory and VALU work overlaps it.
+// one wave while the other wave's LDS and VALU work overlaps it.
 //
 // Wave (pg, wq) computes rows [64 wq, 64 wq + 64) x columns
 // [128 pg, 128 pg + 128): 2 x 4 MFMA tiles, 128 accumulator registers.  The
@@ -673,7 +673,7 @@ struct GPPSmem {
   GEpi epi;
 };
 
-template <bool F16, int PRIO>
+template <bool F16>
 __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
   using GM = GMath<F16>;
   using VT = typename GM::vec;
@@ -790,7 +790,6 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
   // MFMA phase of step k: the loads of stage k + 2, then the 32 MFMAs, with
   // the W fragments of sub-steps 2-3 read under those of sub-steps 0-1.
   auto mfma_phase = [&](int k, auto PG, auto WS) {
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
     issue(k + 2, PG, WS);
     __builtin_amdgcn_sched_barrier(0);
     mfmas(av[0], bv0);
@@ -801,7 +800,6 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     mfmas(av[2], bv2);
     mfmas(av[3], bv3);
-    if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   using Z = std::integral_constant<int, 0>;
@@ -917,14 +915,14 @@ hipError_t launch_grouped(const GroupedCall& c, hipStream_t stream) {
   const int64_t k = c.k;
   if (c.w_f16) {
     if (k % 256 == 0 && k > 0)
-      hipLaunchKernelGGL((grouped_pp_kernel<true, 0>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((grouped_pp_kernel<true>), grid, dim3(512), 0, stream, p);
     else if (k % 64 == 0 && k > 0)
       hipLaunchKernelGGL((grouped_ring_kernel<4, true>), grid, dim3(NT), 0, stream, p);
     else
       hipLaunchKernelGGL(grouped_kernel<true>, grid, dim3(NT), 0, stream, p);
   } else {
     if (k % 256 == 0 && k > 0)
-      hipLaunchKernelGGL((grouped_pp_kernel<false, 0>), grid, dim3(512), 0, stream, p);
+      hipLaunchKernelGGL((grouped_pp_kernel<false>), grid, dim3(512), 0, stream, p);
     else if (k % 64 == 0 && k > 0)
       hipLaunchKernelGGL((grouped_ring_kernel<4, false>), grid, dim3(NT), 0, stream, p);
     else
