@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsgemm.so")
 
-SOURCES = ["api.cpp", "quantize.hip", "gemm_mx.hip", "gemm_nvfp4.hip", "grouped.hip", "w4a16.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm_mx.hip", "gemm_mx8_exact.hip", "gemm_nvfp4.hip", "grouped.hip",
+           "w4a16.hip"]
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-I" + INCLUDE, "-I" + CSRC,

@@ -136,7 +136,7 @@ int check_limits(const char* fn, int64_t rows_a, int64_t rows_b, int64_t k) {
 
 extern "C" {
 
-int bsgemm_version(void) { return 500; }   // 0.5.0: K-ragged grouped GEMM
+int bsgemm_version(void) { return 600; }   // 0.6.0: exact-product MXFP8 GEMM (BSGEMM_MXFP8_EXACT)
 
 const char* bsgemm_status_string(int status) {
   switch (status) {
@@ -239,10 +239,10 @@ int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k, const uint8_t* a,
     if (fmt == BSGEMM_NVFP4) {
       if (a_tscale == nullptr || b_tscale == nullptr)
         return fail(BSGEMM_ERR_INVALID_ARG, "%s: NVFP4 needs a_tscale and b_tscale", fn);
-    } else if (fmt == BSGEMM_MXFP8 || fmt == BSGEMM_MXFP4) {
+    } else if (fmt == BSGEMM_MXFP8 || fmt == BSGEMM_MXFP4 || fmt == BSGEMM_MXFP8_EXACT) {
       if (a_tscale != nullptr || b_tscale != nullptr)
         return fail(BSGEMM_ERR_UNSUPPORTED, "%s: %s takes no tensor scales (pass NULL)", fn,
-                    fmt == BSGEMM_MXFP8 ? "MXFP8" : "MXFP4");
+                    fmt == BSGEMM_MXFP4 ? "MXFP4" : "MXFP8");
     } else {
       return fail(BSGEMM_ERR_UNSUPPORTED, "%s: unknown format %d", fn, fmt);
     }
@@ -260,7 +260,9 @@ int bsgemm_run(int fmt, int64_t m, int64_t n, int64_t k, const uint8_t* a,
     const hipError_t e =
         fmt == BSGEMM_NVFP4   ? bsg::launch_gemm_nvfp4(m, n, k, a, a_scales, a_tscale, b, b_scales, b_tscale, c_bf16, st)
         : fmt == BSGEMM_MXFP8 ? bsg::launch_gemm_mxfp8(m, n, k, a, a_scales, b, b_scales, c_bf16, st)
-                              : bsg::launch_gemm_mxfp4(m, n, k, a, a_scales, b, b_scales, c_bf16, st);
+        : fmt == BSGEMM_MXFP8_EXACT
+            ? bsg::launch_gemm_mxfp8_exact(m, n, k, a, a_scales, b, b_scales, c_bf16, st)
+            : bsg::launch_gemm_mxfp4(m, n, k, a, a_scales, b, b_scales, c_bf16, st);
     return finish_launch(fn, e, st);
   } catch (...) {
     return fail(BSGEMM_ERR_LAUNCH, "%s: internal exception", fn);

@@ -19,6 +19,10 @@ hipError_t launch_quantize_nvfp4(int64_t rows, int64_t k, const float* x, uint8_
 hipError_t launch_gemm_mxfp8(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
                              hipStream_t stream);
+// MXFP8 operands, products expanded exactly to BF16, BF16 MFMA (FP32 accumulation).
+hipError_t launch_gemm_mxfp8_exact(int64_t m, int64_t n, int64_t k, const uint8_t* a,
+                                   const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
+                                   hipStream_t stream);
 hipError_t launch_gemm_mxfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
                              const uint8_t* as, const uint8_t* b, const uint8_t* bs, uint16_t* c,
                              hipStream_t stream);

@@ -53,8 +53,15 @@
  *     gives a message for the last failure on the calling thread.
  *   - Preconditions that are documented but not checked on the device: inputs
  *     are finite, and group offsets are monotone.
+ *   - Accuracy.  Quantizers are bit-exact.  The GEMMs accumulate in FP32 and
+ *     round C once to BF16.  For BSGEMM_NVFP4, BSGEMM_MXFP8_EXACT, BSGEMM_MXFP4
+ *     and every grouped and W4A16 call, every product is exact and the result
+ *     differs from the exact sum only by FP32 summation order and the final
+ *     rounding: |C - C_exact| <= 2^-8 |C_exact| + 1e-5 sum_k |a_k b_k| per
+ *     element, for operands whose products and sums stay in FP32's normal
+ *     range.  BSGEMM_MXFP8 is the exception; see bsgemm_run.
  *   - Results do not depend on the launch configuration chosen internally
- *     beyond FP32 summation order (quantizers: bit-exact).
+ *     beyond FP32 summation order.
  */
 #ifndef BSGEMM_H
 #define BSGEMM_H
@@ -77,8 +84,9 @@ enum bsgemm_status {
 
 enum bsgemm_format {
   BSGEMM_NVFP4 = 1,
-  BSGEMM_MXFP8 = 2,
-  BSGEMM_MXFP4 = 3
+  BSGEMM_MXFP8 = 2,        /* native scaled FP8 MFMA; see the accuracy note at bsgemm_run */
+  BSGEMM_MXFP4 = 3,
+  BSGEMM_MXFP8_EXACT = 4   /* MXFP8 operands, exact products on the BF16 MFMA */
 };
 
 /*
@@ -173,13 +181,31 @@ int bsgemm_quantize_mxfp4(int64_t rows, int64_t k, const float* x, uint8_t* code
  * (e2m1 * e4m3)_A * (e2m1 * e4m3)_B and is then multiplied by
  * (*a_tscale) * (*b_tscale).  MXFP8 and MXFP4 apply their E8M0 block scales
  * inside the matrix-core product.
+ *
+ * MXFP8 accuracy.  The two MXFP8 paths take the same operands:
+ *   BSGEMM_MXFP8        the native scaled FP8 MFMA, at the FP8 rate.  It sums
+ *                       each aligned group of 8 products to about 14 bits
+ *                       below the group's largest product (measured on
+ *                       gfx950; the groups are then combined in FP32).  The
+ *                       per-element bound is therefore
+ *                         2^-8 |C| + 1e-5 sum_k |a_k b_k| + 2^-10 sum_groups max |a_k b_k|.
+ *                       The last term matters only where one 32-element block
+ *                       holds values ~2^10 or more apart next to each other.
+ *                       On quantizer output of data without such spread
+ *                       (e.g. N(0,1)), the plain bound holds.
+ *   BSGEMM_MXFP8_EXACT  every e4m3(code) * 2^(scale - 127) expanded exactly to
+ *                       BF16 and multiplied on the BF16 MFMA: the plain bound
+ *                       (FP32 summation order only) on every operand whose
+ *                       products stay in FP32's normal range, at half the FP8
+ *                       rate.
  * Source: "Together AI Ports ThunderKittens GEMM Kernels to NVIDIA Vera Rubin
  * NVL72", section "Building the GEMM" (NVFP4 and FP8 E4M3 GEMMs, 16k square);
  * MXFP4 is the MX member with the E2M1 element ("Triton #11171 ...", section
  * "The broader related matrix protected neighboring policy").
  *
  * Arguments:
- *   fmt                 BSGEMM_NVFP4, BSGEMM_MXFP8 or BSGEMM_MXFP4
+ *   fmt                 BSGEMM_NVFP4, BSGEMM_MXFP8, BSGEMM_MXFP8_EXACT or
+ *                       BSGEMM_MXFP4
  *   a, a_scales         operand A [m][k] in the layout of `fmt`
  *   a_tscale, b_tscale  device float[1] for NVFP4; must be NULL for the MX
  *                       formats

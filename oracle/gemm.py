@@ -15,8 +15,6 @@ Besides C the references return T[m, n] = sum_k |deq(A)[m, k] * deq(B)[n, k]|,
 the scale of the accumulation error.
 """
 
-from fractions import Fraction
-
 import numpy as np
 
 from .formats import (decode_bf16, decode_e2m1, decode_e4m3, decode_e8m0,
@@ -221,11 +219,6 @@ def w4a16(x_bf16, w_codes, w_scales, w_ts):
     x = decode_bf16(x_bf16)
     w = dequant_nvfp4(w_codes, w_scales, w_ts)
     return _matmul_and_mag(x, w)
-
-
-def exact_dot(avals, bvals) -> Fraction:
-    """sum_k a_k * b_k in exact rationals (brute force for tiny pins)."""
-    return sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(avals, bvals)), Fraction(0))
 
 
 # -------------------------------------------------------------- acceptance --

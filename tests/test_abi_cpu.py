@@ -42,7 +42,7 @@ def test_status_strings_and_version(so):
                        (5, b"BSGEMM_ERR_RESOURCE"), (6, b"BSGEMM_ERR_LAUNCH")]:
         assert so.bsgemm_status_string(code) == name
     assert so.bsgemm_status_string(99) == b"unknown status"
-    assert so.bsgemm_version() == 500
+    assert so.bsgemm_version() == 600
 
 
 def run(so, fmt=L.BSGEMM_NVFP4, m=64, n=64, k=64, a=P, sa=P, ta=P, b=P, sb=P, tb=P, c=P):
@@ -62,6 +62,11 @@ def test_run_validation(so):
     assert b"MXFP4 takes no tensor scales" in so.bsgemm_last_error()
     assert run(so, fmt=L.BSGEMM_MXFP4, ta=None, tb=None, k=80) == L.BSGEMM_ERR_UNSUPPORTED
     assert run(so, fmt=L.BSGEMM_MXFP4, ta=None, tb=None, sb=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert run(so, fmt=L.BSGEMM_MXFP8_EXACT) == L.BSGEMM_ERR_UNSUPPORTED   # tensor scales given
+    assert b"MXFP8 takes no tensor scales" in so.bsgemm_last_error()
+    assert run(so, fmt=L.BSGEMM_MXFP8_EXACT, ta=None, tb=None, k=80) == L.BSGEMM_ERR_UNSUPPORTED
+    assert run(so, fmt=L.BSGEMM_MXFP8_EXACT, ta=None, tb=None, a=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
+    assert run(so, fmt=5) == L.BSGEMM_ERR_UNSUPPORTED
     assert run(so, a=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, c=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
     assert run(so, sa=MIS) == L.BSGEMM_ERR_BAD_ALIGNMENT
@@ -243,6 +248,7 @@ def test_no_device_is_reported_not_launched(so):
     assert so.bsgemm_quantize_mxfp8(4, 64, P, P, P, None) == L.BSGEMM_ERR_DEVICE
     assert so.bsgemm_quantize_mxfp4(4, 64, P, P, P, None) == L.BSGEMM_ERR_DEVICE
     assert run(so, fmt=L.BSGEMM_MXFP4, ta=None, tb=None) == L.BSGEMM_ERR_DEVICE
+    assert run(so, fmt=L.BSGEMM_MXFP8_EXACT, ta=None, tb=None) == L.BSGEMM_ERR_DEVICE
 
 
 def test_binding_raises_on_error():
@@ -250,3 +256,65 @@ def test_binding_raises_on_error():
     x = torch.zeros(4, 40)
     with pytest.raises(Exception):
         L.bsgemm_quantize_mxfp8(x)   # CPU tensor: rejected before any call
+
+
+def test_binding_validates_before_calling():
+    """The binding rejects wrong dtypes, shapes and layouts with ValueError
+    before any call into the library (dtype and shape are checked before the
+    device, so CPU tensors exercise them here)."""
+    import torch
+    u8 = lambda *s: torch.zeros(*s, dtype=torch.uint8)   # noqa: E731
+    f32 = lambda *s: torch.zeros(*s, dtype=torch.float32)   # noqa: E731
+    with pytest.raises(ValueError, match="dtype"):
+        L.bsgemm_quantize_nvfp4(torch.zeros(4, 64, dtype=torch.float64))
+    with pytest.raises(ValueError, match="2-D"):
+        L.bsgemm_quantize_mxfp8(f32(256))
+    with pytest.raises(ValueError, match="codes: shape"):
+        L.bsgemm_quantize_nvfp4(f32(4, 64), codes=u8(4, 16))
+    with pytest.raises(ValueError, match="tensor_scale"):
+        L.bsgemm_quantize_nvfp4(f32(4, 64), codes=u8(4, 32), scales=u8(4, 4), tensor_scale=f32(2))
+    ts = f32(1)
+    # NVFP4 operand [rows, 64]: codes [rows, 32], scales [rows, 4]
+    with pytest.raises(ValueError, match="a_scales: shape"):
+        L.bsgemm_run(L.BSGEMM_NVFP4, u8(8, 32), u8(8, 2), ts, u8(4, 32), u8(4, 4), ts, 64)
+    with pytest.raises(ValueError, match="a: shape"):          # k disagrees with the codes
+        L.bsgemm_run(L.BSGEMM_NVFP4, u8(8, 32), u8(8, 4), ts, u8(4, 32), u8(4, 4), ts, 128)
+    with pytest.raises(ValueError, match="b: shape"):          # MXFP8 codes are [rows, k]
+        L.bsgemm_run(L.BSGEMM_MXFP8_EXACT, u8(8, 64), u8(8, 2), None, u8(4, 32), u8(4, 2), None, 64)
+    with pytest.raises(ValueError, match="c: shape"):
+        L.bsgemm_run(L.BSGEMM_MXFP4, u8(8, 32), u8(8, 2), None, u8(4, 32), u8(4, 2), None, 64,
+                     c=torch.zeros(4, 8, dtype=torch.int16))
+    with pytest.raises(ValueError, match="c: dtype"):
+        L.bsgemm_run(L.BSGEMM_MXFP4, u8(8, 32), u8(8, 2), None, u8(4, 32), u8(4, 2), None, 64,
+                     c=torch.zeros(8, 4, dtype=torch.float32))
+    with pytest.raises(ValueError, match="group_offsets"):
+        L.bsgemm_grouped_run(u8(8, 32), u8(8, 4), ts, torch.zeros(2, dtype=torch.int32),
+                             torch.zeros(2, 16, 64, dtype=torch.int16), 64)
+    with pytest.raises(ValueError, match="gamma"):
+        L.bsgemm_grouped_run_ex(u8(8, 32), u8(8, 4), ts, torch.zeros(3, dtype=torch.int32),
+                                torch.zeros(2, 16, 64, dtype=torch.int16), 64, gamma=f32(7))
+    with pytest.raises(ValueError, match="w_scales: shape"):
+        L.bsgemm_w4a16_run(torch.zeros(2, 64, dtype=torch.bfloat16), u8(16, 32), u8(16, 2), ts)
+    with pytest.raises(ValueError, match="k_offsets"):
+        L.bsgemm_grouped_kragged_run(u8(8, 128), u8(8, 16), ts, torch.zeros(3, dtype=torch.int64),
+                                     torch.zeros(16, 256, dtype=torch.int16), 256)
+    with pytest.raises(ValueError, match="w: shape"):
+        L.bsgemm_grouped_kragged_run(u8(8, 128), u8(8, 16), ts, torch.zeros(3, dtype=torch.int32),
+                                     torch.zeros(16, 512, dtype=torch.int16), 256)
+    with pytest.raises(ValueError, match="c: shape"):
+        L.bsgemm_grouped_kragged_run(u8(8, 128), u8(8, 16), ts, torch.zeros(3, dtype=torch.int32),
+                                     torch.zeros(16, 256, dtype=torch.int16), 256,
+                                     c=torch.zeros(2, 16, 8, dtype=torch.int16))
+    # every check passes: only the placement check (CPU tensors) is left
+    with pytest.raises(ValueError, match="device tensor"):
+        L.bsgemm_grouped_kragged_run(u8(8, 128), u8(8, 16), ts, torch.zeros(3, dtype=torch.int32),
+                                     torch.zeros(16, 256, dtype=torch.uint16), 256)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.bsgemm_grouped_run_ex(u8(8, 32), u8(8, 4), ts, torch.zeros(3, dtype=torch.int32),
+                                torch.zeros(2, 16, 64, dtype=torch.float16), 64, w_dtype=L.BSGEMM_W_F16,
+                                bias=f32(2, 16), gamma=f32(8), gather_idx=torch.zeros(8, dtype=torch.int32),
+                                scatter_idx=torch.zeros(8, dtype=torch.int32))
+    with pytest.raises(ValueError, match="device tensor"):
+        L.bsgemm_w4a16_run(torch.zeros(2, 64, dtype=torch.bfloat16), u8(16, 32), u8(16, 4), ts)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.bsgemm_run(L.BSGEMM_MXFP8_EXACT, u8(8, 64), u8(8, 2), None, u8(4, 64), u8(4, 2), None, 64)
