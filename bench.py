@@ -342,7 +342,10 @@ def grouped_rows(L, synth, dev, par):
         "groups_nonempty": int((counts > 0).sum()), "max_group_rows": int(counts.max())})
     if par.enabled:
         par.flag("grouped_nvfp4_bf16", no_nan(cg), "no_unwritten_output")
-        par.gemm("grouped_nvfp4_bf16", u16(cg)[srows], *G.grouped_nvfp4_bf16(*qa, off, gw, rows=srows),
+        # the oracle indexes A by row: place the sampled rows in a full-size A
+        qfa = (np.zeros((16384, 3584), np.uint8), np.zeros((16384, 448), np.uint8), qa[2])
+        qfa[0][srows], qfa[1][srows] = qa[0], qa[1]
+        par.gemm("grouped_nvfp4_bf16", u16(cg)[srows], *G.grouped_nvfp4_bf16(*qfa, off, gw, rows=srows),
                  f"{len(srows)} rows (first/last of every group + random) x 2048 columns")
 
     # The same problem through the variant entry point: FP16 weights (the BF16
