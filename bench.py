@@ -32,8 +32,8 @@ The same JSON line carries:
     Cache, so their operands are read cold.
 
 ``--only headline|mx|grouped|w4a16|big`` runs one group of rows (profiler
-runs); ``mx``, ``grouped`` and ``headline`` add a 1 GiB device copy that
-calibrates HBM byte counters.  ``--no-parity`` skips the oracle checks.
+runs); all but ``big`` add a 1 GiB device copy that calibrates HBM byte
+counters.  ``--no-parity`` skips the oracle checks.
 """
 
 import argparse
@@ -586,7 +586,9 @@ def main():
             sys.exit(1)
 
     if args.only == "w4a16":
-        finish(w4a16_rows(L, synth, dev, par))
+        out = w4a16_rows(L, synth, dev, par)
+        copy_calibration(out)
+        finish(out)
         return
     if args.only == "grouped":
         out = grouped_rows(L, synth, dev, par)

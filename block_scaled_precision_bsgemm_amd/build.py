@@ -19,7 +19,7 @@ OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbsgemm.so")
 
 SOURCES = ["api.cpp", "quantize.hip", "gemm_mx.hip", "gemm_mx8_exact.hip", "gemm_nvfp4.hip", "grouped.hip",
-           "w4a16.hip"]
+           "w4a16.hip", "w4a16_tile.hip"]
 COMMON_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-I" + INCLUDE, "-I" + CSRC,

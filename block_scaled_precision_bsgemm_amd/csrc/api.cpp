@@ -427,6 +427,9 @@ int w4a16_call(const char* fn, int config, int64_t m, int64_t n, int64_t k, cons
   REQUIRE_ALIGNED(c_bf16);
   if (int s = check_limits(fn, m, n, k)) return s;
   const int cfg = config >= 0 ? config : bsg::w4a16_select(m, n, k);
+  if (k % bsg::w4a16_config_k_multiple(cfg) != 0)
+    return fail(BSGEMM_ERR_UNSUPPORTED, "%s: configuration %s needs k %% %d == 0", fn, bsg::w4a16_config_name(cfg),
+                bsg::w4a16_config_k_multiple(cfg));
   if (m > bsg::w4a16_config_max_m(cfg))
     return fail(BSGEMM_ERR_RESOURCE, "%s: configuration %s takes m <= %d", fn, bsg::w4a16_config_name(cfg),
                 bsg::w4a16_config_max_m(cfg));

@@ -68,7 +68,14 @@ hipError_t launch_grouped_kragged(const KRaggedCall& call, hipStream_t stream);
 int w4a16_num_configs();
 const char* w4a16_config_name(int config);
 int w4a16_config_max_m(int config);
+// K must be a multiple of this for the configuration (32, or 256 for the tile kernels)
+int w4a16_config_k_multiple(int config);
 int w4a16_select(int64_t m, int64_t n, int64_t k);
+// The W4A16 tile kernel (w4a16_tile.hip): shape 0 = 16 x 64, 1 = 64 x 64, 2 = 128 x 128 (m x n);
+// k must be a multiple of w4_tile_k_multiple(shape) (its K per ring stage).
+int w4_tile_k_multiple(int shape);
+hipError_t launch_w4_tile(int shape, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
+                          const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream);
 hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream);
 

@@ -446,6 +446,8 @@ struct W4Config {
   bool ksplit = false;   // MFMA: one 16-row W tile per workgroup, K split over all 8 consumers
   int bps = 1;           // MFMA: K blocks per consumer per stage (one workgroup barrier each)
   int tp = 0;            // MFMA, 64-row m tile: tile groups (0: 4 groups of one tile; 2: 2 groups of two)
+  int tile = -1;         // tile kernel (w4a16_tile.hip) shape: 0 = 16 x 64, 1 = 64 x 64, 2 = 128 x 128 (m x n);
+                         // needs k % 512, 256, 128 == 0 respectively
 };
 
 constexpr W4Config kW4Configs[] = {
@@ -463,6 +465,8 @@ constexpr W4Config kW4Configs[] = {
     {"mfma_m32_nfit_b2", 32, 0, 1, false, 2}, {"mfma_m64_nfit_b2", 64, 0, 2, false, 2},
     {"mfma_m64_n64_b2", 64, 64, 2, false, 2}, {"mfma_m16_n16_ks8_b2", 16, 16, 2, true, 2},
     {"mfma_m64_nfit_t2", 64, 0, 2, false, 1, 2}, {"mfma_m64_n64_t2", 64, 64, 2, false, 1, 2},
+    {"tile_m16_n64", 16, 64, 0, false, 1, 0, 0}, {"tile_m64_n64", 64, 64, 0, false, 1, 0, 1},
+    {"tile_m128_n128", 128, 128, 0, false, 1, 0, 2},
 };
 constexpr int kW4NumConfigs = sizeof(kW4Configs) / sizeof(kW4Configs[0]);
 
@@ -475,6 +479,10 @@ const char* w4a16_config_name(int config) {
 }
 
 int w4a16_config_max_m(int config) { return kW4Configs[config].mt == 0 ? 65535 : (1 << 30); }
+
+int w4a16_config_k_multiple(int config) {
+  return kW4Configs[config].tile >= 0 ? w4_tile_k_multiple(kW4Configs[config].tile) : 32;
+}
 
 // The selector, fitted to rechecked calibration measurements (N x K in
 // {14336 x 4096, 4096 x 14336, 4096 x 4096, 1536 x 8960}) and checked on
@@ -532,6 +540,11 @@ int w4a16_select(int64_t m, int64_t n, int64_t k) {
   if (slabs * ceil_div(m, 32) <= kW4Workgroups) return 22;                   // mfma_m32_n16_ks8
   if (k >= 7168 && slabs * ceil_div(m, 16) <= 2 * kW4Workgroups) return 21;
   if (m <= 8 && m * n <= 24576) return gemv;
+  // The tile kernel's 128 x 128 tiles, once they fill a wave of workgroups:
+  // 14336 x 4096 at m = 192 and 256: 38 and 40 us against 50 and 64 us;
+  // 28672 x 4096 at m = 96 .. 256: 1.4-1.6x; with fewer tiles (14336 at
+  // m <= 128, 8192 at m <= 256) it ties or loses.
+  if (m > 64 && k % 128 == 0 && ceil_div(m, 128) * ceil_div(n, 128) >= 224) return 33;   // tile_m128_n128
   for (int mt : {16, 32, 64})
     if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) {
       if (mt == 64) return 29;                           // mfma_m64_nfit_t2
@@ -554,6 +567,7 @@ int w4a16_select(int64_t m, int64_t n, int64_t k) {
 hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                         const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream) {
   const W4Config& cf = kW4Configs[config];
+  if (cf.tile >= 0) return launch_w4_tile(cf.tile, m, n, k, x, w, ws, wts, c, stream);
   if (cf.mt == 0) {
     const int rows = cf.nb > 0 ? cf.nb : 4;   // W rows per wave
     const dim3 grid((unsigned)ceil_div(n, rows * GV_WAVES), (unsigned)m);

@@ -369,7 +369,13 @@ int bsgemm_w4a16_run(int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
  *                        BF16 MFMA kernel with that m tile and that many W
  *                        rows per workgroup (the tile width along N); "fit"
  *                        takes the narrowest width (16..64) whose grid fits
- *                        in one wave of 256 workgroups.
+ *                        in one wave of 256 workgroups; further variants of
+ *                        it differ in ring depth and K split (suffixes);
+ *   "tile_m16_n64", "tile_m64_n64", "tile_m128_n128"
+ *                        BF16 MFMA tile kernel, one workgroup per m x n
+ *                        output tile over all of K; k must be a multiple of
+ *                        512, 256 and 128 respectively, otherwise the call
+ *                        fails with BSGEMM_ERR_UNSUPPORTED.
  * bsgemm_w4a16_run runs bsgemm_w4a16_select(m, n, k), unless the environment
  * variable BSGEMM_W4A16_FORCE_CONFIG holds a configuration id or name; a
  * value that names none makes the call fail with BSGEMM_ERR_UNSUPPORTED.
@@ -386,8 +392,9 @@ const char* bsgemm_w4a16_config_name(int config);
 int bsgemm_w4a16_select(int64_t m, int64_t n, int64_t k);
 
 /* bsgemm_w4a16_run with configuration `config` forced (the environment
- * override is ignored).  BSGEMM_ERR_UNSUPPORTED for an unknown id;
- * BSGEMM_ERR_RESOURCE when m exceeds what the configuration takes. */
+ * override is ignored).  BSGEMM_ERR_UNSUPPORTED for an unknown id or a k the
+ * configuration does not take; BSGEMM_ERR_RESOURCE when m exceeds what the
+ * configuration takes. */
 int bsgemm_w4a16_run_config(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x_bf16,
                             const uint8_t* w, const uint8_t* w_scales, const float* w_tscale,
                             uint16_t* c_bf16, void* stream);

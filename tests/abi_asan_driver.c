@@ -93,7 +93,7 @@ int main(int argc, char** argv) {
 
   /* W4A16: configurations, selector, forced path */
   const int ncfg = bsgemm_w4a16_num_configs();
-  CHECK(ncfg == 31);
+  CHECK(ncfg == 34);
   for (int i = 0; i < ncfg; ++i) CHECK(bsgemm_w4a16_config_name(i) != NULL);
   CHECK(bsgemm_w4a16_config_name(ncfg) == NULL && bsgemm_w4a16_config_name(-1) == NULL);
   {
@@ -116,6 +116,7 @@ int main(int argc, char** argv) {
   CHECK(bsgemm_w4a16_run(1, 64, 64, MIS, P, P, P, P, NULL) == BSGEMM_ERR_BAD_ALIGNMENT);
   CHECK(bsgemm_w4a16_run_config(99, 1, 64, 64, P, P, P, P, P, NULL) == BSGEMM_ERR_UNSUPPORTED);
   CHECK(bsgemm_w4a16_run_config(0, 70000, 64, 64, P, P, P, P, P, NULL) == BSGEMM_ERR_RESOURCE);
+  CHECK(bsgemm_w4a16_run_config(33, 256, 64, 96, P, P, P, P, P, NULL) == BSGEMM_ERR_UNSUPPORTED);
 
   /* the error message is per thread */
   CHECK(run(BSGEMM_NVFP4, 64, 64, 64, NULL, P, P, P, P, P, P) == BSGEMM_ERR_INVALID_ARG);

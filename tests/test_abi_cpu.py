@@ -139,7 +139,7 @@ def test_grouped_ex_validation(so):
 def test_w4a16_configs_and_exhaustive_selector(so):
     n_cfg = so.bsgemm_w4a16_num_configs()
     names = [so.bsgemm_w4a16_config_name(i).decode() for i in range(n_cfg)]
-    assert n_cfg == 31 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
+    assert n_cfg == 34 and len(set(names)) == n_cfg and names[0] == "valu_gemv"
     assert so.bsgemm_w4a16_config_name(n_cfg) is None and so.bsgemm_w4a16_config_name(-1) is None
     tile = {nm: (0 if nm.startswith("valu_gemv") else int(nm.split("_")[1][1:])) for nm in names}
 
@@ -153,7 +153,8 @@ def test_w4a16_configs_and_exhaustive_selector(so):
     # rows per wave where 4 would leave few waves); then 16-row W slabs with
     # an 8-way K split while that grid fits one wave of 256 workgroups (m
     # tile 16, else 32), or two waves with the 16-row tile at k >= 7168; then
-    # the vector ALU for m <= 8 with m * n <= 24576; then a four-tile pick
+    # the vector ALU for m <= 8 with m * n <= 24576; then the 128 x 128 tile
+    # kernel for m > 64 once its grid fills a wave (224 tiles); then a four-tile pick
     # with the fit width has an m tile whose grid fits one wave with 64-row
     # slabs, and no smaller tile does (variant by m tile and K); otherwise
     # no tile fits and the pick uses 64-row slabs.
@@ -185,6 +186,9 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                 if ks:
                     assert nm == ks, (m, n, k, nm)
                     continue
+                if m > 64 and k % 128 == 0 and -(-m // 128) * -(-n // 128) >= 224:
+                    assert nm == "tile_m128_n128", (m, n, k, nm)
+                    continue
                 fits = [t for t in (16, 32, 64) if grid(m, n, t, 64) <= 256]
                 if fits:
                     sfx = {16: "_b2" if k >= 7168 else "_r2", 32: "_b2" if k >= 4096 else "", 64: "_t2"}[fits[0]]
@@ -205,7 +209,10 @@ def test_w4a16_forced_config_validation(so, monkeypatch):
     monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "no_such_tile")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     assert b"FORCE_CONFIG" in so.bsgemm_last_error()
-    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "31")
+    assert rc(31, 1, 64, 256, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED    # tile m16: k % 512
+    assert b"k % 512" in so.bsgemm_last_error()
+    assert rc(33, 1, 64, 96, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED     # tile m128: k % 128
+    monkeypatch.setenv("BSGEMM_W4A16_FORCE_CONFIG", "34")
     assert so.bsgemm_w4a16_run(1, 64, 64, P, P, P, P, P, None) == L.BSGEMM_ERR_UNSUPPORTED
     import torch
     if not torch.cuda.is_available():

@@ -734,20 +734,27 @@ def _w4_case(m, n, k, seed):
     return x, qw
 
 
-@pytest.mark.parametrize("config", range(31))
+@pytest.mark.parametrize("config", range(34))
 def test_w4a16_every_config(gpu_lib, config):
     """Each configuration, forced, on shapes it would never be chosen for:
     ragged m, n and K tails (K % 256 != 0 uses per-lane scale loads), and a
-    K long enough to wrap the deepest W register ring (8 stages of 1024)."""
+    K long enough to wrap the deepest W register ring (8 stages of 1024).
+    The tile configurations need K % 512, 256 or 128 == 0 (their K per ring
+    stage) and must refuse other K."""
     name = L.w4a16_configs()[config]
     for (m, n, k) in [(1, 300, 1024), (5, 72, 2048 + 96), (33, 129, 512), (70, 260, 4096 + 256),
-                      (9, 40, 9216 + 32)]:
+                      (9, 40, 9216 + 32), (130, 258, 2048), (200, 131, 768), (17, 70, 1536 + 512)]:
         x, qw = _w4_case(m, n, k, 1000 * config + m)
         say("w4a16 forced", name, m, n, k)
         c = out_bf16(m, n)
-        L.bsgemm_w4a16_run_config(config, dev(x.view(np.int16)), dev(qw[0]), dev(qw[1]),
-                                  dev(np.array([qw[2]], np.float32)), c=c)
+        args = (config, dev(x.view(np.int16)), dev(qw[0]), dev(qw[1]), dev(np.array([qw[2]], np.float32)))
+        if name.startswith("tile") and k % {"tile_m16_n64": 512, "tile_m64_n64": 256, "tile_m128_n128": 128}[name]:
+            with pytest.raises(L.BsgemmError, match="UNSUPPORTED"):
+                L.bsgemm_w4a16_run_config(*args, c=c)
+            continue
+        L.bsgemm_w4a16_run_config(*args, c=c)
         assert_ok(G.check(u16(c), *G.w4a16(x, *qw)), f"w4a16 {name} {m}x{n}x{k}")
+        assert not np.any(u16(c) == SENTINEL)
 
 
 def test_w4a16_environment_override(gpu_lib, monkeypatch):
