@@ -535,6 +535,15 @@ int w4a16_config_id(int mt, int nb) {
 int w4a16_select(int64_t m, int64_t n, int64_t k) {
   const int gemv = (n <= 2560 || (m <= 1 && n <= 4096)) ? 18 : 0;   // valu_gemv_w2 / valu_gemv
   if (m <= 2 || (m <= 4 && n <= 2048)) return gemv;
+  // The tile kernel's thin tiles where their grid fills about one wave of
+  // workgroups with 64-row W slabs (n >= 14336): 14336 x 4096 at m = 4 .. 16:
+  // 11.6-11.8 us against 12.1-12.9; 28672 x 4096, m = 16: 22.2 against 24.3;
+  // at m = 64: 18.8 against 20.0.  (Smaller n leaves CUs idle; there the
+  // K-split kernels below win, e.g. 4096 x 4096, m = 16: 7.1 against 10.5.)
+  if (ceil_div(n, 64) >= 224) {
+    if (m <= 16 && k % 512 == 0) return 31;                                   // tile_m16_n64
+    if (m > 48 && m <= 64 && k % 256 == 0 && ceil_div(n, 64) <= 256) return 32;   // tile_m64_n64
+  }
   const int64_t slabs = ceil_div(n, 16);
   if (slabs * ceil_div(m, 16) <= kW4Workgroups) return 21;                   // mfma_m16_n16_ks8_r4
   if (slabs * ceil_div(m, 32) <= kW4Workgroups) return 22;                   // mfma_m32_n16_ks8

@@ -17,8 +17,9 @@
 //     direct loads: per stage the tile's X [MT][2 SK bytes], W codes
 //     [NT][SK / 2 bytes] and E4M3 scales [NT][SK / 16 bytes].  NS - 1 stages
 //     are in flight while one is computed: enough bytes to cover the HBM
-//     latency for the thin tiles of small M (the stage size, not the ring
-//     depth, is what the small tiles lacked).
+//     latency for the thin tiles of small M (measured: with 64-element
+//     stages the 16 x 64 tile took 20 us at 14336 x 4096, with 512-element
+//     stages 12 us).
 //   - W codes are expanded exactly to BF16 in registers (dequant2_bf16: the
 //     product e2m1 * e4m3 has at most 6 significant bits) and the BF16 MFMA
 //     accumulates in FP32; the epilogue multiplies by s_tW.
@@ -51,15 +52,17 @@ struct TileSmem {
   uint4 dummy[64];                // target of the padding loads that keep every wave's load count equal
 };
 
-template <int MT, int NTW, int KS, int SK, int NS>
-__global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
+template <int MT, int NTW, int WN, int KS, int SK, int NS>
+__global__ __launch_bounds__(64 * WN * KS, 1) void w4_tile_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
     const float* __restrict__ Wts, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m) {
-  constexpr int NT = 4 * NTW;
-  constexpr int TW = 4 * KS;                          // waves
+  constexpr int NT = WN * NTW;
+  constexpr int TW = WN * KS;                         // waves
   constexpr int SKW = SK / KS;                        // K elements per wave per stage
-  constexpr bool BIG = NTW == 32;                     // 32x32x16 MFMAs, else 16x16x32
-  constexpr int MJ = MT / (BIG ? 32 : 16);            // m tiles per wave
+  constexpr bool BIG = NTW % 32 == 0;                 // 32x32x16 MFMAs, else 16x16x32
+  constexpr int TS = BIG ? 32 : 16;                   // MFMA tile edge
+  constexpr int WT = NTW / TS;                        // W tiles per wave
+  constexpr int MJ = MT / TS;                         // m tiles per wave
   constexpr int SUB = BIG ? SKW / 16 : SKW / 32;      // sub-steps per wave per stage
   constexpr int XNC = SK / 8, WNC = SK / 32;          // 16-byte chunks per X / W row
   constexpr int SBR = SK / 16;                        // scale bytes per W row per stage
@@ -73,8 +76,9 @@ __global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
   static_assert(XNC <= 64 && WNC <= 64, "row geometry");
   __shared__ TileSmem<MT, NT, SK, NS> sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ng = wave & 3, kh = KS == 1 ? 0 : wave >> 2;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar load selection
+  const int ng = wave % WN, kh = wave / WN;
   // the m tiles of one W slab run on one XCD, one after another
   const int lin = xcd_remap(blockIdx.x, gridDim.x);
   const int n0 = (lin / tiles_m) * NT, m0 = (lin % tiles_m) * MT;
@@ -85,59 +89,78 @@ __global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
   const rsrc4_t rs = make_rsrc4(Ws + (int64_t)n0 * KB, rows_w * KB);
   const rsrc4_t rx = make_rsrc4(X + (int64_t)m0 * K, rows_x * K * 2);
 
-  // --- direct loads of stage st (stages past KT, and padding loads, read
-  // zeros out of range)
-  auto issue = [&](int st) {
-    const int slot = st % NS;
-    const bool live = st < KT;
+  // --- direct loads of stage st into ring slot SLOT.  The per-lane part of
+  // every offset is computed once; a stage adds its K position.  Padding
+  // loads read zeros out of range into the dummy area.  Stages past KT need
+  // no masking: they land in slots that are never computed on, and past the
+  // end of a buffer the resource returns zeros.
+  int xo[XL], wo[WL], so[SL];
 #pragma unroll
-    for (int u = 0; u < XL; ++u) {                    // X: 1 KB = 64 / XNC rows per load
-      const int j = wave * XL + u;
-      constexpr int RPL = 1024 / (2 * SK);            // rows per load
-      const int row = j * RPL + lane / XNC, sl = lane % XNC;
-      const int off = live && j < XCNT ? row * K * 2 + st * SK * 2 + 16 * tswz<XNC>(row, sl) : OOB;
-      dma_x4(rx, lds_addr(j < XCNT ? &sm.x[slot][j * 64] : &sm.dummy[0]), off);
+  for (int u = 0; u < XL; ++u) {                      // X: 1 KB = 1024 / (2 SK) rows per load
+    const int j = wave * XL + u;
+    const int row = j * (1024 / (2 * SK)) + lane / XNC, sl = lane % XNC;
+    xo[u] = j < XCNT ? row * K * 2 + 16 * tswz<XNC>(row, sl) : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < WL; ++u) {                      // W codes: 1 KB = 2048 / SK rows per load
+    const int j = wave * WL + u;
+    const int row = j * (2048 / SK) + lane / WNC, sl = lane % WNC;
+    wo[u] = j < WCNT ? row * KH + 16 * tswz<WNC>(row, sl) : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < SL; ++u) {                      // scales: 256 B = 256 / SBR rows per load
+    const int j = wave * SL + u;
+    const int b = 256 * j + 4 * lane;                 // byte in the stage's scale block
+    so[u] = j < SCNT ? (b / SBR) * KB + b % SBR : -1;
+  }
+  auto issue = [&](int st, auto SLOTC) {
+    constexpr int slot = decltype(SLOTC)::value;
+#pragma unroll
+    for (int u = 0; u < XL; ++u) {
+      const bool real = wave * XL + u < XCNT;         // wave-uniform
+      dma_x4(rx, lds_addr(real ? &sm.x[slot][(wave * XL + u) * 64] : &sm.dummy[0]),
+             real ? xo[u] + st * SK * 2 : OOB);
     }
 #pragma unroll
-    for (int u = 0; u < WL; ++u) {                    // W codes: 1 KB = 64 / WNC rows per load
-      const int j = wave * WL + u;
-      constexpr int RPL = 2048 / SK;
-      const int row = j * RPL + lane / WNC, sl = lane % WNC;
-      const int off = live && j < WCNT ? row * KH + st * (SK / 2) + 16 * tswz<WNC>(row, sl) : OOB;
-      dma_x4(rw, lds_addr(j < WCNT ? &sm.w[slot][j * 64] : &sm.dummy[0]), off);
+    for (int u = 0; u < WL; ++u) {
+      const bool real = wave * WL + u < WCNT;
+      dma_x4(rw, lds_addr(real ? &sm.w[slot][(wave * WL + u) * 64] : &sm.dummy[0]),
+             real ? wo[u] + st * (SK / 2) : OOB);
     }
 #pragma unroll
-    for (int u = 0; u < SL; ++u) {                    // scales: 256 B = 256 / SBR rows per load
-      const int j = wave * SL + u;
-      const int b = 256 * j + 4 * lane;               // byte in the stage's scale block
-      const int row = b / SBR, col = b % SBR;
-      const int off = live && j < SCNT ? row * KB + st * SBR + col : OOB;
-      dma_x1(rs, lds_addr(j < SCNT ? &sm.s[slot][j * 64] : reinterpret_cast<uint32_t*>(&sm.dummy[0])), off);
+    for (int u = 0; u < SL; ++u) {
+      const bool real = wave * SL + u < SCNT;
+      dma_x1(rs, lds_addr(real ? &sm.s[slot][(wave * SL + u) * 64] : reinterpret_cast<uint32_t*>(&sm.dummy[0])),
+             real ? so[u] + st * SBR : OOB);
     }
   };
 
   // --- fragments of one stage for this lane
   const int r = BIG ? (lane & 31) : (lane & 15);
   const int g = BIG ? (lane >> 5) : (lane >> 4);      // lane half (32x32) or quarter (16x16)
-  const int wr = NTW * ng + r;                        // this lane's W row in the tile
+  // this lane's W row of W tile wt: NTW ng + TS wt + r
   constexpr int WB = BIG ? SKW / 4 : SKW / 8;         // W code bytes per lane per stage
   constexpr int WQ = WB / 16;                         // ... in 16-byte chunks
   constexpr int NSB = BIG ? SKW / 32 : SKW / 64;      // scale bytes per lane per stage
   static_assert(WB % 16 == 0 && (NSB == 1 || NSB == 2 || NSB == 4), "fragment geometry");
   struct Frag {
-    uint4 wc[WQ];
-    uint32_t sc;
+    uint4 wc[WT][WQ];
+    uint32_t sc[WT];
     uint4 xf[MJ][SUB];
   };
-  auto read_frag = [&](int st, Frag& f) {
-    const int slot = st % NS;
+  auto read_frag = [&](auto SLOTC, Frag& f) {
+    constexpr int slot = decltype(SLOTC)::value;
     const int wbyte = kh * SKW / 2 + g * WB;          // the lane's first code byte in the stage's W row
 #pragma unroll
-    for (int c = 0; c < WQ; ++c) f.wc[c] = sm.w[slot][wr * WNC + tswz<WNC>(wr, wbyte / 16 + c)];
-    const uint8_t* sb = reinterpret_cast<const uint8_t*>(&sm.s[slot][0]) + wr * SBR + kh * SKW / 16 + g * NSB;
-    if constexpr (NSB == 4) f.sc = *reinterpret_cast<const uint32_t*>(sb);
-    else if constexpr (NSB == 2) f.sc = *reinterpret_cast<const uint16_t*>(sb);
-    else f.sc = *sb;
+    for (int wt = 0; wt < WT; ++wt) {
+      const int wr = NTW * ng + TS * wt + r;
+#pragma unroll
+      for (int c = 0; c < WQ; ++c) f.wc[wt][c] = sm.w[slot][wr * WNC + tswz<WNC>(wr, wbyte / 16 + c)];
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(&sm.s[slot][0]) + wr * SBR + kh * SKW / 16 + g * NSB;
+      if constexpr (NSB == 4) f.sc[wt] = *reinterpret_cast<const uint32_t*>(sb);
+      else if constexpr (NSB == 2) f.sc[wt] = *reinterpret_cast<const uint16_t*>(sb);
+      else f.sc[wt] = *sb;
+    }
     const int xc = (kh * SKW + g * (BIG ? SKW / 2 : SKW / 4)) / 8;   // the lane's first X chunk
 #pragma unroll
     for (int j = 0; j < MJ; ++j) {
@@ -149,37 +172,49 @@ __global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
 
   constexpr int NACC = BIG ? 16 : 4;
   typedef float vacc __attribute__((ext_vector_type(NACC)));
-  vacc acc[MJ];
+  vacc acc[WT][MJ];
 #pragma unroll
-  for (int j = 0; j < MJ; ++j) acc[j] = vacc{};
+  for (int wt = 0; wt < WT; ++wt)
+#pragma unroll
+    for (int j = 0; j < MJ; ++j) acc[wt][j] = vacc{};
 
   // sub-steps [t0, t1) of a stage: the lane's scale bytes decoded exactly
   // (byte t / 2 serves sub-step t), its W codes of each sub-step expanded to
   // BF16, MJ MFMAs each
   auto compute = [&](const Frag& f, auto T0, auto T1) {
     constexpr int t0 = decltype(T0)::value, t1 = decltype(T1)::value;
-    float s[NSB], mn[NSB];
-    static_for<0, (NSB + 1) / 2>([&](auto BC) {
-      constexpr int b = 2 * decltype(BC)::value;
-      const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(f.sc, 1.0f, b >= 2);   // exact E4M3 decode
-      s[b] = v[0];
-      if constexpr (b + 1 < NSB) s[b + 1] = v[1];
-    });
+    float s[WT][NSB], mn[WT][NSB];
 #pragma unroll
-    for (int b = 0; b < NSB; ++b) mn[b] = scale_mantissa_f32(s[b]);
+    for (int wt = 0; wt < WT; ++wt) {
+      static_for<0, (NSB + 1) / 2>([&](auto BC) {
+        constexpr int b = 2 * decltype(BC)::value;
+        const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(f.sc[wt], 1.0f, b >= 2);   // exact E4M3 decode
+        s[wt][b] = v[0];
+        if constexpr (b + 1 < NSB) s[wt][b + 1] = v[1];
+      });
+#pragma unroll
+      for (int b = 0; b < NSB; ++b) mn[wt][b] = scale_mantissa_f32(s[wt][b]);
+    }
 #pragma unroll
     for (int t = t0; t < t1; ++t) {
-      const uint4& q = f.wc[t / 4];
-      const uint32_t d = (t & 3) == 0 ? q.x : (t & 3) == 1 ? q.y : (t & 3) == 2 ? q.z : q.w;
-      const v8bf wv = dequant8_bf16(d, s[t >> 1], mn[t >> 1]);
+      v8bf wv[WT];
+#pragma unroll
+      for (int wt = 0; wt < WT; ++wt) {
+        const uint4& q = f.wc[wt][t / 4];
+        const uint32_t d = (t & 3) == 0 ? q.x : (t & 3) == 1 ? q.y : (t & 3) == 2 ? q.z : q.w;
+        wv[wt] = dequant8_bf16(d, s[wt][t >> 1], mn[wt][t >> 1]);
+      }
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {
         v8bf xv;
         __builtin_memcpy(&xv, &f.xf[j][t], 16);
-        if constexpr (BIG)
-          acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv, xv, acc[j], 0, 0, 0);
-        else
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv, xv, acc[j], 0, 0, 0);
+#pragma unroll
+        for (int wt = 0; wt < WT; ++wt) {
+          if constexpr (BIG)
+            acc[wt][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[wt], xv, acc[wt][j], 0, 0, 0);
+          else
+            acc[wt][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[wt], xv, acc[wt][j], 0, 0, 0);
+        }
       }
     }
   };
@@ -187,24 +222,27 @@ __global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
   // --- pipeline: stage kt+NS-1's loads at the head of step kt; the first
   // half of the wave's sub-steps; wait for stage kt+1 and cross the barrier;
   // read its fragments under the second half.
-  Frag f[2];
-  static_for<0, NS - 1>([&](auto SC) { issue(decltype(SC)::value); });
-  wait_vm_barrier<LOADS * (NS - 2)>();
-  read_frag(0, f[0]);
-  auto step = [&](int kt, auto CURC) {
-    constexpr int CUR = decltype(CURC)::value;
-    issue(kt + NS - 1);
-    compute(f[CUR], std::integral_constant<int, 0>{}, std::integral_constant<int, SUB / 2>{});
-    wait_vm_barrier<LOADS * (NS - 2)>();     // stage kt+1 landed; stage kt's slot is free after this barrier
-    read_frag(kt + 1, f[CUR ^ 1]);
-    compute(f[CUR], std::integral_constant<int, SUB / 2>{}, std::integral_constant<int, SUB>{});
+  // Step kt: wait for stage kt and cross the barrier (after which no wave
+  // still reads stage kt-1's slot), issue stage kt+NS-1 into that slot, read
+  // stage kt's fragments and compute; NS - 1 stages stay in flight.  With two
+  // waves per SIMD the other wave covers the LDS read latency.  The loop body
+  // is NS steps, so every ring slot is a compile-time constant (static LDS
+  // offsets); steps past KT are skipped.
+  Frag f;
+  static_for<0, NS - 1>([&](auto SC) { issue(decltype(SC)::value, SC); });
+  auto step = [&](int kt, auto IC) {
+    constexpr int i = decltype(IC)::value;
+    wait_vm_barrier<LOADS * (NS - 2)>();     // stage kt landed; stage kt-1's slot is free
+    issue(kt + NS - 1, std::integral_constant<int, (i + NS - 1) % NS>{});
+    read_frag(std::integral_constant<int, i>{}, f);
+    compute(f, std::integral_constant<int, 0>{}, std::integral_constant<int, SUB>{});
   };
-  int kt = 0;
-  for (; kt + 2 <= KT; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
+  constexpr int U = NS;
+  for (int kt = 0; kt < KT; kt += U) {
+    static_for<0, U>([&](auto IC) {
+      if (kt + decltype(IC)::value < KT) step(kt + decltype(IC)::value, IC);
+    });
   }
-  if (kt < KT) step(kt, std::integral_constant<int, 0>{});
 
   // --- with two K halves, sum them through LDS (the ring is free once
   // every wave's loads, padding included, have landed and every wave is past
@@ -212,29 +250,35 @@ __global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
   if constexpr (KS == 2) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     vacc* red = reinterpret_cast<vacc*>(&sm.x[0][0]);
-    static_assert(4 * MJ * 64 * sizeof(vacc) <= sizeof(sm.x), "reduction space");
+    static_assert(WN * WT * MJ * 64 * sizeof(vacc) <= sizeof(sm.x), "reduction space");
     if (kh == 1) {
 #pragma unroll
-      for (int j = 0; j < MJ; ++j) red[(ng * MJ + j) * 64 + lane] = acc[j];
+      for (int wt = 0; wt < WT; ++wt)
+#pragma unroll
+        for (int j = 0; j < MJ; ++j) red[((ng * WT + wt) * MJ + j) * 64 + lane] = acc[wt][j];
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (kh == 1) return;
 #pragma unroll
-    for (int j = 0; j < MJ; ++j) acc[j] += red[(ng * MJ + j) * 64 + lane];
+    for (int wt = 0; wt < WT; ++wt)
+#pragma unroll
+      for (int j = 0; j < MJ; ++j) acc[wt][j] += red[((ng * WT + wt) * MJ + j) * 64 + lane];
   }
 
   // --- epilogue: x s_tW, BF16 RNE; lane holds 4 consecutive n of one m
   const float ts = *Wts;
   const bool vec = (N & 3) == 0;
 #pragma unroll
+  for (int wt = 0; wt < WT; ++wt)
+#pragma unroll
   for (int j = 0; j < MJ; ++j) {
-    const int m = m0 + (BIG ? 32 : 16) * j + r;
+    const int m = m0 + TS * j + r;
     if (m >= M) continue;
 #pragma unroll
     for (int grp = 0; grp < NACC / 4; ++grp) {
-      const int n = n0 + NTW * ng + (BIG ? 8 * grp + 4 * g : 4 * g);
-      const uint32_t lo = pack_bf16x2(acc[j][4 * grp] * ts, acc[j][4 * grp + 1] * ts);
-      const uint32_t hi = pack_bf16x2(acc[j][4 * grp + 2] * ts, acc[j][4 * grp + 3] * ts);
+      const int n = n0 + NTW * ng + TS * wt + (BIG ? 8 * grp + 4 * g : 4 * g);
+      const uint32_t lo = pack_bf16x2(acc[wt][j][4 * grp] * ts, acc[wt][j][4 * grp + 1] * ts);
+      const uint32_t hi = pack_bf16x2(acc[wt][j][4 * grp + 2] * ts, acc[wt][j][4 * grp + 3] * ts);
       uint16_t* p = C + (int64_t)m * N + n;
       if (vec && n + 4 <= N) {
         *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
@@ -248,11 +292,11 @@ __global__ __launch_bounds__(256 * KS, 1) void w4_tile_kernel(
   }
 }
 
-template <int MT, int NTW, int KS, int SK, int NS>
+template <int MT, int NTW, int WN, int KS, int SK, int NS>
 hipError_t launch_tile(int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w, const uint8_t* ws,
                        const float* wts, uint16_t* c, hipStream_t stream) {
-  const int tiles_m = (int)ceil_div(m, MT), tiles_n = (int)ceil_div(n, 4 * NTW);
-  hipLaunchKernelGGL((w4_tile_kernel<MT, NTW, KS, SK, NS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(256 * KS), 0, stream,
+  const int tiles_m = (int)ceil_div(m, MT), tiles_n = (int)ceil_div(n, WN * NTW);
+  hipLaunchKernelGGL((w4_tile_kernel<MT, NTW, WN, KS, SK, NS>), dim3((unsigned)(tiles_m * tiles_n)), dim3(64 * WN * KS), 0, stream,
                      x, w, ws, wts, c, (int)m, (int)n, (int)k, tiles_m);
   return hipGetLastError();
 }
@@ -261,19 +305,22 @@ hipError_t launch_tile(int64_t m, int64_t n, int64_t k, const uint16_t* x, const
 
 int w4_tile_k_multiple(int shape) { return shape == 0 ? 512 : shape == 1 ? 256 : 128; }
 
-// Tile shapes (m x n, K per stage, ring stages), all with 8 waves (two K
-// halves per stage):
+// Tile shapes (m x n, K per stage, ring stages), all with 8 waves (4 W row
+// groups x two K halves per stage):
 //   0: 16 x 64,   K 512, 4 stages (136 KB of LDS);
 //   1: 64 x 64,   K 256, 3 stages (123 KB);
 //   2: 128 x 128, K 128, 3 stages (123 KB).
-// Measured on 14336 x 4096, m = 256 (graph replay, cold weights): 4 waves
-// with K 64 x 4 stages and 4 waves with K 128 x 3 stages ran within 3% of
-// the 8-wave shape 2 (box-to-box spread ~10%), so only shape 2 is kept.
+// Measured on 14336 x 4096, m = 256 (graph replay, cold weights), against
+// the 8-wave shape 2: 4 waves with K 64 x 4 stages and 4 waves with K 128 x 3
+// stages within 3%; 4 waves of 2 x 2 (each two W tiles, half the LDS reads of
+// X per MFMA) within 3% (box-to-box spread ~10%).  The 128 x 128 tile takes
+// ~40 us per 128 x 128 x 4096 tile whichever of these it is, ~3x its MFMA
+// time per stage: the two stages in flight do not cover the load latency.
 hipError_t launch_w4_tile(int shape, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,
                           const uint8_t* ws, const float* wts, uint16_t* c, hipStream_t stream) {
-  if (shape == 0) return launch_tile<16, 16, 2, 512, 4>(m, n, k, x, w, ws, wts, c, stream);
-  if (shape == 1) return launch_tile<64, 16, 2, 256, 3>(m, n, k, x, w, ws, wts, c, stream);
-  return launch_tile<128, 32, 2, 128, 3>(m, n, k, x, w, ws, wts, c, stream);
+  if (shape == 0) return launch_tile<16, 16, 4, 2, 512, 4>(m, n, k, x, w, ws, wts, c, stream);
+  if (shape == 1) return launch_tile<64, 16, 4, 2, 256, 3>(m, n, k, x, w, ws, wts, c, stream);
+  return launch_tile<128, 32, 4, 2, 128, 3>(m, n, k, x, w, ws, wts, c, stream);
 }
 
 }  // namespace bsg

@@ -149,7 +149,9 @@ def test_w4a16_configs_and_exhaustive_selector(so):
     def grid(m, n, mt, nb):
         return -(-n // nb) * -(-m // mt)
     # Exhaustive over the grid, checking the selector's stated rule by its
-    # properties: the vector ALU for m <= 2 or m <= 4 with n <= 2048 (2 W
+    # properties: the vector ALU for m <= 2 or m <= 4 with n <= 2048; for
+    # n >= 14273 the thin tile kernels (m <= 16 with k % 512 == 0, and
+    # 48 < m <= 64 with k % 256 == 0 while the grid is one wave); (2 W
     # rows per wave where 4 would leave few waves); then 16-row W slabs with
     # an 8-way K split while that grid fits one wave of 256 workgroups (m
     # tile 16, else 32), or two waves with the 16-row tile at k >= 7168; then
@@ -166,6 +168,10 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                 decisions += 1
                 assert 0 <= c < n_cfg
                 nm = names[c]
+                if m > 2 and -(-n // 64) >= 224 and ((m <= 16 and k % 512 == 0) or
+                                                      (48 < m <= 64 and k % 256 == 0 and -(-n // 64) <= 256)):
+                    assert nm == ("tile_m16_n64" if m <= 16 else "tile_m64_n64"), (m, n, k, nm)
+                    continue
                 slabs = -(-n // 16)
                 if m <= 2 or (m <= 4 and n <= 2048):
                     ks = None
