@@ -289,7 +289,7 @@ int bsgemm_grouped_run(int num_groups, int64_t m_total, int64_t n, int64_t k, co
     REQUIRE_ALIGNED(w_bf16);
     REQUIRE_ALIGNED(c_bf16);
     if (int s = check_limits(fn, m_total, n, k)) return s;
-    if ((m_total / 256 + num_groups) * ((n + 255) / 256) > MAX_ROWS)
+    if (bsg::grouped_grid_blocks(num_groups, m_total, n, k) > MAX_ROWS)
       return fail(BSGEMM_ERR_RESOURCE, "%s: too many tiles", fn);
     int num_cus = 0;
     if (int s = check_device(fn, &num_cus)) return s;
@@ -336,7 +336,7 @@ int bsgemm_grouped_run_ex(int num_groups, int64_t m_total, int64_t n, int64_t k,
     if (a_rows > MAX_ROWS || a_rows * (k / 2) > MAX_ROWS)
       return fail(BSGEMM_ERR_RESOURCE, "%s: A (%lld rows of %lld code bytes) exceeds 2^31 bytes", fn,
                   (long long)a_rows, (long long)(k / 2));
-    if ((m_total / 256 + num_groups) * ((n + 255) / 256) > MAX_ROWS)
+    if (bsg::grouped_grid_blocks(num_groups, m_total, n, k) > MAX_ROWS)
       return fail(BSGEMM_ERR_RESOURCE, "%s: too many tiles", fn);
     int num_cus = 0;
     if (int s = check_device(fn, &num_cus)) return s;

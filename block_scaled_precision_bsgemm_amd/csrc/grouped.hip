@@ -38,6 +38,8 @@
 // elements [32g, 32g + 32) of the step.  Dword sp of that range feeds MFMA
 // sub-step sp at positions 8g..8g+7; its scale block is 2g + sp/2, and its W
 // chunk is 4g + sp.
+#include <algorithm>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -82,6 +84,7 @@ struct GArgs {
   const int32_t* scatter; // [M], rows of C
   const int32_t* koff;    // K-ragged mode: [G + 1] K offsets (multiples of 256); C is [G][M][N]
   int G, M, a_rows, N, K, tiles_n, tiles_m;
+  int mbig;               // ping-pong kernel: 256-row tile slots per n-tile
 };
 
 // Operand type, exact dequantisation and MFMA of the two weight types.
@@ -673,28 +676,77 @@ struct GPPSmem {
   GEpi epi;
 };
 
-template <bool F16>
-__global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
+// Tiles of the ping-pong kernel.  Group g's c rows take c / 256 full
+// 256-row tiles; a remainder of more than 128 rows takes one more 256-row
+// tile, a remainder of 1..128 rows one 128-row tile.  Padding stays under 128
+// rows per group, and the 128-row tiles, dispatched after the 256-row ones,
+// shorten the last round.
+// A 512 x 128 tile (eight waves of 64 distinct rows, so each A row expanded
+// once; 32 KB staged a step instead of 40; a 4-stage ring) was measured no
+// faster per tile: 8 groups of 2048 rows, K = 7168, N = 2048, exactly two
+// rounds of tiles: 428 us against 419 us for the 256 x 256 tile.
+__device__ __forceinline__ int pp_big_tiles(int c) { return (c >> 8) + ((c & 255) > 128 ? 1 : 0); }
+__device__ __forceinline__ int pp_small_tiles(int c) { return ((c & 255) != 0 && (c & 255) <= 128) ? 1 : 0; }
+
+// find_tile for the ping-pong kernel's two tile sizes: tile `mt` among the
+// 256-row tiles (SMALL false) or among the 128-row tiles (SMALL true), counted
+// group by group.  Run by wave 0; writes {group, first row, end row} to
+// `info`, or group = -1 when mt is past the last tile of that size.
+template <bool SMALL>
+__device__ void find_tile_pp(const int32_t* __restrict__ off, int G, int mt, int lane, int* info) {
+  int base = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    int tiles = 0, lo = 0, hi = 0, c = 0;
+    if (g < G) {
+      lo = off[g];
+      hi = off[g + 1];
+      c = max(hi - lo, 0);
+      tiles = SMALL ? pp_small_tiles(c) : pp_big_tiles(c);
+    }
+    int incl = tiles;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const int excl = incl - tiles;
+    if (g < G && mt >= base + excl && mt < base + incl) {
+      const int local = mt - base - excl;
+      info[0] = g;
+      if (SMALL) {
+        info[1] = lo + (c & ~255);
+        info[2] = hi;
+      } else {
+        info[1] = lo + local * 256;
+        info[2] = lo + min((local + 1) * 256, c);
+      }
+    }
+    base += __shfl(incl, 63);
+    if (mt < base) return;
+  }
+  if (lane == 0) info[0] = -1;
+}
+
+// One tile of the ping-pong kernel.  MI = 2: 256 rows, wave (pg, wq) owns
+// rows [64 wq, 64 wq + 64); MI = 1: 128 rows, wave (pg, wq) owns rows
+// [32 wq, 32 wq + 32).  Either way its columns are [128 pg, 128 pg + 128).
+// The loads are those of the 256-row tile in both cases: for a 128-row tile
+// rows 128..255 lie past rows_a and land in LDS as zeros without touching
+// memory.
+__shared__ GPPSmem pp_sm;
+
+template <bool F16, int MI>
+__device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1, int nt) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   using GM = GMath<F16>;
   using VT = typename GM::vec;
   constexpr int U = 4;                       // steps per 16-byte scale load
-  __shared__ GPPSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int TM = 128 * MI;               // tile rows
   const int pg = wave >> 2, wq = wave & 3;
-  const int M = p.M, N = p.N, K = p.K;
+  const int N = p.N, K = p.K;
   const int KH = K / 2, KB = K / 16;
-  // tile order as in the ring kernel (n-major, XCD-contiguous)
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int mtiles = gridDim.x / p.tiles_n;
-  const int nt = t / mtiles;
-  const int mt = t - nt * mtiles;
-  if (wave == 0) find_tile(p.off, p.G, mt, lane, sm.tile_info);
-  __syncthreads();
-  const int grp = sm.tile_info[0];
-  if (grp < 0) return;                        // uniform over the workgroup
-  const int r0 = min(max(sm.tile_info[1], 0), M);
-  const int r1 = min(max(sm.tile_info[2], r0), M);
   const int n0 = nt * BN;
   const int KT = K / BK;                      // a multiple of U
   const int rows_a = r1 - r0, rows_w = min(N - n0, BN);
@@ -702,7 +754,7 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
   const rsrc4_t ra = make_rsrc4(gat ? p.A : p.A + (int64_t)r0 * KH, (gat ? p.a_rows : rows_a) * KH);
   const rsrc4_t rsa = make_rsrc4(gat ? p.As : p.As + (int64_t)r0 * KB, (gat ? p.a_rows : rows_a) * KB);
   const rsrc4_t rw = make_rsrc4(p.W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
-  fill_epi(p, r0, rows_a, tid, sm.epi);   // visible after the prologue's barrier
+  fill_epi(p, r0, rows_a, tid, pp_sm.epi);   // visible after the prologue's barrier
 
   // Load geometry.  Wave w's A load covers rows 32 w .. +31 (two lanes per
   // row); its W load u (0..3) covers rows 8 (4 w + u) .. +7 (eight lanes per
@@ -724,12 +776,12 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
     const bool live = st < KT;
     if constexpr (decltype(PG)::value == 0 && decltype(WITH_SCALES)::value) {
       const int sbuf = (st / U) % GR_SBUF;
-      dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wq * 4]), (live && s_off >= 0) ? s_off + (st / U) * 16 : OOB);
+      dma_x4(rsa, lds_addr(&pp_sm.as[sbuf][64 * wq * 4]), (live && s_off >= 0) ? s_off + (st / U) * 16 : OOB);
     }
-    dma_x4(ra, lds_addr(&sm.a[slot][64 * wave]), (live && a_off >= 0) ? a_off + st * AROWB : OOB);
+    dma_x4(ra, lds_addr(&pp_sm.a[slot][64 * wave]), (live && a_off >= 0) ? a_off + st * AROWB : OOB);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      dma_x4(rw, lds_addr(&sm.w[slot][64 * (4 * wave + u)]),
+      dma_x4(rw, lds_addr(&pp_sm.w[slot][64 * (4 * wave + u)]),
              live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
   };
   // loads per wave for stage st (st % U == s_mod): the scale load joins
@@ -737,8 +789,8 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
   auto loads_of = [](int pg_, int s_mod) { return 5 + ((pg_ == 0 && s_mod == 0) ? 1 : 0); };
 
   const int r = lane & 31, g = lane >> 5;
-  VT av[4][2];
-  // This wave's 2 A row fragments of stage st (st % U == IN), expanded for
+  VT av[4][MI];
+  // This wave's MI A row fragments of stage st (st % U == IN), expanded for
   // all four K16 sub-steps.  Sub-step sp pairs lane half g with K
   // 32 g + 8 sp .. + 7, whose scale is byte 2 g + sp / 2 of the row's 4 scale
   // bytes for the step.
@@ -746,10 +798,10 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
     constexpr int IN = decltype(INC)::value;
     const int slot = st % GR_NS, sbuf = (st / U) % GR_SBUF;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = wq * 64 + i * 32 + r;
-      const uint4 c = sm.a[slot][aswz(row, g)];
-      const uint32_t word = sm.as[sbuf][row * 4 + IN] >> (16 * g);
+    for (int i = 0; i < MI; ++i) {
+      const int row = wq * 32 * MI + i * 32 + r;
+      const uint4 c = pp_sm.a[slot][aswz(row, g)];
+      const uint32_t word = pp_sm.as[sbuf][row * 4 + IN] >> (16 * g);
       const v2f sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);   // exact E4M3
       const uint32_t m0 = GM::mant(sv[0]), m1 = GM::mant(sv[1]);
       av[0][i] = GM::dq8(c.x, sv[0], m0);
@@ -763,19 +815,19 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
     const int slot = st % GR_NS;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint4 q = sm.w[slot][wswz(pg * 128 + j * 32 + r, 4 * g + sp)];
+      const uint4 q = pp_sm.w[slot][wswz(pg * 128 + j * 32 + r, 4 * g + sp)];
       __builtin_memcpy(&bv[j], &q, 16);
     }
   };
 
-  v16f acc[2][4];
+  v16f acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
   auto mfmas = [&](const VT* a, const VT* b) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = GM::mfma(a[i], b[j], acc[i][j]);
   };
@@ -787,8 +839,8 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
     read_w(k, 0, bv0);
     read_w(k, 1, bv1);
   };
-  // MFMA phase of step k: the loads of stage k + 2, then the 32 MFMAs, with
-  // the W fragments of sub-steps 2-3 read under those of sub-steps 0-1.
+  // MFMA phase of step k: the loads of stage k + 2, then the MFMAs, with the
+  // W fragments of sub-steps 2-3 read under those of sub-steps 0-1.
   auto mfma_phase = [&](int k, auto PG, auto WS) {
     issue(k + 2, PG, WS);
     __builtin_amdgcn_sched_barrier(0);
@@ -853,14 +905,15 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
 
-  // Epilogue as in the ring kernel, for this wave's 64 x 128 block.
+  // Epilogue as in the ring kernel, for this wave's (32 MI) x 128 block.
   const float alpha = *p.Ats;
   const bool plain = !p.bias && !p.gamma && !p.scatter;
   const int cn0 = n0 + pg * 128;
-  if (plain && r0 + BM <= r1 && n0 + BN <= N) {
-    uint16_t* cw = p.C + (int64_t)(r0 + wq * 64 + g * 4) * N + cn0 + r;
+  const int wr0 = wq * 32 * MI;               // the wave's first tile row
+  if (plain && r0 + TM <= r1 && n0 + BN <= N) {
+    uint16_t* cw = p.C + (int64_t)(r0 + wr0 + g * 4) * N + cn0 + r;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -873,18 +926,46 @@ __global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
       const int col = cn0 + j * 32 + r;
       const float b = (p.bias && col < N) ? p.bias[(int64_t)grp * N + col] : 0.0f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int lr = wq * 64 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          const int dst = sm.epi.dst[lr];
+          const int lr = wr0 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
+          const int dst = pp_sm.epi.dst[lr];
           float y = acc[i][j][v] * alpha;
           if (p.bias) y += b;
-          if (p.gamma) y *= sm.epi.gamma[lr];
+          if (p.gamma) y *= pp_sm.epi.gamma[lr];
           if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
         }
     }
   }
+}
+
+// Grid: tiles_n n-tiles x (mbig 256-row slots, then min(G, M) 128-row slots),
+// n-major after xcd_remap, so each XCD takes a contiguous run of slots: the
+// 256-row tiles of an n-tile column first, then its 128-row tiles.  Slots
+// past the real tile count exit at once.
+template <bool F16>
+__global__ __launch_bounds__(512, 1) void grouped_pp_kernel(const GArgs p) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int mslots = gridDim.x / p.tiles_n;
+  const int nt = t / mslots;
+  const int slot = t - nt * mslots;
+  const bool small = slot >= p.mbig;
+  if (wave == 0) {
+    if (small) find_tile_pp<true>(p.off, p.G, slot - p.mbig, lane, pp_sm.tile_info);
+    else find_tile_pp<false>(p.off, p.G, slot, lane, pp_sm.tile_info);
+  }
+  __syncthreads();
+  const int grp = pp_sm.tile_info[0];
+  if (grp < 0) return;                        // uniform over the workgroup
+  // Offsets are a documented precondition; clamping keeps even malformed
+  // ones inside the A and C buffers, and a tile within its row count.
+  const int r0 = min(max(pp_sm.tile_info[1], 0), p.M);
+  const int r1 = min(max(pp_sm.tile_info[2], r0), min(p.M, r0 + (small ? 128 : 256)));
+  if (small) pp_tile<F16, 1>(p, grp, r0, r1, nt);
+  else pp_tile<F16, 2>(p, grp, r0, r1, nt);
 }
 
 }  // namespace
@@ -904,14 +985,27 @@ hipError_t launch_grouped_kragged(const KRaggedCall& c, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// 256-row tile slots of the ping-pong kernel: sum_g big_tiles(c_g) <=
+// sum_g (c_g + 127) / 256 <= (m_total + 127 G) / 256.
+static int64_t pp_big_slots(int64_t m_total, int num_groups) { return (m_total + 127 * (int64_t)num_groups) / 256; }
+
+// 128-row tile slots: at most one per non-empty group.
+static int64_t pp_small_slots(int64_t m_total, int num_groups) { return std::min<int64_t>(num_groups, m_total); }
+
+int64_t grouped_grid_blocks(int num_groups, int64_t m_total, int64_t n, int64_t k) {
+  const int64_t tiles_n = ceil_div(n, BN);
+  if (k % 256 == 0 && k > 0) return (pp_big_slots(m_total, num_groups) + pp_small_slots(m_total, num_groups)) * tiles_n;
+  return (m_total / BM + num_groups) * tiles_n;   // >= sum_g ceil(c_g / BM)
+}
+
 hipError_t launch_grouped(const GroupedCall& c, hipStream_t stream) {
   GArgs p{};
   p.A = c.a; p.As = c.as; p.Ats = c.ats; p.off = c.offsets; p.W = c.w; p.C = c.c;
   p.bias = c.bias; p.gamma = c.gamma; p.gather = c.gather; p.scatter = c.scatter;
   p.G = c.num_groups; p.M = (int)c.m_total; p.a_rows = (int)c.a_rows; p.N = (int)c.n; p.K = (int)c.k;
   p.tiles_n = (int)ceil_div(c.n, BN);
-  const int64_t mtiles_max = c.m_total / BM + c.num_groups;   // >= sum_g ceil(c_g / BM)
-  const dim3 grid((unsigned)(mtiles_max * p.tiles_n));
+  p.mbig = (int)pp_big_slots(c.m_total, c.num_groups);
+  const dim3 grid((unsigned)grouped_grid_blocks(c.num_groups, c.m_total, c.n, c.k));
   const int64_t k = c.k;
   if (c.w_f16) {
     if (k % 256 == 0 && k > 0)

@@ -48,6 +48,9 @@ struct GroupedCall {
   uint16_t* c;
 };
 hipError_t launch_grouped(const GroupedCall& call, hipStream_t stream);
+// Workgroups launch_grouped launches for these sizes (an upper bound on the
+// tile count; surplus workgroups exit at once).
+int64_t grouped_grid_blocks(int num_groups, int64_t m_total, int64_t n, int64_t k);
 
 // One K-ragged (inner-expert) grouped launch: k % 256 == 0; k_offsets on the
 // device; c is [num_groups][m][n].

@@ -478,6 +478,22 @@ def test_grouped_shapes(gpu_lib, counts, n, k):
     assert_ok(G.check(c, *G.grouped_nvfp4_bf16(*qa, off, w)), f"grouped {counts} n={n} k={k}")
 
 
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+def test_grouped_tile_sizes(gpu_lib, w_dtype):
+    """Group sizes around the ping-pong kernel's two tile sizes: remainders of
+    0, 1, 127, 128 (one 128-row tile), 129, 255 (one more 256-row tile), with
+    every routing and epilogue variant and without."""
+    counts = [0, 1, 127, 128, 129, 255, 256, 257, 383, 384, 385, 640, 0, 513]
+    n, k = 260, 512
+    m = sum(counts)
+    qa, off, w, v = _variant_case(counts, n, k, 900, w_dtype, a_rows=m)
+    for use in ((), ALL):
+        say("grouped tile sizes", w_dtype, use)
+        c = _gpu_grouped_ex(qa, off, w, k, w_dtype, v, use, m)
+        assert_ok(G.check(c, *_ref_ex(qa, off, w, w_dtype, v, use)), f"grouped tile sizes {w_dtype} {use}")
+        assert not np.any(c == SENTINEL)
+
+
 def test_grouped_config_sampled(gpu_lib):
     """32 groups, Dirichlet(0.5) counts over 16384 rows, K=7168, N=2048.
     GPU quantize + grouped GEMM; sampled rows: first/last row of every
