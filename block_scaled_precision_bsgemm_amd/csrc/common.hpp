@@ -102,6 +102,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Two FP32 values -> packed BF16 pair (lo in bits 15:0) by gfx950's pair
+// conversion (v_cvt_pk_bf16_f32): round to nearest even, the same bits as
+// pack_bf16x2 for finite inputs, in one instruction.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+  const v2bf16 r = __builtin_convertvector((v2f){lo, hi}, v2bf16);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }

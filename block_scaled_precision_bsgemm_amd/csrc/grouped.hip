@@ -361,10 +361,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
     // the 8 XCDs (workgroup b runs on XCD b % 8), so each XCD gets every
     // group's n-tiles in turn: with contiguous blocks of units, the XCD that
     // drew the longest K slices set the kernel time (up to 2.7x its share
-    // for Dirichlet-sized experts).  The grid is padded to whole rounds of 8
+    // for Dirichlet-sized experts).  XCD x starts x/8 of the way along its
+    // sequence, so the XCDs do not all reach their epilogues together (equal
+    // K slices: 669 -> 643 us).  The grid is padded to whole rounds of 8
     // units; padding workgroups exit here.
     const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
-    const int u = (i / p.tiles_m) * 8 + x;
+    const int upx = (gridDim.x >> 3) / p.tiles_m;   // units per XCD
+    const int u = (((i / p.tiles_m) + x * upx / 8) % upx) * 8 + x;
     if (u >= p.G * p.tiles_n) return;        // uniform over the workgroup
     grp = u / p.tiles_n;
     nt = u - grp * p.tiles_n;
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = GM::mfma(av[i], bv[j], acc[i][j]);
+      for (int j = 0; j < 8; ++j) acc[i][j] = GM::mfma(bv[j], av[i], acc[i][j]);   // W first: see the epilogue
   };
   auto interleave = [] {
 #pragma unroll
@@ -615,37 +618,84 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
     }
   }
 
-  // Epilogue: C rows r0..r1 of this group, scaled by the tensor scale.
-  // Plain full tiles store rows in place without per-element checks; the
-  // ragged edge and every variant go through the tile's LDS row table.
+  // Epilogue: C rows r0..r1 of this group (row table in LDS: ragged edge,
+  // scatter), y = (s_t * acc + bias) * gamma rounded once to BF16.  With W
+  // as the MFMA's first operand, lane (r, g) holds tile row 64 wave + 32 i + r
+  // and, for q = v / 4, the four consecutive columns 32 j + 8 q + 4 g + 0..3.
+  // Each wave passes its 64 x 256 block through a private 16 KB of the ring's
+  // LDS in two halves of 128 columns: the lanes write their 4-column pieces
+  // as BF16, then read back 16-byte row chunks and store whole 256-byte row
+  // segments.  Storing from the MFMA layout directly takes one 2-byte store
+  // per element: 784 us against 744 us for the 32-expert K-ragged problem.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
+  __syncthreads();                                   // every wave is done with the ring
   const float alpha = *p.Ats;
-  const bool plain = !p.bias && !p.gamma && !p.scatter;
-  if (plain && r0 + BM <= r1 && n0 + BN <= N) {
-    uint16_t* cw = Cb + (int64_t)(r0 + wave * 64 + g * 4) * N + n0 + r;
+  uint4* const eb = &sm.w[0][0] + wave * (64 * 16);  // 64 rows x 16 chunks of 16 bytes
+  const bool vec_ok = (N & 7) == 0;                  // 16-byte aligned row chunks
+  // Phase 1 of half h: the wave's values as BF16 into its LDS rows; the
+  // variants are decided once per launch, outside the element loops.
+  auto to_lds = [&](int h, auto BIAS, auto GAMMA) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int row = 32 * i + r;                    // wave-local row
+      const float gm = decltype(GAMMA)::value ? sm.epi.gamma[64 * wave + row] : 1.0f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int jj = 0; jj < 4; ++jj) {
+        const int j = 4 * h + jj;
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] =
-              (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
-  } else {
+        for (int q = 0; q < 4; ++q) {
+          float y[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int col = n0 + j * 32 + r;
-      const float b = (p.bias && col < N) ? p.bias[(int64_t)grp * N + col] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int lr = wave * 64 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          const int dst = sm.epi.dst[lr];
-          float y = acc[i][j][v] * alpha;
-          if (p.bias) y += b;
-          if (p.gamma) y *= sm.epi.gamma[lr];
-          if (dst >= 0 && col < N) Cb[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
+          for (int e = 0; e < 4; ++e) {
+            y[e] = acc[i][j][4 * q + e] * alpha;
+            if constexpr (decltype(BIAS)::value) {
+              const int col = n0 + 32 * j + 8 * q + 4 * g + e;
+              y[e] += col < N ? p.bias[(int64_t)grp * N + col] : 0.0f;
+            }
+            if constexpr (decltype(GAMMA)::value) y[e] *= gm;
+          }
+          const int chunk = 4 * jj + q;
+          uint2* dstp = reinterpret_cast<uint2*>(eb + row * 16 + (chunk ^ (row & 15))) + g;
+          *dstp = make_uint2(cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3]));
         }
+      }
+    }
+  };
+  const bool has_bias = !KRAG && p.bias, has_gamma = !KRAG && p.gamma;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (has_bias && has_gamma) to_lds(h, std::true_type{}, std::true_type{});
+    else if (has_bias) to_lds(h, std::true_type{}, std::false_type{});
+    else if (has_gamma) to_lds(h, std::false_type{}, std::true_type{});
+    else to_lds(h, std::false_type{}, std::false_type{});
+    // All 16 row chunks and destination rows of the half are read before the
+    // first store, so the LDS latency is paid once, not once per store.
+    const int cbase = n0 + 128 * h + 8 * (lane & 15);
+    uint4 vals[16];
+    int dsts[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int row = 4 * t + (lane >> 4);
+      const int c = lane & 15;
+      vals[t] = eb[row * 16 + (c ^ (row & 15))];
+      dsts[t] = sm.epi.dst[64 * wave + row];
+    }
+    if (cbase < N) {
+      if (vec_ok) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t)
+          if (dsts[t] >= 0) *reinterpret_cast<uint4*>(Cb + (int64_t)dsts[t] * N + cbase) = vals[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          if (dsts[t] < 0) continue;
+          uint16_t* cp = Cb + (int64_t)dsts[t] * N + cbase;
+          const uint32_t wd[4] = {vals[t].x, vals[t].y, vals[t].z, vals[t].w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (cbase + e < N) cp[e] = (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
+        }
+      }
     }
   }
 }
