@@ -247,6 +247,66 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
+// ------------------------------------------------------------------ epilogue
+
+// Stores one wave's 128 x 128 block of FP32 accumulators to C as BF16 through
+// LDS.  acc[i][j] is the 32 x 32 MFMA tile (i, j) computed with the column
+// operand first, so lane (r, g) holds row 32 i + r and, at acc[i][j][4 q + e],
+// column 32 j + 8 q + 4 g + e.  The lanes write their 4-column pieces (scaled
+// by alpha when SCALE) as BF16 pairs into the wave's private 32 KB at `eb`
+// (128 rows of 256 bytes, 16-byte chunks swizzled by the row), then read
+// back 16-byte row chunks and store 4 whole 256-byte row segments per
+// instruction, instead of one 2-byte store per element.  C block origin
+// (row0, col0); rows >= M and columns >= N are not stored.  The caller makes
+// sure nothing else reads or writes `eb` meanwhile.
+template <bool SCALE>
+__device__ __forceinline__ void store_block128_bf16(const v16f (&acc)[4][4], uint4* eb, uint16_t* C, int M, int N,
+                                                    int row0, int col0, float alpha) {
+  const int lane = threadIdx.x & 63, r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 32 * i + r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = SCALE ? acc[i][j][4 * q + e] * alpha : acc[i][j][4 * q + e];
+        const int chunk = 4 * j + q;
+        uint2* d = reinterpret_cast<uint2*>(eb + row * 16 + (chunk ^ (row & 15))) + g;
+        *d = make_uint2(cvt_pk_bf16(y[0], y[1]), cvt_pk_bf16(y[2], y[3]));
+      }
+  }
+  const int c = lane & 15;
+  const int col = col0 + 8 * c;
+  const bool full = (N & 7) == 0 && col + 8 <= N;   // 16-byte aligned and inside C
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    // 16 row chunks read as a batch: the LDS latency is paid once per batch
+    uint4 v[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int row = 4 * (16 * b + t) + (lane >> 4);
+      v[t] = eb[row * 16 + (c ^ (row & 15))];
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int grow = row0 + 4 * (16 * b + t) + (lane >> 4);
+      if (grow >= M || col >= N) continue;
+      uint16_t* cp = C + (int64_t)grow * N + col;
+      if (full) {
+        *reinterpret_cast<uint4*>(cp) = v[t];
+      } else {
+        const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (col + e < N) cp[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------- tile order
 
 // Output-tile order for large GEMM grids (tiles_m and tiles_n multiples of

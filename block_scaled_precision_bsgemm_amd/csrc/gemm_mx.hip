@@ -399,6 +399,17 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  // MFMA of A fragment a and B fragment b (scale byte select sel).  WFIRST:
+  // the B operand goes first, giving the row-chunk epilogue its layout.  The
+  // FP4 ring with 4-byte scale batches keeps A first: with B first the
+  // compiler spilled ~200 VGPRs in its main loop.
+  constexpr bool WFIRST = !(FP4 && SB == 4);
+  auto mfma_ab = [](const v8i& a, const v8i& b, const v16f& c, auto sel_c, int sa, int sb) {
+    constexpr int fmt = mfma_fmt<FP4>();
+    constexpr int sel = decltype(sel_c)::value;
+    if constexpr (WFIRST) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, fmt, fmt, sel, sb, sel, sa);
+    else return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fmt, fmt, sel, sa, sel, sb);
+  };
   // MFMAs of tile rows i0, i0 + 1.  OPSEL: byte of the (shifted) scale dwords
   // that holds this stage's FP8 scale.  FP4 runs its two K64 halves in turn
   // (all 8 tiles of the first, then the second), so the two MFMAs into one
@@ -412,9 +423,8 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
         for (int i = i0; i < i0 + 2; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j], fmt, fmt,
-                2 * s, f.sa[i], 2 * s, f.sb[j]);
+            acc[i][j] = mfma_ab(frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j],
+                                std::integral_constant<int, 2 * s>{}, f.sa[i], f.sb[j]);
       });
     } else {
       constexpr int sel = decltype(OPSEL)::value;
@@ -422,8 +432,7 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
       for (int i = i0; i < i0 + 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], fmt, fmt, sel,
-                                                                      f.sa[i], sel, f.sb[j]);
+          acc[i][j] = mfma_ab(f.a[i], f.b[j], acc[i][j], std::integral_constant<int, sel>{}, f.sa[i], f.sb[j]);
     }
   };
 
@@ -433,13 +442,11 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
     constexpr int fmt = mfma_fmt<FP4>();
     if constexpr (FP4) {
       constexpr int s = decltype(SC)::value;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j], fmt, fmt, 2 * s, f.sa[i],
-          2 * s, f.sb[j]);
+      acc[i][j] = mfma_ab(frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j],
+                          std::integral_constant<int, 2 * s>{}, f.sa[i], f.sb[j]);
     } else {
       constexpr int sel = decltype(OPSEL)::value;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], fmt, fmt, sel, f.sa[i],
-                                                                  sel, f.sb[j]);
+      acc[i][j] = mfma_ab(f.a[i], f.b[j], acc[i][j], std::integral_constant<int, sel>{}, f.sa[i], f.sb[j]);
     }
   };
 
@@ -528,18 +535,17 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
     });
   }
 
-  // Epilogue.  Tiles wholly inside C (all but the ragged edge) store without
-  // per-element bounds checks; each store writes two 64-byte row segments.
-  uint16_t* cw = C + (int64_t)(m0 + wm * 128 + g * 4) * N + n0 + wn * 128 + r;
-  if (m0 + BM <= M && n0 + BN <= N) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+  // Epilogue.  The MFMAs take the B (column) operand first, so each lane
+  // holds 4 consecutive columns per accumulator quad; the block goes out as
+  // BF16 through the (now idle) A and B rings: 16-byte row-chunk stores
+  // instead of one 2-byte store per element.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
+  __syncthreads();                                   // every wave is done with the rings
+  static_assert(sizeof(sm.a) + sizeof(sm.b) >= 4 * 128 * 256, "epilogue staging needs 32 KB per wave");
+  if constexpr (WFIRST) {
+    store_block128_bf16<false>(acc, &sm.a[0][0] + wave * (128 * 16), C, M, N, m0 + wm * 128, n0 + wn * 128, 1.0f);
   } else {
+    // A first: lane (r, g) holds column 32 j + r, rows 32 i + 8 (v / 4) + 4 g + v % 4
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
