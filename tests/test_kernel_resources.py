@@ -1,0 +1,65 @@
+"""Register and LDS budgets of the gfx950 kernels (CPU only: hipcc's
+resource-usage remarks, no GPU).
+
+A VGPR spill in a main loop goes to scratch memory and costs more than any
+scheduling choice, and it appears silently when a change shifts the
+compiler's register allocation.  Every kernel must fit the CU's LDS, and
+none may spill except the ones listed, whose spills sit outside their main
+loops (epilogue address registers) or in a fallback path."""
+
+import os
+import re
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from block_scaled_precision_bsgemm_amd import build as B
+
+LDS_BYTES = 160 * 1024
+# kernel-name fragment -> most VGPR spills accepted
+SPILL_ALLOWED = {
+    "grouped_ring_kernel": 2,      # the row-chunk epilogue's addresses, after the main loop
+    "mx_gemm_kernelILb1E": 40,     # register-staged MXFP4 fallback (K % 128 != 0)
+}
+
+
+def _hipcc():
+    path = "/opt/rocm/bin/hipcc"
+    return path if os.path.exists(path) else shutil.which("hipcc")
+
+
+def _resources(src):
+    cmd = [_hipcc()] + [f for f in B.COMMON_FLAGS if f != "-Wall"] + B.EXTRA_FLAGS.get(src, []) + \
+        (["-x", "hip"] if src.endswith(".cpp") else []) + \
+        ["--cuda-device-only", "-c", os.path.join(B.CSRC, src), "-o", os.devnull,
+         "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    kernels, cur = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = kernels.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(VGPRs Spill|AGPRs|VGPRs|LDS Size \[bytes/block\]): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1)] = int(m.group(2))
+    return kernels
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc is not installed")
+def test_kernel_register_and_lds_budgets():
+    srcs = [s for s in B.SOURCES if s.endswith(".hip")]
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
+        per_src = dict(zip(srcs, ex.map(_resources, srcs)))
+    seen = 0
+    for src, kernels in per_src.items():
+        for name, res in kernels.items():
+            seen += 1
+            assert res.get("LDS Size [bytes/block]", 0) <= LDS_BYTES, (src, name, res)
+            assert res.get("VGPRs", 0) + res.get("AGPRs", 0) <= 512, (src, name, res)
+            cap = next((v for k, v in SPILL_ALLOWED.items() if k in name), 0)
+            assert res.get("VGPRs Spill", 0) <= cap, f"{src}: {name} spills {res.get('VGPRs Spill')} VGPRs"
+    assert seen >= 20   # every kernel of the library was reported
