@@ -229,7 +229,7 @@ __global__ __launch_bounds__(NT, 1) void mx8x_ring_kernel(
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv[j], av[i], acc[i][j], 0, 0, 0);   // B first
   };
   // 16 groups of 1 MFMA, NV VALU and NL LDS reads
   auto interleave = [](auto NV, auto NL) {
@@ -318,29 +318,12 @@ __global__ __launch_bounds__(NT, 1) void mx8x_ring_kernel(
     });
   }
 
-  // Epilogue: BF16 RNE; interior tiles store without per-element checks.
-  uint16_t* cw = C + (int64_t)(m0 + wm * 128 + g * 4) * N + n0 + wn * 128 + r;
-  if (m0 + BM <= M && n0 + BN <= N) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 128 + j * 32 + r;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-          if (row < M && col < N) C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
-        }
-      }
-  }
+  // Epilogue: BF16 through the (now idle) A and B rings as whole row
+  // segments (the MFMAs took the B operand first).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
+  __syncthreads();                                   // every wave is done with the rings
+  static_assert(sizeof(sm.a) + sizeof(sm.b) >= 4 * 128 * 256, "epilogue staging needs 32 KB per wave");
+  store_block128_bf16<false>(acc, &sm.a[0][0] + wave * (128 * 16), C, M, N, m0 + wm * 128, n0 + wn * 128, 1.0f);
 }
 
 // ---------------------------------------------------------------------------

@@ -440,7 +440,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     for (int i = i0; i < i0 + 2; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[i], bv[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bv[j], av[i], acc[i][j], 0, 0, 0);   // B first
   };
   // 8 groups of 1 MFMA, NV VALU and NL LDS reads
   auto interleave = [](auto NV, auto NL) {
@@ -552,19 +552,14 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     step(kt + 1, std::integral_constant<int, 1>{});
   }
 
+  // Epilogue: x s_tA s_tB, BF16, through the (now idle) A and B rings as
+  // whole row segments (the MFMAs took the B operand first, so each lane holds
+  // 4 consecutive columns per accumulator quad).
   const float alpha = __fmul_rn(*Ats, *Bts);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = n0 + wn * 128 + j * 32 + r;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * 128 + i * 32 + (v >> 2) * 8 + g * 4 + (v & 3);
-        if (row < M && col < N)
-          C[(int64_t)row * N + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
-      }
-    }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
+  __syncthreads();                                   // every wave is done with the rings
+  static_assert(sizeof(sm.a) + sizeof(sm.b) >= 4 * 128 * 256, "epilogue staging needs 32 KB per wave");
+  store_block128_bf16<true>(acc, &sm.a[0][0] + wave * (128 * 16), C, M, N, m0 + wm * 128, n0 + wn * 128, alpha);
 }
 
 

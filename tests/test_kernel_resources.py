@@ -21,6 +21,7 @@ LDS_BYTES = 160 * 1024
 # kernel-name fragment -> most VGPR spills accepted
 SPILL_ALLOWED = {
     "grouped_ring_kernel": 2,      # the row-chunk epilogue's addresses, after the main loop
+    "nvfp4_gemm_ring_kernel": 1,   # likewise
     "mx_gemm_kernelILb1E": 40,     # register-staged MXFP4 fallback (K % 128 != 0)
 }
 
