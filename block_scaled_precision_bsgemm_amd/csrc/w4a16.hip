@@ -554,11 +554,17 @@ int w4a16_select(int64_t m, int64_t n, int64_t k) {
   // 28672 x 4096 at m = 96 .. 256: 1.4-1.6x; with fewer tiles (14336 at
   // m <= 128, 8192 at m <= 256) it ties or loses.
   if (m > 64 && k % 128 == 0 && ceil_div(m, 128) * ceil_div(n, 128) >= 224) return 33;   // tile_m128_n128
+  // Where the four-tile kernel would take 16-row m tiles, the 16 x 64 tile
+  // kernel is faster whenever it takes the K (the calibration's 278 cells:
+  // 22 cells 3-19% faster, e.g. 2048 x 6144, m = 128: 1.19x; 2 cells 3-4%
+  // slower); likewise its 64 x 64 tile in place of the 64-row four-tile
+  // kernel from n = 6144.
   for (int mt : {16, 32, 64})
     if (ceil_div(n, 64) * ceil_div(m, mt) <= kW4Workgroups) {
-      if (mt == 64) return 29;                           // mfma_m64_nfit_t2
-      if (mt == 32) return k >= 4096 ? 25 : 5;           // mfma_m32_nfit_b2 / mfma_m32_nfit
-      return k >= 7168 ? 23 : 13;                        // mfma_m16_nfit_b2 / mfma_m16_nfit_r2
+      if (mt == 64) return n >= 6144 && k % 256 == 0 ? 32 : 29;   // tile_m64_n64 / mfma_m64_nfit_t2
+      if (mt == 32) return k >= 4096 ? 25 : 5;                    // mfma_m32_nfit_b2 / mfma_m32_nfit
+      if (k % 512 == 0) return 31;                                // tile_m16_n64
+      return k >= 7168 ? 23 : 13;                                 // mfma_m16_nfit_b2 / mfma_m16_nfit_r2
     }
   int best = 64;
   double best_cost = 0;
@@ -570,7 +576,19 @@ int w4a16_select(int64_t m, int64_t n, int64_t k) {
       best_cost = cost;
     }
   }
-  return best == 64 ? 30 : w4a16_config_id(best, 64);   // mfma_m64_n64_t2
+  if (best != 64) return w4a16_config_id(best, 64);
+  // 64-row slabs over more than one wave: the tile kernel (5-12% faster than
+  // the four-tile one on every calibrated cell), with 128 x 128 tiles where
+  // their rounds of workgroups cost less: a 128 x 128 tile takes ~2.5x a
+  // 64 x 64 one (14336 x 4096, m = 256: one round of 128 x 128 tiles, 43 us;
+  // four of 64 x 64 tiles, 66 us).  10240 x 2560, m = 256: 1 round against 3,
+  // 1.42x; 8192 x 2048: 1 against 2, and the 64 x 64 tiles win by 8%.
+  if (m > 128 && k % 128 == 0) {
+    const int64_t r128 = ceil_div(ceil_div(m, 128) * ceil_div(n, 128), kW4Workgroups);
+    const int64_t r64 = ceil_div(ceil_div(m, 64) * ceil_div(n, 64), kW4Workgroups);
+    if (5 * r128 < 2 * r64) return 33;   // tile_m128_n128
+  }
+  return k % 256 == 0 ? 32 : 30;   // tile_m64_n64 / mfma_m64_n64_t2
 }
 
 hipError_t launch_w4a16(int config, int64_t m, int64_t n, int64_t k, const uint16_t* x, const uint8_t* w,

@@ -156,10 +156,14 @@ def test_w4a16_configs_and_exhaustive_selector(so):
     # an 8-way K split while that grid fits one wave of 256 workgroups (m
     # tile 16, else 32), or two waves with the 16-row tile at k >= 7168; then
     # the vector ALU for m <= 8 with m * n <= 24576; then the 128 x 128 tile
-    # kernel for m > 64 once its grid fills a wave (224 tiles); then a four-tile pick
-    # with the fit width has an m tile whose grid fits one wave with 64-row
-    # slabs, and no smaller tile does (variant by m tile and K); otherwise
-    # no tile fits and the pick uses 64-row slabs.
+    # kernel for m > 64 once its grid fills a wave (224 tiles); then, with
+    # the smallest m tile whose grid fits one wave with 64-row slabs: the
+    # 16 x 64 tile kernel (16-row m tile, k % 512 == 0), the 64 x 64 one
+    # (64-row m tile, n >= 6144, k % 256 == 0), or the four-tile kernel
+    # (variant by m tile and K); otherwise no tile fits: the tile kernel's
+    # 128 x 128 tiles (m > 128, where 2.5 x their rounds of 256 workgroups
+    # are fewer than the 64 x 64 tiles' rounds) or 64 x 64 tiles, or a
+    # four-tile pick with 64-row slabs.
     decisions = 0
     for n in (1, 64, 896, 1536, 3072, 4096, 4112, 5120, 7168, 8192, 10240, 14336, 65536):
         for k in (32, 4096, 7168, 8192, 14336):
@@ -197,10 +201,23 @@ def test_w4a16_configs_and_exhaustive_selector(so):
                     continue
                 fits = [t for t in (16, 32, 64) if grid(m, n, t, 64) <= 256]
                 if fits:
-                    sfx = {16: "_b2" if k >= 7168 else "_r2", 32: "_b2" if k >= 4096 else "", 64: "_t2"}[fits[0]]
-                    assert nm == f"mfma_m{fits[0]}_nfit" + sfx, (m, n, k, nm)
+                    if fits[0] == 16 and k % 512 == 0:
+                        assert nm == "tile_m16_n64", (m, n, k, nm)
+                    elif fits[0] == 64 and n >= 6144 and k % 256 == 0:
+                        assert nm == "tile_m64_n64", (m, n, k, nm)
+                    else:
+                        sfx = {16: "_b2" if k >= 7168 else "_r2", 32: "_b2" if k >= 4096 else "", 64: "_t2"}[fits[0]]
+                        assert nm == f"mfma_m{fits[0]}_nfit" + sfx, (m, n, k, nm)
+                elif nm in ("tile_m128_n128", "tile_m64_n64", "mfma_m64_n64_t2"):
+                    # 64-row slabs over more than one wave
+                    r128 = -(-(-(-m // 128) * -(-n // 128)) // 256)
+                    r64 = -(-(-(-m // 64) * -(-n // 64)) // 256)
+                    if m > 128 and k % 128 == 0 and 5 * r128 < 2 * r64:
+                        assert nm == "tile_m128_n128", (m, n, k, nm)
+                    else:
+                        assert nm == ("tile_m64_n64" if k % 256 == 0 else "mfma_m64_n64_t2"), (m, n, k, nm)
                 else:
-                    assert nm.endswith("_n64") or nm == "mfma_m64_n64_t2", (m, n, nm)
+                    assert nm.endswith("_n64"), (m, n, nm)
     assert decisions == 13 * 5 * 135
     assert so.bsgemm_w4a16_select(4, 64, 48) == -1 and so.bsgemm_w4a16_select(-1, 64, 64) == -1
 
