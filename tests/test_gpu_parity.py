@@ -252,7 +252,8 @@ def test_gemm_shapes(gpu_lib, fmt, m, n, k):
     assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(1536, 1400, 512), (1536, 1400, 640), (1300, 1600, 544), (1300, 1600, 2048)])
+@pytest.mark.parametrize("m,n,k", [(1536, 1400, 512), (1536, 1400, 640), (1300, 1600, 544), (1300, 1600, 2048),
+                                   (1300, 1601, 1024)])   # n % 8 != 0: the epilogue's 2-byte stores
 def test_gemm_nvfp4_large_grid_paths(gpu_lib, m, n, k):
     """Grids of at least 32 tiles of 256 x 256 (below that the small-problem
     kernel runs): the ring kernel (K % 256 == 0) and the register-staged
@@ -267,7 +268,8 @@ def test_gemm_nvfp4_large_grid_paths(gpu_lib, m, n, k):
     assert_ok(G.check(c, *_ref(L.BSGEMM_NVFP4, qa, qb)), f"nvfp4 {m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(1536, 1400, 512), (1536, 1400, 640), (1300, 1600, 544), (2048, 1024, 1024 + 512)])
+@pytest.mark.parametrize("m,n,k", [(1536, 1400, 512), (1536, 1400, 640), (1300, 1600, 544), (2048, 1024, 1024 + 512),
+                                   (1536, 1402, 1024)])   # n % 8 != 0
 def test_gemm_mxfp8_exact_large_grid_paths(gpu_lib, m, n, k):
     """Exact MXFP8 on grids of at least 32 tiles of 256 x 256: the ring kernel
     with 16-byte (K % 512 == 0) and 4-byte (K % 128 == 0) scale batches, and
@@ -741,6 +743,35 @@ def test_w4a16_config_sampled(gpu_lib, m):
     got = u16(c)
     qw = (cw.cpu().numpy()[cols], sw.cpu().numpy()[cols], np.float32(tw.item()))
     assert_ok(G.check(got[:, cols], *G.w4a16(x, *qw)), f"w4a16 m={m} sampled")
+    assert not np.any(got == SENTINEL)
+
+
+@pytest.mark.parametrize("m,n,k,expect", [
+    (128, 2048, 6144, "tile_m16_n64"),     # 16-row m tiles fit one wave
+    (48, 2560, 5120, "tile_m16_n64"),
+    (128, 6144, 4096, "tile_m64_n64"),     # 64-row m tiles fit one wave, n >= 6144
+    (130, 7000, 1536, "tile_m64_n64"),     # ragged m and n
+    (256, 8192, 2048, "tile_m64_n64"),     # past one wave, 64 x 64 tiles in fewer rounds
+    (256, 10240, 2560, "tile_m128_n128"),  # past one wave, 128 x 128 tiles in fewer rounds
+    (300, 9000, 1024, "tile_m128_n128"),
+    (200, 6144, 4224, "mfma_m64_n64_t2"),  # K % 256 != 0: no tile kernel
+])
+def test_w4a16_selector_branches(gpu_lib, m, n, k, expect):
+    """bsgemm_w4a16_run at shapes where the selector takes each of its
+    tile-kernel branches (and one it must not): W quantized on the GPU, all
+    m rows x 512 sampled columns against the oracle, no unwritten output."""
+    assert L.w4a16_configs()[L.load().bsgemm_w4a16_select(m, n, k)] == expect
+    x = synth.bf16_bits(synth.normal_f32((m, k), m + n + k))
+    wf = synth.normal_f32((n, k), m * k + n, std=0.02)
+    cols = _sample(n, 512, n + k)
+    cw, sw, tw = _check_nvfp4_quant(wf, f"w4a16 W {n}x{k} (sampled rows)", cols)
+    del wf
+    say("w4a16 selector", expect, m, n, k)
+    c = out_bf16(m, n)
+    L.bsgemm_w4a16_run(dev(x), cw, sw, tw, c=c)
+    got = u16(c)
+    qw = (cw.cpu().numpy()[cols], sw.cpu().numpy()[cols], np.float32(tw.item()))
+    assert_ok(G.check(got[:, cols], *G.w4a16(x, *qw)), f"w4a16 selector {expect} {m}x{n}x{k}")
     assert not np.any(got == SENTINEL)
 
 
