@@ -24,11 +24,12 @@
 //
 // Scheduling.  The host knows only G, m_total and n; the row counts stay on
 // the device.  The grid therefore covers an upper bound on the number of
-// tiles: sum_g ceil(c_g / BM) <= m_total / BM + G.  Each workgroup finds its
-// (group, m-tile) with a wave-wide prefix scan over the offsets.  Workgroups
-// past the real tile count exit at once.  Tiles are ordered m-tile-major, so
-// the n-tiles of one m-tile (same A rows) and the m-tiles of one group (same
-// W panel) run close together.  xcd_remap keeps neighbours on one XCD's L2.
+// tiles (256-row tiles: sum_g ceil(c_g / BM) <= m_total / BM + G; the
+// ping-pong kernel's two tile heights: see grouped_grid_blocks).  Each
+// workgroup finds its (group, m-tile) with a wave-wide prefix scan over the
+// offsets.  Workgroups past the real tile count exit at once.  Tiles are
+// ordered n-tile-major, so the m-tiles of one group (same W panel) run close
+// together; xcd_remap keeps neighbours on one XCD's L2.
 //
 // Tile: 256 rows x 256 columns, 4 waves of 128 x 128, K step 64 elements:
 //   - A codes [256][32] bytes (chunks swizzled by (row >> 3) & 1), A scales

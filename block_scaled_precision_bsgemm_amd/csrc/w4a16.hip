@@ -5,11 +5,13 @@
 // (bitsandbytes PR #2030), sections "Methodology" and "The SIMT / MMA layer".
 // That PR measures a fused dequant+GEMM against dequantise-then-linear, and a
 // SIMT (vector ALU) kernel against a matrix-core kernel at small M.  Here:
-//   - m == 1: gemv_kernel, vector ALU only;
-//   - m >= 2: skinny_kernel, BF16 MFMA.
-// Both read every weight byte from HBM once per 64 rows of X and keep X in
-// L2.  At these sizes the kernels are bound by the weight stream, so both
-// are built to keep as much of it in flight as the hardware allows.
+//   - the smallest m: gemv_kernel, vector ALU only;
+//   - larger m: skinny_kernel (K-split and four-tile forms), BF16 MFMA, or the
+//     tile kernel of w4a16_tile.hip;
+// chosen per shape by the selector at the end of this file.  The kernels read
+// every weight byte from HBM once per m tile and keep X in L2.  At these sizes
+// they are bound by the weight stream and the exact expansion of the weights,
+// so they are built to keep as much of the stream in flight as they can.
 #include <algorithm>
 
 #include "common.hpp"
