@@ -515,6 +515,41 @@ def test_grouped_config_sampled(gpu_lib):
     assert not np.any(got == SENTINEL)
 
 
+@pytest.mark.parametrize("k", [512, 320, 96])   # ping-pong, 4-byte-scale ring, register-staged
+def test_grouped_malformed_offsets_stay_in_bounds(gpu_lib, k):
+    """Group offsets are a documented precondition (non-decreasing, off[0] =
+    0, off[G] = m_total).  The kernels clamp them, so malformed offsets
+    (decreasing, negative, past m_total) still touch only A and C: the call
+    succeeds and guard rows on both sides of C keep their sentinel."""
+    m, n, guard = 800, 136, 8                        # 272-byte rows: the view stays 16-byte aligned
+    qa, _, w = _grouped_case([160] * 5, n, k, 4242 + k)
+    for off in ([0, 300, 100, 700, 650, 2000], [0, -50, 900, 400, 400, 800], [5, 5, 5, 5, 5, 5]):
+        say("grouped malformed offsets", k, off)
+        big = torch.full((m + 2 * guard, n), SENTINEL, dtype=torch.int16, device="cuda")
+        c = big[guard:guard + m]
+        L.bsgemm_grouped_run(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)),
+                             dev(np.array(off, np.int32)), dev(w), k, c=c)
+        torch.cuda.synchronize()
+        g = u16(big)
+        assert np.all(g[:guard] == SENTINEL) and np.all(g[guard + m:] == SENTINEL)
+
+
+def test_grouped_kragged_malformed_offsets_stay_in_bounds(gpu_lib):
+    """The K-ragged offsets are clamped to [0, K] and rounded down to 256:
+    malformed ones (decreasing, negative, past K) still touch only A, W and
+    C; guard groups on both sides of C keep their sentinel."""
+    qa, _, w, k = _kragged_case([300, 200, 256], 300, 260, 77, "bf16")   # k = 1024
+    for off in ([0, 512, 256, 2048], [-300, 1000, 9999, 512], [0, 0, 0, 0]):
+        say("grouped K-ragged malformed offsets", off)
+        big = torch.full((5, 300, 260), SENTINEL, dtype=torch.int16, device="cuda")
+        c = big[1:4]
+        L.bsgemm_grouped_kragged_run(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)),
+                                     dev(np.array(off, np.int32)), dev(w), k, c=c)
+        torch.cuda.synchronize()
+        g = u16(big)
+        assert np.all(g[0] == SENTINEL) and np.all(g[4] == SENTINEL)
+
+
 # ------------------------------------------- grouped: routing / epilogue --
 
 def _variant_case(counts, n, k, seed, w_dtype, a_rows=None):
