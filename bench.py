@@ -528,10 +528,25 @@ def headline(L, synth, dev, args, par):
         t0 = time.perf_counter()
         cref, tref = G.gemm_nvfp4(*qa, *qb)
         t = time.perf_counter() - t0
+        # The parts of that time, measured again separately: the exact float64
+        # decode of both operands and the two BLAS products (C_ref and the
+        # magnitude sum T of the acceptance bound).
+        t0 = time.perf_counter()
+        ua, ub = G.nvfp4_units(qa[0], qa[1]), G.nvfp4_units(qb[0], qb[1])
+        t_dec = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        _ = ua @ ub.T
+        t_c = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        _ = np.abs(ua) @ np.abs(ub).T
+        t_t = time.perf_counter() - t0
+        del ua, ub, _
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         res["cpu_baseline"] = {
             "value": round(2.0 * 8192 * N * K / t / 1e12, 4), "unit": "TFLOPS", "cores": threads, "kind": "oracle",
             "seconds": round(t, 2), "cpu_model": cpu_model(), "oracle_quantize_seconds": round(tq, 2),
+            "parts_seconds": {"decode": round(t_dec, 2), "c_ref_matmul": round(t_c, 2), "t_matmul": round(t_t, 2)},
+            "c_ref_gflops": round(2.0 * 8192 * N * K / t_c / 1e9, 1),
             "sample": f"oracle.gemm.gemm_nvfp4 on A[0:8192] x B[0:16384] of the 16384^3 operands, K={K} "
                       "(float64 decode of every code, C and sum|ab| matmuls); the same result is the parity "
                       "reference of the timed output"}
