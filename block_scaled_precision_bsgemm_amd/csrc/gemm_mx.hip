@@ -415,7 +415,6 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   // (all 8 tiles of the first, then the second), so the two MFMAs into one
   // accumulator are 7 issues apart.
   auto mfma_rows = [&](const Frags<FP4>& f, int i0, auto OPSEL) {
-    constexpr int fmt = mfma_fmt<FP4>();
     if constexpr (FP4) {
       static_for<0, 2>([&](auto SC) {
         constexpr int s = decltype(SC)::value;
@@ -439,7 +438,6 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   // One MFMA of tile (i, j) of a stage: the FP8 one, or the FP4 one of K64
   // half SC.
   auto mfma_one = [&](const Frags<FP4>& f, int i, int j, auto OPSEL, auto SC) {
-    constexpr int fmt = mfma_fmt<FP4>();
     if constexpr (FP4) {
       constexpr int s = decltype(SC)::value;
       acc[i][j] = mfma_ab(frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j],

@@ -495,7 +495,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     constexpr bool NEW_SC = ((PAR + NS - 1) & 1) == 0;   // stage kt+NS-1 is even
     auto loads = [&](auto Q) {
       constexpr int q = decltype(Q)::value;
-      return [&, q] {
+      return [&] {
         if constexpr (IL) {
           if (q == 0 && NEW_SC) issue_scales(kt + NS - 1);
           if (q < 4) {
