@@ -1,11 +1,16 @@
-"""Register and LDS budgets of the gfx950 kernels (CPU only: hipcc's
-resource-usage remarks, no GPU).
+"""Register and LDS budgets of the gfx950 kernels, and the memory
+instructions they use (CPU only: hipcc's resource-usage remarks and its
+assembly, no GPU).
 
 A VGPR spill in a main loop goes to scratch memory and costs more than any
 scheduling choice, and it appears silently when a change shifts the
 compiler's register allocation.  Every kernel must fit the CU's LDS, and
 none may spill except the ones listed, whose spills sit outside their main
-loops (epilogue address registers) or in a fallback path."""
+loops (epilogue address registers) or in a fallback path.
+
+Every global write must go through the vector memory path: the library
+writes nothing through the scalar data cache (no scalar stores or atomics,
+no scalar cache write-back or discard)."""
 
 import os
 import re
@@ -31,13 +36,22 @@ def _hipcc():
     return path if os.path.exists(path) else shutil.which("hipcc")
 
 
-def _resources(src):
+# scalar-memory writes: stores, atomics, cache write-back / discard
+SCALAR_WRITE = re.compile(r"^\s*s_(store|atomic|dcache_wb|dcache_discard|buffer_store|buffer_atomic|scratch_store)\w*",
+                          re.MULTILINE)
+
+
+def _resources(src, tmp):
+    asm = os.path.join(tmp, src + ".s")
     cmd = [_hipcc()] + [f for f in B.COMMON_FLAGS if f != "-Wall"] + B.EXTRA_FLAGS.get(src, []) + \
         (["-x", "hip"] if src.endswith(".cpp") else []) + \
-        ["--cuda-device-only", "-c", os.path.join(B.CSRC, src), "-o", os.devnull,
+        ["--cuda-device-only", "-S", os.path.join(B.CSRC, src), "-o", asm,
          "-Rpass-analysis=kernel-resource-usage"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
+    with open(asm) as f:
+        bad = SCALAR_WRITE.findall(f.read())
+    assert not bad, f"{src}: scalar-memory writes in the device code: {sorted(set(bad))}"
     kernels, cur = {}, None
     for line in r.stderr.splitlines():
         m = re.search(r"remark: Function Name: (\S+)", line)
@@ -51,10 +65,10 @@ def _resources(src):
 
 
 @pytest.mark.skipif(_hipcc() is None, reason="hipcc is not installed")
-def test_kernel_register_and_lds_budgets():
+def test_kernel_register_and_lds_budgets(tmp_path):
     srcs = [s for s in B.SOURCES if s.endswith(".hip")]
     with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as ex:
-        per_src = dict(zip(srcs, ex.map(_resources, srcs)))
+        per_src = dict(zip(srcs, ex.map(lambda s: _resources(s, str(tmp_path)), srcs)))
     seen = 0
     for src, kernels in per_src.items():
         for name, res in kernels.items():
@@ -64,3 +78,14 @@ def test_kernel_register_and_lds_budgets():
             cap = next((v for k, v in SPILL_ALLOWED.items() if k in name), 0)
             assert res.get("VGPRs Spill", 0) <= cap, f"{src}: {name} spills {res.get('VGPRs Spill')} VGPRs"
     assert seen >= 20   # every kernel of the library was reported
+
+
+def test_scalar_write_pattern():
+    # the pattern catches the scalar-memory write forms and nothing the kernels legitimately use
+    for line in ("\ts_store_dword s4, s[0:1], 0x0", "  s_atomic_add s2, s[4:5], 0x10", "\ts_dcache_wb",
+                 "\ts_buffer_store_dwordx2 s[2:3], s[8:11], 0x0"):
+        assert SCALAR_WRITE.search(line), line
+    for line in ("\ts_load_dwordx2 s[0:1], s[0:1], 0x0", "\tglobal_store_dword v0, v0, s[0:1]",
+                 "\tbuffer_store_dwordx4 v[0:3], v4, s[8:11], 0 offen", "\ts_waitcnt lgkmcnt(0)",
+                 "\tglobal_atomic_umax v0, v1, s[0:1]"):
+        assert not SCALAR_WRITE.search(line), line
