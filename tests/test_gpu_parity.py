@@ -955,3 +955,114 @@ def test_gemm_mxfp4_every_code(gpu_lib, k):
     say("gemm mxfp4 every code, k =", k)
     c = _gpu_gemm(L.BSGEMM_MXFP4, qa, qb, k)
     assert_ok(G.check(c, *G.gemm_mxfp4(*qa, *qb)), f"mxfp4 every code k={k}")
+
+
+# ------------------------------------------------- graphs and streams --
+
+def test_hot_path_graph_replays_and_two_streams(gpu_lib):
+    """The whole hot path captured once in a HIP graph: the three quantizers
+    (on the device, from FP32), the NVFP4, MXFP8, exact-MXFP8 and MXFP4 GEMMs,
+    the grouped and K-ragged GEMMs and W4A16.  The graph is replayed three
+    times with every output refilled between replays, eager library work and
+    a synchronisation in between; every output of every replay must equal the
+    eager run bit for bit (the kernels are deterministic, and nothing they
+    launch is a memset node).  Then two GEMMs launched at once on two streams
+    must equal their eager results too."""
+    k = 1024
+    xa, xb = dev(synth.normal_f32((512, k), 7001)), dev(synth.normal_f32((768, k), 7002))
+    qa, qb = L.bsgemm_quantize_nvfp4(xa), L.bsgemm_quantize_nvfp4(xb)
+    m8a, m8b = L.bsgemm_quantize_mxfp8(xa), L.bsgemm_quantize_mxfp8(xb)
+    m4a, m4b = L.bsgemm_quantize_mxfp4(xa), L.bsgemm_quantize_mxfp4(xb)
+    counts = [300, 0, 257, 1]
+    gq, goff, gw = _grouped_case(counts, 260, 512, 7003)
+    gq = (dev(gq[0]), dev(gq[1]), dev(np.array([gq[2]], np.float32)))
+    goff, gw = dev(goff), dev(gw)
+    kq, koff, kw, kk = _kragged_case([100, 0, 700, 256], 300, 260, 7004, "bf16")
+    kq = (dev(kq[0]), dev(kq[1]), dev(np.array([kq[2]], np.float32)))
+    koff, kw = dev(koff), dev(kw)
+    wx = dev(synth.bf16_bits(synth.normal_f32((16, 4096), 7005)))
+    wq = L.bsgemm_quantize_nvfp4(dev(synth.normal_f32((640, 4096), 7006, std=0.02)))
+    outs = {"nv": out_bf16(512, 768), "mx8": out_bf16(512, 768), "mx8x": out_bf16(512, 768),
+            "mx4": out_bf16(512, 768), "grouped": out_bf16(558, 260),
+            "kragged": torch.full((4, 300, 260), SENTINEL, dtype=torch.int16, device="cuda"),
+            "w4a16": out_bf16(16, 640)}
+    quant_outs = {"qa": qa, "qb": qb, "m8a": m8a, "m8b": m8b, "m4a": m4a, "m4b": m4b}
+
+    def run():
+        L.bsgemm_quantize_nvfp4(xa, *qa)
+        L.bsgemm_quantize_nvfp4(xb, *qb)
+        L.bsgemm_run(L.BSGEMM_NVFP4, *qa, *qb, k, c=outs["nv"])
+        L.bsgemm_quantize_mxfp8(xa, *m8a)
+        L.bsgemm_quantize_mxfp8(xb, *m8b)
+        L.bsgemm_run(L.BSGEMM_MXFP8, m8a[0], m8a[1], None, m8b[0], m8b[1], None, k, c=outs["mx8"])
+        L.bsgemm_run(L.BSGEMM_MXFP8_EXACT, m8a[0], m8a[1], None, m8b[0], m8b[1], None, k, c=outs["mx8x"])
+        L.bsgemm_quantize_mxfp4(xa, *m4a)
+        L.bsgemm_quantize_mxfp4(xb, *m4b)
+        L.bsgemm_run(L.BSGEMM_MXFP4, m4a[0], m4a[1], None, m4b[0], m4b[1], None, k, c=outs["mx4"])
+        L.bsgemm_grouped_run(*gq, goff, gw, 512, c=outs["grouped"])
+        L.bsgemm_grouped_kragged_run(*kq, koff, kw, kk, c=outs["kragged"])
+        L.bsgemm_w4a16_run(wx, *wq, c=outs["w4a16"])
+
+    def every_output():
+        return dict(outs, **{f"{n}[{i}]": t for n, q in quant_outs.items() for i, t in enumerate(q)})
+
+    def junk(t):
+        return {torch.float32: float("nan"), torch.uint8: 0xAB}.get(t.dtype, SENTINEL)
+
+    def clobber():
+        for t in every_output().values():
+            t.fill_(junk(t))
+
+    say("graph: eager reference run")
+    clobber()
+    run()
+    torch.cuda.synchronize()
+    eager = {n: t.clone() for n, t in every_output().items()}
+    for n, t in eager.items():
+        assert not torch.equal(t, torch.full_like(t, junk(t))), f"the eager run left {n} unwritten"
+    assert_ok(G.check(u16(outs["nv"]), *G.gemm_nvfp4(*Q.quantize_nvfp4(xa.cpu().numpy()),
+                                                   *Q.quantize_nvfp4(xb.cpu().numpy()))), "graph test eager NVFP4")
+
+    say("graph: capture")
+    clobber()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        run()
+    torch.cuda.synchronize()
+    scratch = out_bf16(512, 512)
+    for rep in range(3):
+        say("graph: replay", rep)
+        clobber()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for n, t in every_output().items():
+            assert torch.equal(t, eager[n]), f"replay {rep}: {n} differs from the eager run"
+        # eager library work between replays, on the default stream
+        L.bsgemm_run(L.BSGEMM_MXFP8, m8b[0][:512], m8b[1][:512], None, m8a[0], m8a[1], None, k, c=scratch)
+        torch.cuda.synchronize()
+    del g
+
+    say("two streams")
+    ya, yb = dev(synth.normal_f32((2048, 2048), 7007)), dev(synth.normal_f32((2048, 2048), 7008))
+    na, nb = L.bsgemm_quantize_nvfp4(ya), L.bsgemm_quantize_nvfp4(yb)
+    ea, eb = L.bsgemm_quantize_mxfp8(ya), L.bsgemm_quantize_mxfp8(yb)
+    c1, c2 = out_bf16(2048, 2048), out_bf16(2048, 2048)
+    L.bsgemm_run(L.BSGEMM_NVFP4, *na, *nb, 2048, c=c1)
+    L.bsgemm_run(L.BSGEMM_MXFP8, ea[0], ea[1], None, eb[0], eb[1], None, 2048, c=c2)
+    torch.cuda.synchronize()
+    r1, r2 = c1.clone(), c2.clone()
+    c1.fill_(SENTINEL)
+    c2.fill_(SENTINEL)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            L.bsgemm_run(L.BSGEMM_NVFP4, *na, *nb, 2048, c=c1)
+        with torch.cuda.stream(s2):
+            L.bsgemm_run(L.BSGEMM_MXFP8, ea[0], ea[1], None, eb[0], eb[1], None, 2048, c=c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, r1) and torch.equal(c2, r2)
