@@ -222,13 +222,28 @@ __device__ __forceinline__ rsrc4_t make_rsrc4(const void* base, int bytes) {
 // multi-stage ring.  Hidden in assembly, the loads are invisible to its wait
 // insertion.  The kernel waits for them itself (vmcnt) before the barrier that
 // publishes a stage.  The compiler never holds a value in m0 in these
-// kernels; the assembly sets m0 itself.
+// kernels; the assembly sets m0 itself, with the one wait state that an LDS
+// DMA load needs after a scalar write of m0 (the compiler puts the same
+// s_nop 0 there for its own LDS DMA builtins on gfx950).
 __device__ __forceinline__ void dma_x4(rsrc4_t rsrc, uint32_t lds_base, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+// The same with a wave-uniform scalar offset added to the address.  Callers
+// keep the whole address (vector + scalar offset) of every load that must
+// read data inside the resource, and pass an empty resource (0 bytes) for
+// loads that must read zero, so the result does not depend on whether the
+// range check counts the scalar offset.
+__device__ __forceinline__ void dma_x4_so(rsrc4_t rsrc, uint32_t lds_base, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_x1_so(rsrc4_t rsrc, uint32_t lds_base, int voff, int soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_base), "v"(voff), "s"(rsrc), "s"(soff) : "memory", "m0");
+}
 __device__ __forceinline__ void dma_x1(rsrc4_t rsrc, uint32_t lds_base, int voff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                :: "s"(lds_base), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
 

@@ -291,7 +291,8 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   constexpr int U = Sm::U;                        // stages per scale super-stage
   constexpr int NSB = ring_scale_bufs<U>();
   __shared__ Sm sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases in SGPRs
   int tm, tn;
   if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
     supertile_order(blockIdx.x, tiles_n, tm, tn);
@@ -306,6 +307,10 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   const rsrc4_t rb = make_rsrc4(B + (int64_t)n0 * KP, rows_b * KP);
   const rsrc4_t rsa = make_rsrc4(As + (int64_t)m0 * KB, rows_a * KB);
   const rsrc4_t rsb = make_rsrc4(Bs + (int64_t)n0 * KB, rows_b * KB);
+  // Past-the-end stages load through empty resources: every offset is then
+  // out of range and reads zero.
+  const rsrc4_t ra0 = make_rsrc4(A, 0), rb0 = make_rsrc4(B, 0);
+  const rsrc4_t rsa0 = make_rsrc4(As, 0), rsb0 = make_rsrc4(Bs, 0);
 
   // Code-load geometry: instruction u of this wave covers rows 16 (4 wave + u)
   // .. +15; lane i fills LDS slot i & 3 of row 16 (4 wave + u) + (i >> 2) with
@@ -320,27 +325,31 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   const int scale_off = (64 * wave + lane) * KB;
 
   // Stage st: its codes, plus (when st starts a super-stage) the scales of the
-  // whole super-stage.  Stages past the last are issued at an out-of-range
-  // offset: zeros land in slots nobody reads, and every step keeps the same
-  // static wait count.
+  // whole super-stage.  Stages past the last load through the empty
+  // resources: zeros land in slots nobody reads, and every step keeps the same
+  // static wait count.  The lane's offset is a loop constant and the stage's
+  // K offset the load's scalar offset, so a load costs no vector
+  // instructions.
   // code load u (0..7) of stage st: A rows for u < 4, B rows for u >= 4
   auto issue_code = [&](int st, int u) {
     const int slot = st % RB_NS;
-    const int off = st < KT ? code_off[u & 3] + st * RB_K : OOB;
+    const bool live = st < KT;
     if (u < 4)
-      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
+      dma_x4_so(live ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[slot][64 * (4 * wave + u)], code_off[u & 3], st * RB_K);
     else
-      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + (u & 3))]), off);
+      dma_x4_so(live ? rb : rb0, (uint32_t)(uintptr_t)&sm.b[slot][64 * (4 * wave + (u & 3))], code_off[u & 3],
+                st * RB_K);
   };
   auto issue_scales = [&](int st) {
     const int sbuf = (st / U) % NSB;
-    const int soff = st < KT ? scale_off + (st / U) * SB : OOB;
+    const bool live = st < KT;
+    const int so = (st / U) * SB;
     if (SB == 16) {
-      dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
-      dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave * 4]), soff);
+      dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[sbuf][64 * wave * 4], scale_off, so);
+      dma_x4_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[sbuf][64 * wave * 4], scale_off, so);
     } else {
-      dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
-      dma_x1(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
+      dma_x1_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[sbuf][64 * wave], scale_off, so);
+      dma_x1_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[sbuf][64 * wave], scale_off, so);
     }
   };
   auto issue = [&](int st, auto WITH_SCALES) {

@@ -221,23 +221,22 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 // scale bytes (OCP E4M3, exact for every code, subnormals included).
 struct Scales2 {
   float s[2];
-  uint32_t m2[2];
+  uint32_t mp;    // (1 + f) of block 0 (low half) and block 1 (high half), FP16
 };
 
-__device__ __forceinline__ Scales2 decode_scale_pair(uint32_t word16) {
+__device__ __forceinline__ Scales2 decode_scale_pair(uint32_t word16, uint32_t bias2) {
   const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word16, 1.0f, false);
   Scales2 d;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    d.s[b] = v[b];
-    // (1 + f): the FP32 value with its exponent replaced by 0, converted to an
-    // FP16 pair (exact: at most 3 fraction bits, for subnormal E4M3 codes too,
-    // whose FP32 value is normalised).  A zero scale needs no special case:
-    // the conversion then scales by 2^-127, which rounds to zero in FP16.
-    const float mant = __uint_as_float((__float_as_uint(v[b]) & 0x007FFFFFu) | 0x3F800000u);
-    const auto m2 = __builtin_amdgcn_cvt_pkrtz(mant, mant);
-    __builtin_memcpy(&d.m2[b], &m2, 4);
-  }
+  d.s[0] = v[0];
+  d.s[1] = v[1];
+  // Both scales as FP16 (exact: every E4M3 value is an FP16 normal or zero),
+  // then the exponent fields replaced by the bias: (1 + f) for each.  A zero
+  // scale gives 1.0 here; its conversion scales by 2^-127, which rounds to
+  // zero in FP16, so the product is still zero.
+  const auto h = __builtin_amdgcn_cvt_pkrtz(v[0], v[1]);
+  uint32_t hb;
+  __builtin_memcpy(&hb, &h, 4);
+  d.mp = (hb & 0x03FF03FFu) | bias2;
   return d;
 }
 
@@ -255,10 +254,11 @@ __device__ __forceinline__ v8h convert8_f16(uint32_t codes, float s) {
 }
 // ... and the multiply by (1 + f), an FP16 pair, exact (the products have at
 // most 6 significant bits).
-__device__ __forceinline__ v8h scale8_f16(const v8h& v, uint32_t mant2) {
+template <int B>
+__device__ __forceinline__ v8h scale8_f16(const v8h& v, uint32_t mp) {
   v2h m;
-  __builtin_memcpy(&m, &mant2, 4);
-  const v8h mm = {m[0], m[1], m[0], m[1], m[0], m[1], m[0], m[1]};
+  __builtin_memcpy(&m, &mp, 4);
+  const v8h mm = {m[B], m[B], m[B], m[B], m[B], m[B], m[B], m[B]};
   return v * mm;
 }
 
@@ -320,7 +320,8 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
     uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
   __shared__ NRingSmem<NS> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases in SGPRs
   int tm, tn;
   if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
     supertile_order(blockIdx.x, tiles_n, tm, tn);
@@ -334,6 +335,10 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   const rsrc4_t rb = make_rsrc4(B + (int64_t)n0 * KH, rows_b * KH);
   const rsrc4_t rsa = make_rsrc4(As + (int64_t)m0 * KB, rows_a * KB);
   const rsrc4_t rsb = make_rsrc4(Bs + (int64_t)n0 * KB, rows_b * KB);
+  // Past-the-end stages load through empty resources: every offset is then
+  // out of range and reads zero.
+  const rsrc4_t ra0 = make_rsrc4(A, 0), rb0 = make_rsrc4(B, 0);
+  const rsrc4_t rsa0 = make_rsrc4(As, 0), rsb0 = make_rsrc4(Bs, 0);
 
   int code_off[4];
 #pragma unroll
@@ -344,21 +349,27 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   }
   const int scale_off = (64 * wave + lane) * KB;
 
-  // Stage st (past-the-end stages load zeros from an out-of-range offset):
-  // code load u (A rows for u < 4, B rows for u >= 4) and the scale loads.
+  // Stage st: code load u (A rows for u < 4, B rows for u >= 4) and the
+  // scale loads.  The lane's offset within the tile's panel is a loop
+  // constant, the stage's K offset is the load's scalar offset, and
+  // past-the-end stages load zeros through the empty resources, so issuing a
+  // load costs no vector instructions (measured against per-lane offsets with
+  // a select: 2.3% faster at 16384^3, 1.3-1.6% at 4096^3 and 4096^2 x 16384,
+  // bit-identical).
   auto issue_code = [&](int st, int u) {
     const int slot = st % NS;
-    const int off = st < KT ? code_off[u & 3] + st * ROWB : OOB;
+    const bool live = st < KT;
     if (u < 4)
-      dma_x4(ra, lds_addr(&sm.a[slot][64 * (4 * wave + u)]), off);
+      dma_x4_so(live ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[slot][64 * (4 * wave + u)], code_off[u & 3], st * ROWB);
     else
-      dma_x4(rb, lds_addr(&sm.b[slot][64 * (4 * wave + (u & 3))]), off);
+      dma_x4_so(live ? rb : rb0, (uint32_t)(uintptr_t)&sm.b[slot][64 * (4 * wave + (u & 3))], code_off[u & 3],
+                st * ROWB);
   };
   auto issue_scales = [&](int st) {
     const int sbuf = (st / 2) % NR_SBUF;
-    const int soff = st < KT ? scale_off + (st / 2) * 16 : OOB;
-    dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
-    dma_x4(rsb, lds_addr(&sm.bs[sbuf][64 * wave]), soff);
+    const bool live = st < KT;
+    dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[sbuf][64 * wave], scale_off, (st / 2) * 16);
+    dma_x4_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[sbuf][64 * wave], scale_off, (st / 2) * 16);
   };
   auto issue = [&](int st, auto WITH_SCALES) {
 #pragma unroll
@@ -369,6 +380,11 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     if (decltype(WITH_SCALES)::value) issue_scales(st);
   };
 
+  // 0x3C00 (FP16 1.0) in both halves, held in a VGPR: with the mask in an
+  // SGPR the mantissa extraction is then one v_and_or_b32 (a VOP3 takes one
+  // scalar operand).
+  uint32_t bias2;
+  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(bias2));
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   // Half h of stage st; `par` = st & 1 selects the stage's 8 bytes of the
@@ -394,9 +410,9 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   };
   auto decode = [&](const NHalf& x, NDec& d) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d.a[i] = decode_scale_pair(x.wa[i]);
+    for (int i = 0; i < 4; ++i) d.a[i] = decode_scale_pair(x.wa[i], bias2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d.b[j] = decode_scale_pair(x.wb[j]);
+    for (int j = 0; j < 4; ++j) d.b[j] = decode_scale_pair(x.wb[j], bias2);
   };
   // quarter q of decode: A fragments 2q, 2q + 1 (q < 2) or B fragments
   // 2q - 4, 2q - 3
@@ -404,17 +420,19 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     constexpr int q = decltype(QC)::value;
 #pragma unroll
     for (int i = 2 * (q & 1); i < 2 * (q & 1) + 2; ++i) {
-      if (q < 2) d.a[i] = decode_scale_pair(x.wa[i]);
-      else d.b[i] = decode_scale_pair(x.wb[i]);
+      if (q < 2) d.a[i] = decode_scale_pair(x.wa[i], bias2);
+      else d.b[i] = decode_scale_pair(x.wb[i], bias2);
     }
   };
   auto dequant = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      av[i] = dequant8_f16(dword_of(x.ca[i], sp), d.a[i].s[sp >> 1], d.a[i].m2[sp >> 1]);
+      av[i] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.ca[i], sp), d.a[i].s[1]), d.a[i].mp)
+                     : scale8_f16<0>(convert8_f16(dword_of(x.ca[i], sp), d.a[i].s[0]), d.a[i].mp);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bv[j] = dequant8_f16(dword_of(x.cb[j], sp), d.b[j].s[sp >> 1], d.b[j].m2[sp >> 1]);
+      bv[j] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.cb[j], sp), d.b[j].s[1]), d.b[j].mp)
+                     : scale8_f16<0>(convert8_f16(dword_of(x.cb[j], sp), d.b[j].s[0]), d.b[j].mp);
   };
   auto convert = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
@@ -424,9 +442,9 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   };
   auto rescale = [&](const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = scale8_f16(av[i], d.a[i].m2[sp >> 1]);
+    for (int i = 0; i < 4; ++i) av[i] = (sp >> 1) ? scale8_f16<1>(av[i], d.a[i].mp) : scale8_f16<0>(av[i], d.a[i].mp);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = scale8_f16(bv[j], d.b[j].m2[sp >> 1]);
+    for (int j = 0; j < 4; ++j) bv[j] = (sp >> 1) ? scale8_f16<1>(bv[j], d.b[j].mp) : scale8_f16<0>(bv[j], d.b[j].mp);
   };
 
   v16f acc[4][4];

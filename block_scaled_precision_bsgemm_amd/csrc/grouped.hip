@@ -352,7 +352,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   using VT = typename GM::vec;
   constexpr int U = SB / 4;                  // steps per scale load
   __shared__ GRingSmem<SB> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases in SGPRs
   const int M = p.M, N = p.N, K = p.K;
   const int KH = K / 2, KB = K / 16;
   int grp, r0, r1, nt, k0 = 0, k1 = K;
@@ -408,6 +409,9 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
                                  (gat ? p.a_rows : rows_a) * KB - k0 / 16);
   const rsrc4_t rw = make_rsrc4(p.W + (KRAG ? (int64_t)n0 * K : ((int64_t)grp * N + n0) * K) + k0,
                                 rows_w * K * 2 - k0 * 2);
+  // Past-the-end stages load through empty resources: every offset is then
+  // out of range and reads zero.
+  const rsrc4_t ra0 = make_rsrc4(p.A, 0), rsa0 = make_rsrc4(p.As, 0), rw0 = make_rsrc4(p.W, 0);
   uint16_t* const Cb = KRAG ? p.C + (int64_t)grp * M * N : p.C;
   fill_epi(p, r0, rows_a, tid, sm.epi);   // visible after the prologue's barrier
 
@@ -422,7 +426,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
     const int row = 32 * (2 * wave + u) + (lane >> 1);
     const int src = gat ? gather_row(p, r0, rows_a, row) : row;
     a_ok[u] = src >= 0;
-    a_off[u] = src * KH + (((lane & 1) ^ ((row >> 3) & 1)) * 16);
+    a_off[u] = a_ok[u] ? src * KH + (((lane & 1) ^ ((row >> 3) & 1)) * 16) : OOB;
   }
   int w_off[2];   // even and odd u differ in the swizzle; rows step by 16 per pair
 #pragma unroll
@@ -432,32 +436,36 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
   }
   const int s_src = gat ? gather_row(p, r0, rows_a, 64 * wave + lane) : 64 * wave + lane;
   const bool s_ok = s_src >= 0;
-  const int s_off = s_src * KB;
+  const int s_off = s_ok ? s_src * KB : OOB;
 
   // Part `part` of stage st's loads (IL spreads them over three sub-steps):
   // 0: the scales (when the stage starts a super-stage), A and W loads 0-1;
-  // 1: W loads 2-4; 2: W loads 5-7.  part < 0: all of them.
+  // 1: W loads 2-4; 2: W loads 5-7.  part < 0: all of them.  Each lane's
+  // offset is a loop constant (rows with no source carry the out-of-range
+  // offset), the stage's K offset and the row block are the load's scalar
+  // offset, and past-the-end stages use the empty resources, so issuing a
+  // load costs no vector instructions.
   auto issue_part = [&](int st, int part, bool with_scales) {
     const int slot = st % GR_NS;
     const bool live = st < KT;
     if (part <= 0) {
       if (with_scales) {
         const int sbuf = (st / U) % GR_SBUF;
-        const int soff = (live && s_ok) ? s_off + (st / U) * SB : OOB;
-        if (SB == 16) dma_x4(rsa, lds_addr(&sm.as[sbuf][64 * wave * 4]), soff);
-        else dma_x1(rsa, lds_addr(&sm.as[sbuf][64 * wave]), soff);
+        const int so = (st / U) * SB;
+        if (SB == 16) dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[sbuf][64 * wave * 4], s_off, so);
+        else dma_x1_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[sbuf][64 * wave], s_off, so);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
-        dma_x4(ra, lds_addr(&sm.a[slot][64 * (2 * wave + u)]), (live && a_ok[u]) ? a_off[u] + st * AROWB : OOB);
+        dma_x4_so(live ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[slot][64 * (2 * wave + u)], a_off[u], st * AROWB);
     }
     const int u0 = part < 0 ? 0 : part == 0 ? 0 : part == 1 ? 2 : 5;
     const int u1 = part < 0 ? 8 : part == 0 ? 2 : part == 1 ? 5 : 8;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (u >= u0 && u < u1)
-        dma_x4(rw, lds_addr(&sm.w[slot][64 * (8 * wave + u)]),
-               live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
+        dma_x4_so(live ? rw : rw0, (uint32_t)(uintptr_t)&sm.w[slot][64 * (8 * wave + u)], w_off[u & 1],
+                  (u >> 1) * 16 * K * 2 + st * WROWB);
   };
   auto issue = [&](int st, auto WITH_SCALES) { issue_part(st, -1, decltype(WITH_SCALES)::value); };
 
@@ -809,6 +817,9 @@ __device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1,
   const rsrc4_t ra = make_rsrc4(gat ? p.A : p.A + (int64_t)r0 * KH, (gat ? p.a_rows : rows_a) * KH);
   const rsrc4_t rsa = make_rsrc4(gat ? p.As : p.As + (int64_t)r0 * KB, (gat ? p.a_rows : rows_a) * KB);
   const rsrc4_t rw = make_rsrc4(p.W + ((int64_t)grp * N + n0) * K, rows_w * K * 2);
+  // Past-the-end stages load through empty resources: every offset is then
+  // out of range and reads zero.
+  const rsrc4_t ra0 = make_rsrc4(p.A, 0), rsa0 = make_rsrc4(p.As, 0), rw0 = make_rsrc4(p.W, 0);
   fill_epi(p, r0, rows_a, tid, pp_sm.epi);   // visible after the prologue's barrier
 
   // Load geometry.  Wave w's A load covers rows 32 w .. +31 (two lanes per
@@ -816,7 +827,10 @@ __device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1,
   // row); group 0's waves also load the scales of rows 64 wq .. +63.
   const int arow = 32 * wave + (lane >> 1);
   const int asrc = gat ? gather_row(p, r0, rows_a, arow) : arow;
-  const int a_off = asrc >= 0 ? asrc * KH + (((lane & 1) ^ ((arow >> 3) & 1)) * 16) : -1;
+  // Lane offsets are loop constants (rows with no source carry the
+  // out-of-range offset); the stage's K offset and the row block are the
+  // load's scalar offset; past-the-end stages use the empty resources.
+  const int a_off = asrc >= 0 ? asrc * KH + (((lane & 1) ^ ((arow >> 3) & 1)) * 16) : OOB;
   int w_off[2];   // loads u and u + 2 differ by 16 rows and share the swizzle
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -824,20 +838,20 @@ __device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1,
     w_off[u] = row * K * 2 + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
   }
   const int s_src = gat ? gather_row(p, r0, rows_a, 64 * wq + lane) : 64 * wq + lane;
-  const int s_off = s_src >= 0 ? s_src * KB : -1;
+  const int s_off = s_src >= 0 ? s_src * KB : OOB;
 
   auto issue = [&](int st, auto PG, auto WITH_SCALES) {
     const int slot = st % GR_NS;
     const bool live = st < KT;
     if constexpr (decltype(PG)::value == 0 && decltype(WITH_SCALES)::value) {
       const int sbuf = (st / U) % GR_SBUF;
-      dma_x4(rsa, lds_addr(&pp_sm.as[sbuf][64 * wq * 4]), (live && s_off >= 0) ? s_off + (st / U) * 16 : OOB);
+      dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&pp_sm.as[sbuf][64 * wq * 4], s_off, (st / U) * 16);
     }
-    dma_x4(ra, lds_addr(&pp_sm.a[slot][64 * wave]), (live && a_off >= 0) ? a_off + st * AROWB : OOB);
+    dma_x4_so(live ? ra : ra0, (uint32_t)(uintptr_t)&pp_sm.a[slot][64 * wave], a_off, st * AROWB);
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      dma_x4(rw, lds_addr(&pp_sm.w[slot][64 * (4 * wave + u)]),
-             live ? w_off[u & 1] + (u >> 1) * 16 * K * 2 + st * WROWB : OOB);
+      dma_x4_so(live ? rw : rw0, (uint32_t)(uintptr_t)&pp_sm.w[slot][64 * (4 * wave + u)], w_off[u & 1],
+                (u >> 1) * 16 * K * 2 + st * WROWB);
   };
   // loads per wave for stage st (st % U == s_mod): the scale load joins
   // group 0's A and W loads at the start of each 4-step scale batch
