@@ -224,10 +224,11 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_kernel(
 
 
 // ---------------------------------------------------------------------------
-// Ring kernel (K % 128 == 0): the operands stream HBM -> LDS by direct
-// loads through a 4-stage ring of 64-code-byte K steps (64 K-elements of FP8,
-// 128 of FP4), so three steps are in flight while one is computed.  The
-// pages' FP8 GEMM got its gains from the same lever: ring depth.
+// Ring kernel (K % 128 == 0; launched for K % 512 != 0, where the pair ring
+// below does not apply): the operands stream HBM -> LDS by direct loads
+// through a 4-stage ring of 64-code-byte K steps (64 K-elements of FP8, 128
+// of FP4), so three steps are in flight while one is computed.  The pages'
+// FP8 GEMM got its gains from the same lever: ring depth.
 //
 // Codes, per stage and operand: [256][64] bytes, 16-byte chunk c of row r at
 // c ^ ((r >> 2) & 3) (conflict-free reads).  Each wave issues 8 code loads
@@ -567,12 +568,242 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pair ring kernel (K % 512 == 0): the ring of the kernel above, but each
+// direct load fetches whole 128-byte lines, two K steps of a row at once.
+//
+// What bounds the single-step ring is the rate at which a CU's L1 completes
+// requests to L2: it keeps about 130 of them in flight, so at ~380 cycles of
+// L2 latency it completes ~0.35 per clock, and with 64-byte row segments a
+// step of 32 KiB needs 512 requests (MXFP8 at the full MFMA rate needs 0.5
+// per clock).  A 128-byte segment per row halves the requests for the same
+// bytes.
+//
+// Ring: two pair slots, each [256][128] code bytes per operand (the two K
+// steps of a row side by side), 16-byte chunk c of row r at c ^ ((r >> 1) &
+// 7); the same 128 KiB as four single-step stages.  Scales in 16-byte
+// batches per row (U steps), two batch buffers.
+// Schedule, for pair p = steps 2p and 2p + 1:
+//   step 2p:     its first-half MFMAs interleaved with the B loads of pair
+//                p + 1; then the fragments of step 2p + 1 (same slot) are
+//                read under the second-half MFMAs.  No barrier.
+//   step 2p + 1: first-half MFMAs; wait for every load (all of pair p + 1)
+//                and cross the barrier (after which no wave still reads
+//                slot p); issue the A loads of pair p + 2 (and a scale batch
+//                when it starts one) into slot p; read the fragments of step
+//                2p + 2 under the second-half MFMAs.
+// So one barrier per two steps, and pair p + 1's loads have 1.5-2 steps to
+// land.
+constexpr int PR_CH = 8;   // 16-byte chunks per row of a pair slot
+
+template <bool FP4>
+struct PairSmem {
+  static constexpr int U = 16 / (2 * per_byte<FP4>());   // steps per 16-byte scale batch
+  uint4 a[2][BM * PR_CH];
+  uint4 b[2][BN * PR_CH];
+  uint32_t as[2][BM * 4];
+  uint32_t bs[2][BN * 4];
+};
+
+__device__ __forceinline__ int prswz(int row, int chunk) { return row * PR_CH + (chunk ^ ((row >> 1) & 7)); }
+
+template <bool FP4>
+__global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
+    int tiles_n) {
+  using Sm = PairSmem<FP4>;
+  constexpr int U = Sm::U;             // FP8 8, FP4 4: an even number of steps
+  constexpr int PB = U / 2;            // pairs per scale batch
+  __shared__ Sm sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int tm, tn;
+  if (tiles_m % 16 == 0 && tiles_n % 16 == 0)
+    supertile_order(blockIdx.x, tiles_n, tm, tn);
+  else
+    raster(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KP = K / per_byte<FP4>();  // code bytes per row
+  const int KT = KP / RB_K;            // steps: a positive multiple of U
+  const int KPR = KT / 2;              // pairs
+  const int KB = K / 32;
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+  const rsrc4_t ra = make_rsrc4(A + (int64_t)m0 * KP, rows_a * KP);
+  const rsrc4_t rb = make_rsrc4(B + (int64_t)n0 * KP, rows_b * KP);
+  const rsrc4_t rsa = make_rsrc4(As + (int64_t)m0 * KB, rows_a * KB);
+  const rsrc4_t rsb = make_rsrc4(Bs + (int64_t)n0 * KB, rows_b * KB);
+  const rsrc4_t ra0 = make_rsrc4(A, 0), rb0 = make_rsrc4(B, 0);
+  const rsrc4_t rsa0 = make_rsrc4(As, 0), rsb0 = make_rsrc4(Bs, 0);
+
+  // Load u (0..7) of an operand covers rows 8 (8 wave + u) .. + 7; lane i
+  // fills chunk position i & 7 of row 8 (8 wave + u) + (i >> 3) with the
+  // chunk that the swizzle puts there.
+  int code_off[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int row = 8 * (8 * wave + u) + (lane >> 3);
+    code_off[u] = row * KP + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
+  }
+  const int scale_off = (64 * wave + lane) * KB;
+  auto issue_a = [&](int p, int u) {
+    dma_x4_so(p < KPR ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[p & 1][64 * (8 * wave + u)], code_off[u],
+              p * (2 * RB_K));
+  };
+  auto issue_b = [&](int p, int u) {
+    dma_x4_so(p < KPR ? rb : rb0, (uint32_t)(uintptr_t)&sm.b[p & 1][64 * (8 * wave + u)], code_off[u],
+              p * (2 * RB_K));
+  };
+  auto issue_scales = [&](int p) {   // p starts a batch
+    const int bat = p / PB, buf = bat & 1;
+    const bool live = p < KPR;
+    dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[buf][64 * wave * 4], scale_off, bat * 16);
+    dma_x4_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[buf][64 * wave * 4], scale_off, bat * 16);
+  };
+
+  const int wm = wave >> 1, wn = wave & 1;
+  const int r = lane & 31, g = lane >> 5;
+  // Fragments of step st (st % U == in): its half st & 1 of the pair slot,
+  // chunks 4 h + g and 4 h + 2 + g; scales as in the single-step ring.
+  auto read_frags = [&](int st, auto INC, Frags<FP4>& f) {
+    constexpr int in = decltype(INC)::value;
+    constexpr int word = FP4 ? in : in / 2;
+    constexpr int h = in & 1;
+    const int slot = (st >> 1) & 1, buf = (st / U) & 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.sa[i] = (int)(sm.as[buf][(wm * 128 + i * 32 + r) * 4 + word] >> (8 * g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.sb[j] = (int)(sm.bs[buf][(wn * 128 + j * 32 + r) * 4 + word] >> (8 * g));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r;
+      const uint4 lo = sm.a[slot][prswz(row, 4 * h + g)], hi = sm.a[slot][prswz(row, 4 * h + 2 + g)];
+      if constexpr (FP4) {
+        f.alo[i] = lo;
+        f.ahi[i] = hi;
+      } else {
+        f.a[i] = frag8(lo, hi);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + r;
+      const uint4 lo = sm.b[slot][prswz(row, 4 * h + g)], hi = sm.b[slot][prswz(row, 4 * h + 2 + g)];
+      if constexpr (FP4) {
+        f.blo[j] = lo;
+        f.bhi[j] = hi;
+      } else {
+        f.b[j] = frag8(lo, hi);
+      }
+    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v16f{};
+  auto mfma_ab = [](const v8i& a, const v8i& b, const v16f& c, auto sel_c, int sa, int sb) {
+    constexpr int fmt = mfma_fmt<FP4>();
+    constexpr int sel = decltype(sel_c)::value;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, fmt, fmt, sel, sb, sel, sa);   // B first
+  };
+  auto mfma_one = [&](const Frags<FP4>& f, int i, int j, auto OPSEL, auto SC) {
+    if constexpr (FP4) {
+      constexpr int s = decltype(SC)::value;
+      acc[i][j] = mfma_ab(frag4(s ? f.ahi[i] : f.alo[i]), frag4(s ? f.bhi[j] : f.blo[j]), acc[i][j],
+                          std::integral_constant<int, 2 * s>{}, f.sa[i], f.sb[j]);
+    } else {
+      constexpr int sel = decltype(OPSEL)::value;
+      acc[i][j] = mfma_ab(f.a[i], f.b[j], acc[i][j], std::integral_constant<int, sel>{}, f.sa[i], f.sb[j]);
+    }
+  };
+  // the MFMAs of tile rows 2 hf, 2 hf + 1 (FP4: all 8 tiles' first K64 halves,
+  // then their second halves), one load of `ld` (if any) before each of the
+  // first 8 issues
+  auto mfma_half = [&](const Frags<FP4>& f, int hf, auto OPSEL, auto ld) {
+    static_for<0, 8 * per_byte<FP4>()>([&](auto IX) {
+      constexpr int ix = decltype(IX)::value, t = ix % 8;
+      if constexpr (ix % per_byte<FP4>() == 0) ld(ix / per_byte<FP4>());
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_one(f, 2 * hf + (t >> 2), t & 3, OPSEL, std::integral_constant<int, ix / 8>{});
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  auto no_load = [](int) {};
+
+  Frags<FP4> f[2];
+  // step kt (kt % U == IN; parity IN & 1; fragments in f[IN & 1])
+  auto step = [&](int kt, auto INC) {
+    constexpr int IN = decltype(INC)::value;
+    constexpr int CUR = IN & 1;
+    constexpr auto SEL = std::integral_constant<int, 2 * (IN % 2)>{};
+    const int p = kt >> 1;
+    if constexpr (CUR == 0) {
+      mfma_half(f[CUR], 0, SEL, [&](int u) { issue_b(p + 1, u); });
+    } else {
+      mfma_half(f[CUR], 0, SEL, no_load);
+      wait_vm_barrier<0>();            // pair p + 1 landed; nobody reads slot p any more
+      constexpr bool NEW_BATCH = ((IN + 3) / 2) % PB == 0;   // pair p + 2 starts a scale batch
+      if constexpr (NEW_BATCH) issue_scales(p + 2);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) issue_a(p + 2, u);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, f[CUR ^ 1]);
+    if constexpr (FP4) {
+      static_for<0, 2>([&](auto SC) {
+#pragma unroll
+        for (int i = 2; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mfma_one(f[CUR], i, j, SEL, SC);
+      });
+    } else {
+#pragma unroll
+      for (int i = 2; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mfma_one(f[CUR], i, j, SEL, std::integral_constant<int, 0>{});
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, per_byte<FP4>(), 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                  // 3 LDS reads
+    }
+  };
+
+  // prologue: pair 0 (with the first scale batch) and the A loads of pair 1;
+  // wait for pair 0
+  issue_scales(0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    issue_a(0, u);
+    issue_b(0, u);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) issue_a(1, u);
+  wait_vm_barrier<8>();
+  read_frags(0, std::integral_constant<int, 0>{}, f[0]);
+  for (int kt = 0; kt < KT; kt += U) {
+    static_for<0, U>([&](auto IC) { step(kt + decltype(IC)::value, IC); });
+  }
+
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
+  __syncthreads();                                   // every wave is done with the rings
+  static_assert(sizeof(sm.a) + sizeof(sm.b) >= 4 * 128 * 256, "epilogue staging needs 32 KB per wave");
+  store_block128_bf16<false>(acc, &sm.a[0][0] + wave * (128 * 16), C, M, N, m0 + wm * 128, n0 + wn * 128, 1.0f);
+}
+
+// K % 512 == 0: the pair ring (same-process A/B against the single-step ring,
+// bit-identical output: MXFP8 16384^3 -7.6%, MXFP4 16384^3 -6.7%, MXFP8
+// 4096^3 -5%; loads of the next pair spread one per MFMA beat bursts after the
+// barrier by 3-5%).  K % 128 == 0 otherwise: the single-step ring with 4-byte
+// scale batches.  Any other K: the register-staged kernel.
 template <bool FP4>
 hipError_t launch_mx(int64_t m, int64_t n, int64_t k, const uint8_t* a, const uint8_t* as,
                      const uint8_t* b, const uint8_t* bs, uint16_t* c, hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
   if (k % 512 == 0 && k > 0)
-    hipLaunchKernelGGL((mx_gemm_ring_kernel<16, FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+    hipLaunchKernelGGL((mx_pair_kernel<FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else if (k % 128 == 0 && k > 0)
     hipLaunchKernelGGL((mx_gemm_ring_kernel<4, FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
