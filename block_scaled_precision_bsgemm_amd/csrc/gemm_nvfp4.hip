@@ -268,16 +268,26 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
 
 // ---------------------------------------------------------------------------
 // Ring kernel (K % 256 == 0).  The operands stream HBM -> LDS by direct loads
-// through a 4-stage ring of 128-element K steps; three steps are in flight
-// while one is computed (a step is ~4096 MFMA cycles; the fourth stage
-// measured +3% over three at 16384^3, bit-identical, and fills 152 KiB of LDS).
+// into two pair slots; a pair is two 128-element K steps, so each row of a
+// slot holds the 128 code bytes of two steps and every direct load fetches
+// whole 128-byte lines (against 64-byte half lines with one step per slot:
+// half the L2 requests for the same bytes; same-process A/B against a 4-stage
+// ring of single steps, bit-identical: 16384^3 2.5% faster, 4096^3 and
+// ragged shapes 2-3.5%).  A step is ~4096 MFMA cycles, so the 1.5-2 steps a
+// pair has to land cover the load latency.
 //
-// Per stage and operand, codes are [256][64] bytes, 16-byte chunk c of row r
-// at c ^ ((r >> 2) & 3).  Each wave issues 8 code loads per stage (1 KiB =
-// 16 rows each).  Scales come in batches of 16 bytes per row (two stages of
-// eight 16-element blocks): one load per operand per wave every two stages,
-// with one lane per row.  There are 3 super-stage buffers, so a buffer is
-// rewritten only after the barrier that follows its last read.
+// Per pair slot and operand, codes are [256][128] bytes, 16-byte chunk c of
+// row r at c ^ ((r >> 1) & 7) (conflict-free ds_read_b128); step 2p of pair p
+// is chunks 0-3, step 2p + 1 chunks 4-7.  Scales are the pair's 16 bytes per
+// row (eight 16-element blocks per step), one lane per row.  Each wave issues
+// 8 code loads per operand per pair (1 KiB = 8 rows each) and one scale load.
+// Pair p, steps 2p and 2p + 1:
+//   - step 2p: the B loads of pair p + 1 go out two per sub-step over its
+//     first four sub-steps (into the slot of pair p - 1, free since the last
+//     barrier); no barrier, the next step is in the same slot;
+//   - step 2p + 1: between sub-steps 3 and 4 the wave waits for every load
+//     (pair p + 1) and crosses the barrier, after which nobody reads slot p;
+//     the A loads of pair p + 2 go out two per sub-step over sub-steps 4-7.
 //
 // A step is 8 sub-steps of 16 MFMAs (K16 each); sub-step t uses half t/4 of
 // the step's K range and dword t%4 of the lane's code chunk.  Software
@@ -288,19 +298,14 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
 //     (measured: +3% over issuing them in pairs);
 //   - half 1's codes and scale words are read from LDS during sub-step 0 and
 //     decoded in four quarters over sub-steps 1 and 2;
-//   - between sub-steps 3 and 4 the wave waits for the next stage and crosses
-//     the barrier; the next stage's half-0 data is read during sub-step 4,
-//     decoded over sub-steps 5 and 6, and prepared for its sub-step 0 during
-//     sub-step 7.
-constexpr int NR_NS = 4, NR_ROW = ROWB / 16, NR_SBUF = 3;
-constexpr int NR_CODE_LOADS = 8;
-
-template <int NS>
+//   - the next step's half-0 data is read during sub-step 4 (after the
+//     barrier in odd steps), decoded over sub-steps 5 and 6, and prepared for
+//     its sub-step 0 during sub-step 7.
 struct NRingSmem {
-  uint4 a[NS][BM * NR_ROW];
-  uint4 b[NS][BN * NR_ROW];
-  uint4 as[NR_SBUF][BM];          // 16 scale bytes per row: stage 2q then 2q+1
-  uint4 bs[NR_SBUF][BN];
+  uint4 a[2][BM * 8];             // pair slots: the 128 code bytes of two steps per row
+  uint4 b[2][BN * 8];
+  uint4 as[2][BM];                // 16 scale bytes per row: step 2p then 2p + 1
+  uint4 bs[2][BN];
 };
 
 // Codes and scale words of one half step for one lane: chunk 2h+g of its 4 A
@@ -314,12 +319,11 @@ struct NDec {
   Scales2 a[4], b[4];
 };
 
-template <bool IL = true, int NS = NR_NS>
 __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const float* __restrict__ Ats,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs, const float* __restrict__ Bts,
     uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
-  __shared__ NRingSmem<NS> sm;
+  __shared__ NRingSmem sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: LDS bases in SGPRs
   int tm, tn;
@@ -340,14 +344,16 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   const rsrc4_t ra0 = make_rsrc4(A, 0), rb0 = make_rsrc4(B, 0);
   const rsrc4_t rsa0 = make_rsrc4(As, 0), rsb0 = make_rsrc4(Bs, 0);
 
-  int code_off[4];
+  // load u (0..7) of an operand covers rows 8 (8 wave + u) .. + 7, the 128
+  // bytes of one pair per row; lane i fills chunk position i & 7
+  int code_off[8];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = 16 * (4 * wave + u) + (lane >> 2);
-    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
-    code_off[u] = row * KH + chunk * 16;
+  for (int u = 0; u < 8; ++u) {
+    const int row = 8 * (8 * wave + u) + (lane >> 3);
+    code_off[u] = row * KH + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
   }
   const int scale_off = (64 * wave + lane) * KB;
+  const int KPR = KT / 2;         // pairs
 
   // Stage st: code load u (A rows for u < 4, B rows for u >= 4) and the
   // scale loads.  The lane's offset within the tile's panel is a loop
@@ -356,28 +362,17 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   // load costs no vector instructions (measured against per-lane offsets with
   // a select: 2.3% faster at 16384^3, 1.3-1.6% at 4096^3 and 4096^2 x 16384,
   // bit-identical).
-  auto issue_code = [&](int st, int u) {
-    const int slot = st % NS;
-    const bool live = st < KT;
-    if (u < 4)
-      dma_x4_so(live ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[slot][64 * (4 * wave + u)], code_off[u & 3], st * ROWB);
-    else
-      dma_x4_so(live ? rb : rb0, (uint32_t)(uintptr_t)&sm.b[slot][64 * (4 * wave + (u & 3))], code_off[u & 3],
-                st * ROWB);
+  auto issue_a = [&](int p, int u) {
+    dma_x4_so(p < KPR ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[p & 1][64 * (8 * wave + u)], code_off[u], p * 128);
   };
-  auto issue_scales = [&](int st) {
-    const int sbuf = (st / 2) % NR_SBUF;
-    const bool live = st < KT;
-    dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[sbuf][64 * wave], scale_off, (st / 2) * 16);
-    dma_x4_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[sbuf][64 * wave], scale_off, (st / 2) * 16);
+  auto issue_b = [&](int p, int u) {
+    dma_x4_so(p < KPR ? rb : rb0, (uint32_t)(uintptr_t)&sm.b[p & 1][64 * (8 * wave + u)], code_off[u], p * 128);
   };
-  auto issue = [&](int st, auto WITH_SCALES) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      issue_code(st, u);
-      issue_code(st, 4 + u);
-    }
-    if (decltype(WITH_SCALES)::value) issue_scales(st);
+  auto issue_sa = [&](int p) {
+    dma_x4_so(p < KPR ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[p & 1][64 * wave], scale_off, p * 16);
+  };
+  auto issue_sb = [&](int p) {
+    dma_x4_so(p < KPR ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[p & 1][64 * wave], scale_off, p * 16);
   };
 
   // 0x3C00 (FP16 1.0) in both halves, held in a VGPR: with the mask in an
@@ -391,20 +386,21 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   // 16-byte super-stage entry (static).
   auto read_half = [&](int st, auto PARC, auto HC, NHalf& x) {
     constexpr int par = decltype(PARC)::value, h = decltype(HC)::value;
-    const int slot = st % NS, sbuf = (st / 2) % NR_SBUF;
+    const int slot = (st >> 1) & 1;
+    constexpr int chunk = 4 * par + 2 * h;   // + g: the lane's chunk of the pair row
     // lane g's two scale bytes: the 16-bit half g of the half step's dword
-    const uint16_t* sa16 = reinterpret_cast<const uint16_t*>(&sm.as[sbuf][0]);
-    const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(&sm.bs[sbuf][0]);
+    const uint16_t* sa16 = reinterpret_cast<const uint16_t*>(&sm.as[slot][0]);
+    const uint16_t* sb16 = reinterpret_cast<const uint16_t*>(&sm.bs[slot][0]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + r;
-      x.ca[i] = sm.a[slot][swz(row, 2 * h + g)];
+      x.ca[i] = sm.a[slot][row * 8 + ((chunk + g) ^ ((row >> 1) & 7))];
       x.wa[i] = sa16[(row * 4 + par * 2 + h) * 2 + g];
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wn * 128 + j * 32 + r;
-      x.cb[j] = sm.b[slot][swz(row, 2 * h + g)];
+      x.cb[j] = sm.b[slot][row * 8 + ((chunk + g) ^ ((row >> 1) & 7))];
       x.wb[j] = sb16[(row * 4 + par * 2 + h) * 2 + g];
     }
   };
@@ -504,31 +500,31 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     constexpr int PAR = decltype(PARC)::value;
     using H0 = std::integral_constant<int, 0>;
     using H1 = std::integral_constant<int, 1>;
-    // stage kt+2 carries a scale super-stage when it is even, i.e. PAR == 0.
-    // IL: its loads go out two per sub-step over the first four sub-steps
-    // (a burst of ten direct loads holds up the wave's MFMA issue while the
-    // memory queue drains: measured +2.7% at 16384^3, +4-5% at 4096 x 4096 x
-    // 16384, bit-identical output; one load per sub-step over all eight was
-    // 1% slower at 16384^3); otherwise all at the head of the step.
-    constexpr bool NEW_SC = ((PAR + NS - 1) & 1) == 0;   // stage kt+NS-1 is even
+    // pair p = kt / 2.  Even step: the B loads (and B scales) of pair p + 1,
+    // two per sub-step over the first four.  Odd step: after the mid-step
+    // barrier, the A loads (and A scales) of pair p + 2 over sub-steps 4-7.
+    // (Loads spread over sub-steps: a burst of ten direct loads held up the
+    // wave's MFMA issue while the memory queue drained, measured -2.7% at
+    // 16384^3 with single-step stages.)
+    const int p = kt >> 1;
     auto loads = [&](auto Q) {
       constexpr int q = decltype(Q)::value;
       return [&] {
-        if constexpr (IL) {
-          if (q == 0 && NEW_SC) issue_scales(kt + NS - 1);
+        if constexpr (PAR == 0) {
+          if (q == 0) issue_sb(p + 1);
           if (q < 4) {
-            issue_code(kt + NS - 1, q);
-            issue_code(kt + NS - 1, 4 + q);
+            issue_b(p + 1, 2 * q);
+            issue_b(p + 1, 2 * q + 1);
           }
-        } else if (q == 0) {
-          issue(kt + NS - 1, std::integral_constant<bool, NEW_SC>{});
+        } else {
+          if (q == 4) issue_sa(p + 2);
+          if (q >= 4) {
+            issue_a(p + 2, 2 * (q - 4));
+            issue_a(p + 2, 2 * (q - 4) + 1);
+          }
         }
       };
     };
-    // stages kt+2 .. kt+NS-1 stay in flight at the mid-step wait (all of
-    // stage kt+NS-1's loads are issued before it); an even stage brings the
-    // scales of its super-stage
-    constexpr int EARLY = NR_CODE_LOADS * (NS - 2) + 2 * ((NS - 2 + (PAR == 0 ? 1 : 0)) / 2);
     sub(av[0], bv[0], x0, d0, 1, av[1], bv[1], none, [&] { read_half(kt, PARC, H1{}, x1); }, N4{}, N4{}, N2{},
         loads(std::integral_constant<int, 0>{}));
     sub(av[1], bv[1], x0, d0, 2, av[0], bv[0], [&] { decode_part(x1, d1, std::integral_constant<int, 0>{}); },
@@ -538,8 +534,10 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
         [&] { decode_part(x1, d1, std::integral_constant<int, 3>{}); }, N6{}, N6{}, N0{},
         loads(std::integral_constant<int, 2>{}));
     sub(av[1], bv[1], x1, d1, 0, av[0], bv[0], none, none, N4{}, N4{}, N0{}, loads(std::integral_constant<int, 3>{}));
-    // stage kt+1 landed (stage kt+2 stays in flight)
-    wait_vm_barrier<EARLY>();
+    // odd step: pair p + 1 (every load issued so far) landed, and nobody reads
+    // slot p any more; even step: the next stage is in the same pair slot
+    if constexpr (PAR == 1) wait_vm_barrier<0>();
+    else __builtin_amdgcn_sched_barrier(0);
     sub(av[0], bv[0], x1, d1, 1, av[1], bv[1], none,
         [&] { read_half(kt + 1, std::integral_constant<int, PAR ^ 1>{}, H0{}, x0); }, N4{}, N4{}, N2{},
         loads(std::integral_constant<int, 4>{}));
@@ -552,14 +550,18 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     sub(av[1], bv[1], x0, d0, 0, av[0], bv[0], none, none, N4{}, N4{}, N0{}, loads(std::integral_constant<int, 7>{}));
   };
 
-  // prologue: stages 0 (with the first scale super-stage) and 1
-  // prologue: stages 0 .. NS-2 (even ones with their scale super-stage);
-  // wait for stage 0
-  static_for<0, NS - 1>([&](auto SC) {
-    constexpr int st = decltype(SC)::value;
-    issue(st, std::integral_constant<bool, (st & 1) == 0>{});
-  });
-  wait_vm_barrier<NR_CODE_LOADS * (NS - 2) + 2 * ((NS - 2) / 2)>();
+  // prologue: pair 0 and the A half of pair 1; wait for pair 0
+  issue_sa(0);
+  issue_sb(0);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    issue_a(0, u);
+    issue_b(0, u);
+  }
+  issue_sa(1);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) issue_a(1, u);
+  wait_vm_barrier<9>();
   read_half(0, std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{}, x0);
   decode(x0, d0);
   dequant(x0, d0, 0, av[0], bv[0]);
@@ -668,7 +670,7 @@ hipError_t launch_gemm_nvfp4(int64_t m, int64_t n, int64_t k, const uint8_t* a,
     hipLaunchKernelGGL(nvfp4_small_kernel, dim3(sm * sn), dim3(256), 0, stream, a, as, ats, b, bs, bts, c, (int)m,
                        (int)n, (int)k, sn);
   } else if (k % 256 == 0 && k > 0)
-    hipLaunchKernelGGL((nvfp4_gemm_ring_kernel<true, NR_NS>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+    hipLaunchKernelGGL(nvfp4_gemm_ring_kernel, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, ats, b, bs, bts, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else if (k % 128 == 0)
     hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
