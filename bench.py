@@ -429,6 +429,20 @@ def w4a16_rows(L, synth, dev, par):
         tc = torch.from_numpy(cols).to(dev)
         par.same_bytes("w4a16", [qw[0][tc].cpu().numpy(), qw[1][tc].cpu().numpy(), np.float32(qw[2].item())],
                        list(qwr))
+    # the measured stream floor: a 1 GiB device-to-device copy (read + write
+    # bytes over its event-timed duration), beside the 8 TB/s nameplate
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s_ev, e_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_ev.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e_ev.record()
+    torch.cuda.synchronize()
+    copy_gbps = 5 * 2 * (1 << 30) / (s_ev.elapsed_time(e_ev) * 1e-3) / 1e9
+    del src, dst
     copies = 16
     wc = [qw[0].clone() for _ in range(copies)]
     ws = [qw[1].clone() for _ in range(copies)]
@@ -444,6 +458,7 @@ def w4a16_rows(L, synth, dev, par):
             "config": L.w4a16_configs()[L.bsgemm_w4a16_select(m, Nw, Kw)],
             "us": round(st["ms"] * 1e3, 2), "us_min": round(st["ms_min"] * 1e3, 2), "us_max": round(st["ms_max"] * 1e3, 2),
             "gbps": round(gbps, 1), "frac_hbm": round(gbps / PEAK["hbm_gbps"], 4),
+            "stream_copy_gbps": round(copy_gbps, 1), "frac_stream_copy": round(gbps / copy_gbps, 4),
             "tflops": round(2.0 * m * Nw * Kw / (st["ms"] * 1e-3) / 1e12, 2),
             "graph_matches_eager": st["graph_matches_eager"],
             "timing": f"{REPS} x {2 * copies} graph launches, median, weights rotated through {copies} copies"}
