@@ -311,7 +311,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(const GArgs p) {
         float y = acc[i][j][v] * alpha;
         if (p.bias) y += b;
         if (p.gamma) y *= epi.gamma[lr];
-        if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
+        if (dst >= 0 && col < N) store_nt2(&p.C[(int64_t)dst * N + col], (uint16_t)f32_to_bf16_rne(y));
       }
   }
 }
@@ -697,7 +697,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
       if (vec_ok) {
 #pragma unroll
         for (int t = 0; t < 16; ++t)
-          if (dsts[t] >= 0) *reinterpret_cast<uint4*>(Cb + (int64_t)dsts[t] * N + cbase) = vals[t];
+          if (dsts[t] >= 0) store_nt16(Cb + (int64_t)dsts[t] * N + cbase, vals[t]);
       } else {
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
           const uint32_t wd[4] = {vals[t].x, vals[t].y, vals[t].z, vals[t].w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (cbase + e < N) cp[e] = (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
+            if (cbase + e < N) store_nt2(cp + e, (uint16_t)(wd[e >> 1] >> (16 * (e & 1))));
         }
       }
     }
@@ -987,8 +987,8 @@ __device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1,
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32] =
-              (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha);
+          store_nt2(&cw[(int64_t)(i * 32 + (v >> 2) * 8 + (v & 3)) * N + j * 32],
+                    (uint16_t)f32_to_bf16_rne(acc[i][j][v] * alpha));
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1003,7 +1003,7 @@ __device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1,
           float y = acc[i][j][v] * alpha;
           if (p.bias) y += b;
           if (p.gamma) y *= pp_sm.epi.gamma[lr];
-          if (dst >= 0 && col < N) p.C[(int64_t)dst * N + col] = (uint16_t)f32_to_bf16_rne(y);
+          if (dst >= 0 && col < N) store_nt2(&p.C[(int64_t)dst * N + col], (uint16_t)f32_to_bf16_rne(y));
         }
     }
   }
