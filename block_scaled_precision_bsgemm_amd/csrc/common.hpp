@@ -173,6 +173,14 @@ __device__ __forceinline__ uint4 buffer_load_x4(rsrc_t r, int off) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// The same with cache policy nt (streaming), for data that one launch reads
+// exactly once: it then does not evict data that the launch re-reads.
+__device__ __forceinline__ uint4 buffer_load_x4_nt(rsrc_t r, int off) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const u4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ uint32_t buffer_load_u32(rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
