@@ -276,7 +276,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // launch reads back: the output stream then does not evict the operand
 // panels that neighbouring tiles still share through L2 (32-expert K-ragged
 // problem, 940 MB of C: 707 -> 633 us; MXFP8 4096^3 -5%, MXFP4 16384^3 -2%;
-// bit-identical output).
+// bit-identical output).  Only for stores that write whole 64-byte or longer
+// row segments per instruction: streaming writes of 8- or 16-byte pieces of
+// many lines made the same kernel 4-6x slower, so the element-wise edge
+// paths keep plain stores.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_nt16(void* p, const uint4& v) {
   const u32x4_t x = {v.x, v.y, v.z, v.w};
@@ -336,7 +339,7 @@ __device__ __forceinline__ void store_block128_bf16(const v16f (&acc)[4][4], uin
         const uint32_t w[4] = {v[t].x, v[t].y, v[t].z, v[t].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (col + e < N) store_nt2(cp + e, (uint16_t)(w[e >> 1] >> (16 * (e & 1))));
+          if (col + e < N) cp[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
       }
     }
   }

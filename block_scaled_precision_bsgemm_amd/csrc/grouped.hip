@@ -706,7 +706,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
           const uint32_t wd[4] = {vals[t].x, vals[t].y, vals[t].z, vals[t].w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (cbase + e < N) store_nt2(cp + e, (uint16_t)(wd[e >> 1] >> (16 * (e & 1))));
+            if (cbase + e < N) cp[e] = (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
         }
       }
     }
