@@ -581,8 +581,8 @@ def main():
     ap.add_argument("--no-parity", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); run it with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path, so every "
+              "figure it reports is one GPU's; run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
