@@ -581,8 +581,16 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
 //
 // Ring: two pair slots, each [256][128] code bytes per operand (the two K
 // steps of a row side by side), 16-byte chunk c of row r at c ^ ((r >> 1) &
-// 7); the same 128 KiB as four single-step stages.  Scales in 16-byte
-// batches per row (U steps), two batch buffers.
+// 7); the same 128 KiB as four single-step stages.  Scales in batches per
+// row, two batch buffers: WIDE (K % 1024 == 0) 32 bytes per row (2 U steps),
+// else 16 bytes (U steps).  Every scale row is a separate L2 request, so the
+// wide batches halve the scale requests (MXFP4 16384^3 -3.0%, MXFP8 -0.8%,
+// bit-identical).  A 32-byte row holds two 16-byte chunks, swapped on bit 3
+// of the row, so the 32 lanes that read one scale dword of 32 consecutive
+// rows meet 2-way bank conflicts, as with 16-byte rows (4-way unswapped).
+// The K loop then covers a whole 32-byte batch (both halves unrolled, the
+// half a compile-time constant): a run-time half split the loop body and
+// made the compiler spill.
 // Schedule, for pair p = steps 2p and 2p + 1:
 //   step 2p:     its first-half MFMAs interleaved with the B loads of pair
 //                p + 1; then the fragments of step 2p + 1 (same slot) are
@@ -596,25 +604,27 @@ __global__ __launch_bounds__(NT, 1) void mx_gemm_ring_kernel(
 // land.
 constexpr int PR_CH = 8;   // 16-byte chunks per row of a pair slot
 
-template <bool FP4>
+template <bool FP4, bool WIDE>
 struct PairSmem {
-  static constexpr int U = 16 / (2 * per_byte<FP4>());   // steps per 16-byte scale batch
+  static constexpr int U = 16 / (2 * per_byte<FP4>());   // steps per 16 scale bytes of a row
+  static constexpr int SCW = WIDE ? 8 : 4;                // scale dwords per row of a batch
   uint4 a[2][BM * PR_CH];
   uint4 b[2][BN * PR_CH];
-  uint32_t as[2][BM * 4];
-  uint32_t bs[2][BN * 4];
+  uint32_t as[2][BM * SCW];
+  uint32_t bs[2][BN * SCW];
 };
 
 __device__ __forceinline__ int prswz(int row, int chunk) { return row * PR_CH + (chunk ^ ((row >> 1) & 7)); }
 
-template <bool FP4>
+template <bool FP4, bool WIDE>
 __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, uint16_t* __restrict__ C, int M, int N, int K, int tiles_m,
     int tiles_n) {
-  using Sm = PairSmem<FP4>;
+  using Sm = PairSmem<FP4, WIDE>;
   constexpr int U = Sm::U;             // FP8 8, FP4 4: an even number of steps
-  constexpr int PB = U / 2;            // pairs per scale batch
+  constexpr int SCW = Sm::SCW;
+  constexpr int PB = WIDE ? U : U / 2; // pairs per scale batch
   __shared__ Sm sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -645,7 +655,11 @@ __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
     const int row = 8 * (8 * wave + u) + (lane >> 3);
     code_off[u] = row * KP + (((lane & 7) ^ ((row >> 1) & 7)) * 16);
   }
-  const int scale_off = (64 * wave + lane) * KB;
+  // 16-byte batches: lane i loads row 64 wave + i.  32-byte batches: scale
+  // load v covers rows 64 wave + 32 v .. + 31, two lanes per row, each lane
+  // the chunk that the swap puts in its slot (rows r and r + 32 swap alike).
+  const int srow = WIDE ? 64 * wave + (lane >> 1) : 64 * wave + lane;
+  const int scale_off = WIDE ? srow * KB + 16 * ((lane & 1) ^ ((srow >> 3) & 1)) : srow * KB;
   auto issue_a = [&](int p, int u) {
     dma_x4_so(p < KPR ? ra : ra0, (uint32_t)(uintptr_t)&sm.a[p & 1][64 * (8 * wave + u)], code_off[u],
               p * (2 * RB_K));
@@ -657,23 +671,30 @@ __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
   auto issue_scales = [&](int p) {   // p starts a batch
     const int bat = p / PB, buf = bat & 1;
     const bool live = p < KPR;
-    dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[buf][64 * wave * 4], scale_off, bat * 16);
-    dma_x4_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[buf][64 * wave * 4], scale_off, bat * 16);
+#pragma unroll
+    for (int v = 0; v < (WIDE ? 2 : 1); ++v) {
+      const int lds = 64 * wave * SCW + 256 * v, so = bat * (4 * SCW) + v * 32 * KB;
+      dma_x4_so(live ? rsa : rsa0, (uint32_t)(uintptr_t)&sm.as[buf][lds], scale_off, so);
+      dma_x4_so(live ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[buf][lds], scale_off, so);
+    }
   };
 
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
+  const int ssw = WIDE ? ((r >> 3) & 1) << 2 : 0;   // the chunk swap of this lane's rows (32 i + r)
   // Fragments of step st (st % U == in): its half st & 1 of the pair slot,
   // chunks 4 h + g and 4 h + 2 + g; scales as in the single-step ring.
-  auto read_frags = [&](int st, auto INC, Frags<FP4>& f) {
+  // (HALF: which 16 bytes of a 32-byte batch row hold step st's scales.)
+  auto read_frags = [&](int st, auto INC, auto HALFC, Frags<FP4>& f) {
     constexpr int in = decltype(INC)::value;
     constexpr int word = FP4 ? in : in / 2;
     constexpr int h = in & 1;
-    const int slot = (st >> 1) & 1, buf = (st / U) & 1;
+    const int slot = (st >> 1) & 1, buf = (st / (WIDE ? 2 * U : U)) & 1;
+    const int sdw = (decltype(HALFC)::value ? 4 - ssw : ssw) + word;   // the step's dword of its row
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.sa[i] = (int)(sm.as[buf][(wm * 128 + i * 32 + r) * 4 + word] >> (8 * g));
+    for (int i = 0; i < 4; ++i) f.sa[i] = (int)(sm.as[buf][(wm * 128 + i * 32 + r) * SCW + sdw] >> (8 * g));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.sb[j] = (int)(sm.bs[buf][(wn * 128 + j * 32 + r) * 4 + word] >> (8 * g));
+    for (int j = 0; j < 4; ++j) f.sb[j] = (int)(sm.bs[buf][(wn * 128 + j * 32 + r) * SCW + sdw] >> (8 * g));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + r;
@@ -734,8 +755,9 @@ __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
 
   Frags<FP4> f[2];
   // step kt (kt % U == IN; parity IN & 1; fragments in f[IN & 1])
-  auto step = [&](int kt, auto INC) {
+  auto step = [&](int kt, auto INC, auto HALFC) {
     constexpr int IN = decltype(INC)::value;
+    constexpr int HALF = decltype(HALFC)::value;
     constexpr int CUR = IN & 1;
     constexpr auto SEL = std::integral_constant<int, 2 * (IN % 2)>{};
     const int p = kt >> 1;
@@ -744,13 +766,15 @@ __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
     } else {
       mfma_half(f[CUR], 0, SEL, no_load);
       wait_vm_barrier<0>();            // pair p + 1 landed; nobody reads slot p any more
-      constexpr bool NEW_BATCH = ((IN + 3) / 2) % PB == 0;   // pair p + 2 starts a scale batch
+      // pair p + 2 starts a scale batch
+      constexpr bool NEW_BATCH = WIDE ? HALF == 1 && ((IN + 3) / 2) % (U / 2) == 0 : ((IN + 3) / 2) % PB == 0;
       if constexpr (NEW_BATCH) issue_scales(p + 2);
 #pragma unroll
       for (int u = 0; u < 8; ++u) issue_a(p + 2, u);
       __builtin_amdgcn_sched_barrier(0);
     }
-    read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{}, f[CUR ^ 1]);
+    read_frags(kt + 1, std::integral_constant<int, (IN + 1) % U>{},
+               std::integral_constant<int, WIDE && (IN + 1 == U) ? 1 - HALF : HALF>{}, f[CUR ^ 1]);
     if constexpr (FP4) {
       static_for<0, 2>([&](auto SC) {
 #pragma unroll
@@ -782,9 +806,18 @@ __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
 #pragma unroll
   for (int u = 0; u < 8; ++u) issue_a(1, u);
   wait_vm_barrier<8>();
-  read_frags(0, std::integral_constant<int, 0>{}, f[0]);
-  for (int kt = 0; kt < KT; kt += U) {
-    static_for<0, U>([&](auto IC) { step(kt + decltype(IC)::value, IC); });
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
+  read_frags(0, std::integral_constant<int, 0>{}, H0{}, f[0]);
+  if constexpr (WIDE) {
+    for (int kt = 0; kt < KT; kt += 2 * U) {   // one 32-byte scale batch (KT % (2 U) == 0)
+      static_for<0, U>([&](auto IC) { step(kt + decltype(IC)::value, IC, H0{}); });
+      static_for<0, U>([&](auto IC) { step(kt + U + decltype(IC)::value, IC, H1{}); });
+    }
+  } else {
+    for (int kt = 0; kt < KT; kt += U) {
+      static_for<0, U>([&](auto IC) { step(kt + decltype(IC)::value, IC, H0{}); });
+    }
   }
 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the out-of-range tail loads
@@ -796,14 +829,18 @@ __global__ __launch_bounds__(NT, 1) void mx_pair_kernel(
 // K % 512 == 0: the pair ring (same-process A/B against the single-step ring,
 // bit-identical output: MXFP8 16384^3 -7.6%, MXFP4 16384^3 -6.7%, MXFP8
 // 4096^3 -5%; loads of the next pair spread one per MFMA beat bursts after the
-// barrier by 3-5%).  K % 128 == 0 otherwise: the single-step ring with 4-byte
-// scale batches.  Any other K: the register-staged kernel.
+// barrier by 3-5%), with 32-byte scale batches when K % 1024 == 0.  K % 128
+// == 0 otherwise: the single-step ring with 4-byte scale batches.  Any other
+// K: the register-staged kernel.
 template <bool FP4>
 hipError_t launch_mx(int64_t m, int64_t n, int64_t k, const uint8_t* a, const uint8_t* as,
                      const uint8_t* b, const uint8_t* bs, uint16_t* c, hipStream_t stream) {
   const int tiles_m = (int)ceil_div(m, BM), tiles_n = (int)ceil_div(n, BN);
-  if (k % 512 == 0 && k > 0)
-    hipLaunchKernelGGL((mx_pair_kernel<FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+  if (k % 1024 == 0 && k > 0)
+    hipLaunchKernelGGL((mx_pair_kernel<FP4, true>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
+                       as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
+  else if (k % 512 == 0 && k > 0)
+    hipLaunchKernelGGL((mx_pair_kernel<FP4, false>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
                        as, b, bs, c, (int)m, (int)n, (int)k, tiles_m, tiles_n);
   else if (k % 128 == 0 && k > 0)
     hipLaunchKernelGGL((mx_gemm_ring_kernel<4, FP4>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a,
