@@ -284,6 +284,24 @@ def test_gemm_mxfp8_exact_large_grid_paths(gpu_lib, m, n, k):
     assert_ok(G.check(c, *G.gemm_mxfp8(*qa, *qb)), f"mxfp8 exact {m}x{n}x{k}")
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("m,n,k", [(1300, 1500, 2048), (1536, 1402, 1024), (1300, 1600, 1536), (1536, 1400, 640)])
+def test_gemm_mx_large_grid_paths(gpu_lib, fmt, m, n, k):
+    """Native MXFP8 / MXFP4 on grids of 30+ tiles of 256 x 256 with ragged M
+    and N (n % 8 != 0 in one case): the pair ring with 32-byte scale batches
+    (K % 1024 == 0), with 16-byte batches (K % 512 == 0 only), and the
+    single-step ring (K % 128 == 0)."""
+    f = FMTS[fmt]
+    r = np.random.Generator(np.random.PCG64(m * 7919 + n * 31 + k + 11))
+    xa = r.standard_normal((m, k)).astype(np.float32)
+    xb = r.standard_normal((n, k)).astype(np.float32)
+    xa[:: 97] *= np.float32(50.0)                      # mixed block scales
+    qa, qb = _quant(f, xa), _quant(f, xb)
+    say("gemm", fmt, "large grid", m, n, k)
+    c = _gpu_gemm(f, qa, qb, k)
+    assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "mxfp8_exact"])
 def test_gemm_zero_rows_and_k0(gpu_lib, fmt):
     f = FMTS[fmt]
