@@ -302,6 +302,37 @@ def test_gemm_mx_large_grid_paths(gpu_lib, fmt, m, n, k):
     assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
 
 
+def _random_shapes(count, seed):
+    """Seeded shapes that cross every dispatch boundary: K a multiple of 1024,
+    512, 256, 128, 64 or only 32; M and N from single rows to grids of 40+
+    tiles of 256 x 256, mostly ragged."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    ks = [1024, 2048, 512 * 3, 256 * 5, 128 * 7, 64 * 9, 32 * 11, 32 * 37]
+    out = []
+    for i in range(count):
+        k = ks[i % len(ks)]
+        big = i % 2 == 0
+        m = int(r.integers(1300, 1800)) if big else int(r.integers(1, 700))
+        n = int(r.integers(1300, 1800)) if big else int(r.integers(1, 700))
+        out.append((m, n, k))
+    return out
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "mxfp8_exact"])
+@pytest.mark.parametrize("m,n,k", _random_shapes(16, 20261202))
+def test_gemm_random_shapes(gpu_lib, fmt, m, n, k):
+    """Every format on seeded random shapes against the oracle (all elements)."""
+    f = FMTS[fmt]
+    r = np.random.Generator(np.random.PCG64(m * 104729 + n * 131 + k))
+    xa = r.standard_normal((m, k)).astype(np.float32)
+    xb = r.standard_normal((n, k)).astype(np.float32)
+    xa[:: 53] *= np.float32(30.0)                      # mixed block scales
+    qa, qb = _quant(f, xa), _quant(f, xb)
+    say("gemm random", fmt, m, n, k)
+    c = _gpu_gemm(f, qa, qb, k)
+    assert_ok(G.check(c, *_ref(f, qa, qb)), f"{fmt} {m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "mxfp8_exact"])
 def test_gemm_zero_rows_and_k0(gpu_lib, fmt):
     f = FMTS[fmt]
