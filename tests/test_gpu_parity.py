@@ -529,6 +529,30 @@ def test_grouped_shapes(gpu_lib, counts, n, k):
     assert_ok(G.check(c, *G.grouped_nvfp4_bf16(*qa, off, w)), f"grouped {counts} n={n} k={k}")
 
 
+def _random_grouped(count, seed):
+    """Seeded grouped problems: 1-20 groups with empty ones, ragged N, and K
+    on each kernel path (K % 256 == 0 ping-pong, K % 64 == 0 ring, K % 32 ==
+    0 register-staged)."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    ks = [256 * 3, 64 * 5, 32 * 7, 1024, 64 * 13, 32 * 33]
+    out = []
+    for i in range(count):
+        g = int(r.integers(1, 21))
+        counts = [int(c) if r.random() > 0.2 else 0 for c in r.integers(0, 700, g)]
+        n = int(r.integers(1, 1200))
+        out.append((counts, n, ks[i % len(ks)]))
+    return out
+
+
+@pytest.mark.parametrize("counts,n,k", _random_grouped(12, 20261203))
+def test_grouped_random(gpu_lib, counts, n, k):
+    """The grouped GEMM on seeded random group mixes against the oracle (every element)."""
+    qa, off, w = _grouped_case(counts, n, k, sum(counts) * 7 + n + k)
+    say("grouped random", len(counts), sum(counts), n, k)
+    c = _gpu_grouped(qa, off, w, k)
+    assert_ok(G.check(c, *G.grouped_nvfp4_bf16(*qa, off, w)), f"grouped random {counts} n={n} k={k}")
+
+
 @pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
 def test_grouped_tile_sizes(gpu_lib, w_dtype):
     """Group sizes around the ping-pong kernel's two tile sizes: remainders of
