@@ -787,6 +787,31 @@ def test_grouped_kragged_shapes(gpu_lib, w_dtype, counts, m, n):
         assert_ok(G.check(got[g], cref[g], t[g]), f"K-ragged group {g} of {counts} {w_dtype}")
 
 
+def _random_kragged(count, seed):
+    """Seeded K-ragged problems: 1-12 experts with empty ones, ragged M and N."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for i in range(count):
+        g = int(r.integers(1, 13))
+        counts = [int(c) if r.random() > 0.2 else 0 for c in r.integers(0, 900, g)]
+        out.append((counts, int(r.integers(1, 800)), int(r.integers(1, 700)), "bf16" if i % 2 == 0 else "f16"))
+    return out
+
+
+@pytest.mark.parametrize("counts,m,n,w_dtype", _random_kragged(8, 20261204))
+def test_grouped_kragged_random(gpu_lib, counts, m, n, w_dtype):
+    """The K-ragged mode on seeded random expert mixes, every group against the oracle."""
+    qa, off, w, k = _kragged_case(counts, m, n, sum(counts) * 3 + m + n, w_dtype)
+    say("grouped K-ragged random", w_dtype, len(counts), m, n, k)
+    c = torch.full((len(counts), m, n), SENTINEL, dtype=torch.int16, device="cuda")
+    L.bsgemm_grouped_kragged_run(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)), dev(off), dev(w), k,
+                                 w_dtype=L.BSGEMM_W_F16 if w_dtype == "f16" else L.BSGEMM_W_BF16, c=c)
+    got = u16(c)
+    cref, t = G.grouped_kragged(*qa, off, w, w_dtype)
+    for g in range(len(counts)):
+        assert_ok(G.check(got[g], cref[g], t[g]), f"K-ragged random group {g} of {counts} {w_dtype}")
+
+
 def test_grouped_kragged_config_sampled(gpu_lib):
     """Weight-gradient shape of the grouped config: 32 experts' token counts
     (the Dirichlet draw over 16384 tokens) split K, each padded to 256;
