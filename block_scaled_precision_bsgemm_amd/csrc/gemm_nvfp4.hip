@@ -10,8 +10,11 @@
 // 8-bit MFMA operands.  The exact mapping used here:
 //   - e2m1(code) * e4m3(scale) has at most 6 significant bits and lies in
 //     [2^-10, 2688], so it is exact in FP16;
-//   - the scaled FP4->FP16 conversion supplies the scale's power of two;
-//   - one packed FP16 multiply supplies (1 + f);
+//   - ring kernel: the FP4->FP16 conversion gives the code value and one
+//     packed FP16 multiply the whole scale (both E4M3 scales of a lane's
+//     blocks decoded to an FP16 pair by one conversion);
+//   - register-staged and small kernels: the scaled conversion supplies the
+//     scale's power of two and the multiply (1 + f);
 //   - the FP16 MFMA (v_mfma_f32_32x32x16_f16) accumulates in FP32;
 //   - the epilogue multiplies by s_tA * s_tB.
 // The roofline of this path is therefore the FP16/BF16 dense MFMA peak.
@@ -215,45 +218,38 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 }
 
 
-// Decoded scales of one lane for one half step: for each of its two 16-element
-// blocks, the E4M3 value as FP32 (whose exponent drives the conversion) and
-// (1 + f) as an FP16 pair.  One packed FP8->FP32 conversion decodes both
-// scale bytes (OCP E4M3, exact for every code, subnormals included).
+// Decoded scales of one lane for one half step: the E4M3 scales of its two
+// 16-element blocks as an FP16 pair (block 0 low, block 1 high), from one
+// packed FP8 -> FP16 conversion (exact: every E4M3 value, subnormals
+// included, is an FP16 normal or zero).
 struct Scales2 {
-  float s[2];
-  uint32_t mp;    // (1 + f) of block 0 (low half) and block 1 (high half), FP16
+  uint32_t mp;
 };
 
-__device__ __forceinline__ Scales2 decode_scale_pair(uint32_t word16, uint32_t bias2) {
-  const v2f v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word16, 1.0f, false);
+__device__ __forceinline__ Scales2 decode_scale_pair(uint32_t word16) {
+  const v2h h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word16, 1.0f, false);
   Scales2 d;
-  d.s[0] = v[0];
-  d.s[1] = v[1];
-  // Both scales as FP16 (exact: every E4M3 value is an FP16 normal or zero),
-  // then the exponent fields replaced by the bias: (1 + f) for each.  A zero
-  // scale gives 1.0 here; its conversion scales by 2^-127, which rounds to
-  // zero in FP16, so the product is still zero.
-  const auto h = __builtin_amdgcn_cvt_pkrtz(v[0], v[1]);
-  uint32_t hb;
-  __builtin_memcpy(&hb, &h, 4);
-  d.mp = (hb & 0x03FF03FFu) | bias2;
+  __builtin_memcpy(&d.mp, &h, 4);
   return d;
 }
 
-// The two halves of dequant8_f16, issued apart: the scaled conversion
-// (e2m1 * 2^E, exact) ...
-__device__ __forceinline__ v8h convert8_f16(uint32_t codes, float s) {
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 0);
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 1);
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 2);
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 3);
+// The two halves of the exact expansion, issued apart: the code values
+// (e2m1 as FP16, exact) ...
+__device__ __forceinline__ v8h convert8_f16(uint32_t codes) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
   v8h out;
   out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
   out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
   return out;
 }
-// ... and the multiply by (1 + f), an FP16 pair, exact (the products have at
-// most 6 significant bits).
+// ... and the multiply by the block's whole scale (half B of the FP16 pair),
+// exact: an e2m1 value times an E4M3 scale has at most 6 significant bits and
+// lies in [2^-10, 2688] or is zero.  (Before: the conversion took 2^E from an
+// FP32 scale and the multiply only (1 + f), which cost two more instructions
+// per scale pair to build; same bits, 1.2-2.4% slower.)
 template <int B>
 __device__ __forceinline__ v8h scale8_f16(const v8h& v, uint32_t mp) {
   v2h m;
@@ -293,7 +289,7 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
 // the step's K range and dword t%4 of the lane's code chunk.  Software
 // pipeline inside a step:
 //   - the operands of sub-step t+1 are prepared during sub-step t: the
-//     scaled conversions under its first 8 MFMAs, the (1 + f) multiplies
+//     code conversions under its first 8 MFMAs, the scale multiplies
 //     under its last 8, so no multiply waits on a conversion just issued
 //     (measured: +3% over issuing them in pairs);
 //   - half 1's codes and scale words are read from LDS during sub-step 0 and
@@ -375,11 +371,6 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     dma_x4_so(p < KPR ? rsb : rsb0, (uint32_t)(uintptr_t)&sm.bs[p & 1][64 * wave], scale_off, p * 16);
   };
 
-  // 0x3C00 (FP16 1.0) in both halves, held in a VGPR: with the mask in an
-  // SGPR the mantissa extraction is then one v_and_or_b32 (a VOP3 takes one
-  // scalar operand).
-  uint32_t bias2;
-  asm volatile("v_mov_b32 %0, 0x3c003c00" : "=v"(bias2));
   const int wm = wave >> 1, wn = wave & 1;
   const int r = lane & 31, g = lane >> 5;
   // Half h of stage st; `par` = st & 1 selects the stage's 8 bytes of the
@@ -406,9 +397,9 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   };
   auto decode = [&](const NHalf& x, NDec& d) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d.a[i] = decode_scale_pair(x.wa[i], bias2);
+    for (int i = 0; i < 4; ++i) d.a[i] = decode_scale_pair(x.wa[i]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) d.b[j] = decode_scale_pair(x.wb[j], bias2);
+    for (int j = 0; j < 4; ++j) d.b[j] = decode_scale_pair(x.wb[j]);
   };
   // quarter q of decode: A fragments 2q, 2q + 1 (q < 2) or B fragments
   // 2q - 4, 2q - 3
@@ -416,25 +407,25 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
     constexpr int q = decltype(QC)::value;
 #pragma unroll
     for (int i = 2 * (q & 1); i < 2 * (q & 1) + 2; ++i) {
-      if (q < 2) d.a[i] = decode_scale_pair(x.wa[i], bias2);
-      else d.b[i] = decode_scale_pair(x.wb[i], bias2);
+      if (q < 2) d.a[i] = decode_scale_pair(x.wa[i]);
+      else d.b[i] = decode_scale_pair(x.wb[i]);
     }
   };
   auto dequant = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      av[i] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.ca[i], sp), d.a[i].s[1]), d.a[i].mp)
-                     : scale8_f16<0>(convert8_f16(dword_of(x.ca[i], sp), d.a[i].s[0]), d.a[i].mp);
+      av[i] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.ca[i], sp)), d.a[i].mp)
+                     : scale8_f16<0>(convert8_f16(dword_of(x.ca[i], sp)), d.a[i].mp);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bv[j] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.cb[j], sp), d.b[j].s[1]), d.b[j].mp)
-                     : scale8_f16<0>(convert8_f16(dword_of(x.cb[j], sp), d.b[j].s[0]), d.b[j].mp);
+      bv[j] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.cb[j], sp)), d.b[j].mp)
+                     : scale8_f16<0>(convert8_f16(dword_of(x.cb[j], sp)), d.b[j].mp);
   };
   auto convert = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = convert8_f16(dword_of(x.ca[i], sp), d.a[i].s[sp >> 1]);
+    for (int i = 0; i < 4; ++i) av[i] = convert8_f16(dword_of(x.ca[i], sp));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = convert8_f16(dword_of(x.cb[j], sp), d.b[j].s[sp >> 1]);
+    for (int j = 0; j < 4; ++j) bv[j] = convert8_f16(dword_of(x.cb[j], sp));
   };
   auto rescale = [&](const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
