@@ -67,7 +67,7 @@ def gemm_nvfp4(a_codes, a_scales, a_ts, b_codes, b_scales, b_ts, rows=None):
     ua, ub = nvfp4_units(a_codes, a_scales), nvfp4_units(b_codes, b_scales)
     st = np.float64(np.float32(a_ts)) * np.float64(np.float32(b_ts))
     c, t = _matmul_and_mag(ua, ub)
-    return c * st, t * st
+    return c * st, t * abs(st)     # T sums the terms' magnitudes
 
 
 def dequant_mxfp4(codes, scales) -> np.ndarray:

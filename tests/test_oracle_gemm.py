@@ -387,3 +387,15 @@ def test_planted_nibble_swap_fails_the_one_sided_pins(monkeypatch):
     assert any(Fraction(float(d[r, k])) != ea[r][k] for r in range(4) for k in range(64))
     c1, t1 = G.w4a16(x, *a)
     assert np.max(np.abs(c1 - c0) / t1) > 1e-6
+
+
+def test_nvfp4_negative_tensor_scale():
+    """T is the sum of the magnitudes of the summed terms, so a negative
+    tensor scale flips C and leaves T as for its magnitude; T >= |C|."""
+    r = np.random.Generator(np.random.PCG64(11))
+    a = (r.integers(0, 256, (5, 16)).astype(np.uint8), r.integers(0, 0xFF, (5, 2)).astype(np.uint8) & 0xFE)
+    b = (r.integers(0, 256, (7, 16)).astype(np.uint8), r.integers(0, 0x7F, (7, 2)).astype(np.uint8))
+    cp, tp = G.gemm_nvfp4(a[0], a[1], np.float32(0.5), b[0], b[1], np.float32(3.0))
+    cn, tn = G.gemm_nvfp4(a[0], a[1], np.float32(0.5), b[0], b[1], np.float32(-3.0))
+    assert np.array_equal(cn, -cp) and np.array_equal(tn, tp)
+    assert np.all(tn >= np.abs(cn)) and np.all(tn > 0)
