@@ -62,31 +62,20 @@ __device__ __forceinline__ float e4m3_decode_mag(uint32_t c) {
   return c < 8u ? sub : nrm;
 }
 
-// Exact FP32 value of an E4M3 scale code.  NVFP4 scales are non-negative; the
-// sign bit is ignored.  The NaN code 0x7F is not produced by the quantizer.
-__device__ __forceinline__ float e4m3_scale_value(uint32_t code) {
-  return e4m3_decode_mag(code & 0x7Fu);
+// Bytes 0 and 1 of `word` as two exact E4M3 (FN) values in FP32, signs
+// included; the NaN codes 0x7F and 0xFF give NaN.
+__device__ __forceinline__ v2f e4m3_pair_f32(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);
 }
 
-// The gfx950 scaled conversions (v_cvt_scalef32_pk_*_fp4) multiply by 2^E,
-// where E is the exponent field of their FP32 scale operand; the mantissa is
-// ignored.  An E4M3 scale s = 2^E * (1 + f), with f in {0, 1/8, ..., 7/8}, is
-// therefore applied in two exact steps:
-//   - the conversion, given s itself, supplies 2^E;
-//   - a multiply supplies (1 + f).
-// This returns 1 + f as an FP16 pair, for v_pk_mul_f16.  For s == 0 it
-// returns 0, so a zero scale gives exact zeros: the conversion alone would
-// scale by 2^-127.
-__device__ __forceinline__ uint32_t scale_mantissa_f16x2(float s) {
-  const uint32_t m = ((__float_as_uint(s) >> 13) & 0x3FFu) | 0x3C00u;  // 1.f as FP16
-  return s == 0.0f ? 0u : (m | (m << 16));
-}
-
-// The same mantissa factor as an FP32 value, for the FP32 dequantisation
-// path; 0 for a zero scale.
-__device__ __forceinline__ float scale_mantissa_f32(float s) {
-  const float m = __uint_as_float((__float_as_uint(s) & 0x007FFFFFu) | 0x3F800000u);
-  return s == 0.0f ? 0.0f : m;
+// Bytes 0 and 1 of `word` as two E4M3 values in an FP16 pair (byte 0 in bits
+// 15:0).  Exact: every E4M3 value, subnormals included, is an FP16 normal or
+// zero.
+__device__ __forceinline__ uint32_t e4m3_pair_f16(uint32_t word) {
+  const v2h h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
 }
 
 // ---------------------------------------------------------------------- BF16
@@ -118,40 +107,53 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 }
 
 // ------------------------------------------------------- FP4 -> 16-bit dequant
+//
+// A block-scaled element is e2m1(code) * e4m3(scale).  Both factors are
+// decoded exactly (the FP4 conversions at scale 1.0 give the code values)
+// and multiplied once: the product has at most 6 significant bits and its
+// magnitude is zero or in [2^-10, 2688], so it is exact in FP16, BF16 and
+// FP32.  The scale keeps its sign; a NaN scale code gives NaN products.
 
-// Eight E2M1 codes (one dword; element j in nibble j) scaled by an E4M3 scale
-// `s` (its FP32 value) and its mantissa factor `mant2` (scale_mantissa_f16x2(s)).
-// Returns the eight exact FP16 products e2m1 * s, element j in lane j.
-// Each product has at most 6 significant bits and lies in [2^-10, 2688], so it
-// is exact in FP16.
-__device__ __forceinline__ v8h dequant8_f16(uint32_t codes, float s, uint32_t mant2) {
-  v2h m;
-  __builtin_memcpy(&m, &mant2, 4);
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 0) * m;
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 1) * m;
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 2) * m;
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, s, 3) * m;
+// Eight E2M1 codes (one dword; element j in nibble j) as exact FP16 values.
+__device__ __forceinline__ v8h e2m1x8_f16(uint32_t codes) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
   v8h out;
   out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
   out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
   return out;
 }
 
-// Eight E2M1 codes times an E4M3 scale, as exact BF16 values.  The BF16
-// products have at most 6 significant bits, so they are exact.  The
-// conversion gives v * 2^E as FP32; one FP32 multiply by (1 + f) completes the
-// scale; the high halves of the exact FP32 results are the BF16 patterns,
-// packed by one byte permute.  `mant` is scale_mantissa_f32(s): 0 for a zero
-// scale, which the conversion alone would leave as 2^-127 (not zero).
-template <int J>
-__device__ __forceinline__ uint32_t dequant2_bf16(uint32_t codes, float s, float mant) {
-  const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, s, J);
-  return __builtin_amdgcn_perm(__float_as_uint(p[1] * mant), __float_as_uint(p[0] * mant), 0x07060302u);
+// v times the scale in half `b` (0 or 1; a constant once inlined) of the FP16
+// pair `pair` (e4m3_pair_f16): four packed multiplies with the scale half
+// selected by the instruction's operand select.
+__device__ __forceinline__ v8h scale8_f16(const v8h& v, uint32_t pair, int b) {
+  v2h m;
+  __builtin_memcpy(&m, &pair, 4);
+  const _Float16 s = b ? m[1] : m[0];
+  const v8h mm = {s, s, s, s, s, s, s, s};
+  return v * mm;
 }
 
-__device__ __forceinline__ v8bf dequant8_bf16(uint32_t codes, float s, float mant) {
-  const uint32_t w[4] = {dequant2_bf16<0>(codes, s, mant), dequant2_bf16<1>(codes, s, mant),
-                         dequant2_bf16<2>(codes, s, mant), dequant2_bf16<3>(codes, s, mant)};
+// Eight E2M1 codes times the E4M3 scale in half `b` of `pair`, exact FP16.
+__device__ __forceinline__ v8h dequant8_f16(uint32_t codes, uint32_t pair, int b) {
+  return scale8_f16(e2m1x8_f16(codes), pair, b);
+}
+
+// Two E2M1 codes (pair J of the dword) times the E4M3 scale `s` (FP32),
+// packed as BF16 (low element in bits 15:0): the FP32 products are exact and
+// their high halves are the BF16 patterns, packed by one byte permute.
+template <int J>
+__device__ __forceinline__ uint32_t dequant2_bf16(uint32_t codes, float s) {
+  const v2f p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, J);
+  return __builtin_amdgcn_perm(__float_as_uint(p[1] * s), __float_as_uint(p[0] * s), 0x07060302u);
+}
+
+__device__ __forceinline__ v8bf dequant8_bf16(uint32_t codes, float s) {
+  const uint32_t w[4] = {dequant2_bf16<0>(codes, s), dequant2_bf16<1>(codes, s),
+                         dequant2_bf16<2>(codes, s), dequant2_bf16<3>(codes, s)};
   v8bf out;
   __builtin_memcpy(&out, w, 16);
   return out;

@@ -10,11 +10,9 @@
 // 8-bit MFMA operands.  The exact mapping used here:
 //   - e2m1(code) * e4m3(scale) has at most 6 significant bits and lies in
 //     [2^-10, 2688], so it is exact in FP16;
-//   - ring kernel: the FP4->FP16 conversion gives the code value and one
-//     packed FP16 multiply the whole scale (both E4M3 scales of a lane's
-//     blocks decoded to an FP16 pair by one conversion);
-//   - register-staged and small kernels: the scaled conversion supplies the
-//     scale's power of two and the multiply (1 + f);
+//   - the FP4->FP16 conversion gives the code value and one packed FP16
+//     multiply the whole scale (both E4M3 scales of a lane's two blocks
+//     decoded to an FP16 pair by one conversion);
 //   - the FP16 MFMA (v_mfma_f32_32x32x16_f16) accumulates in FP32;
 //   - the epilogue multiplies by s_tA * s_tB.
 // The roofline of this path is therefore the FP16/BF16 dense MFMA peak.
@@ -61,18 +59,6 @@ __device__ __forceinline__ void raster(int t, int tiles_m, int tiles_n, int& tm,
   const int in = t - group * per_group;
   tm = first_m + in % gsize;
   tn = in / gsize;
-}
-
-struct Scale2 {
-  float s;        // E4M3 scale as FP32 (its exponent drives the conversion)
-  uint32_t m2;    // (1 + f) as an FP16 pair
-};
-
-__device__ __forceinline__ Scale2 decode_scale(uint32_t byte) {
-  Scale2 d;
-  d.s = e4m3_scale_value(byte);
-  d.m2 = scale_mantissa_f16x2(d.s);
-  return d;
 }
 
 template <bool SCALE_QW>
@@ -159,15 +145,14 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       uint4 ca[4], cb[4];
-      Scale2 da[4][2], db[4][2];
+      uint32_t da[4], db[4];   // the lane's two block scales per row, FP16 pair
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = wm * 128 + i * 32 + r;
         ca[i] = sm.a[buf][swz(row, 2 * h + g)];
         const uint2 sc = sm.as[buf][row];
         const uint32_t w = h ? sc.y : sc.x;           // blocks 4h .. 4h+3
-        da[i][0] = decode_scale((w >> (16 * g)) & 0xFFu);
-        da[i][1] = decode_scale((w >> (16 * g + 8)) & 0xFFu);
+        da[i] = e4m3_pair_f16(w >> (16 * g));
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -175,8 +160,7 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
         cb[j] = sm.b[buf][swz(row, 2 * h + g)];
         const uint2 sc = sm.bs[buf][row];
         const uint32_t w = h ? sc.y : sc.x;
-        db[j][0] = decode_scale((w >> (16 * g)) & 0xFFu);
-        db[j][1] = decode_scale((w >> (16 * g + 8)) & 0xFFu);
+        db[j] = e4m3_pair_f16(w >> (16 * g));
       }
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
@@ -184,12 +168,12 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const uint32_t d = sp == 0 ? ca[i].x : sp == 1 ? ca[i].y : sp == 2 ? ca[i].z : ca[i].w;
-          av[i] = dequant8_f16(d, da[i][sp >> 1].s, da[i][sp >> 1].m2);
+          av[i] = dequant8_f16(d, da[i], sp >> 1);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t d = sp == 0 ? cb[j].x : sp == 1 ? cb[j].y : sp == 2 ? cb[j].z : cb[j].w;
-          bv[j] = dequant8_f16(d, db[j][sp >> 1].s, db[j][sp >> 1].m2);
+          bv[j] = dequant8_f16(d, db[j], sp >> 1);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -219,44 +203,21 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_kernel(
 
 
 // Decoded scales of one lane for one half step: the E4M3 scales of its two
-// 16-element blocks as an FP16 pair (block 0 low, block 1 high), from one
-// packed FP8 -> FP16 conversion (exact: every E4M3 value, subnormals
-// included, is an FP16 normal or zero).
+// 16-element blocks as an FP16 pair (block 0 low, block 1 high).
 struct Scales2 {
   uint32_t mp;
 };
 
 __device__ __forceinline__ Scales2 decode_scale_pair(uint32_t word16) {
-  const v2h h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word16, 1.0f, false);
-  Scales2 d;
-  __builtin_memcpy(&d.mp, &h, 4);
-  return d;
+  return Scales2{e4m3_pair_f16(word16)};
 }
 
-// The two halves of the exact expansion, issued apart: the code values
-// (e2m1 as FP16, exact) ...
-__device__ __forceinline__ v8h convert8_f16(uint32_t codes) {
-  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
-  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
-  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
-  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
-  v8h out;
-  out[0] = p0[0]; out[1] = p0[1]; out[2] = p1[0]; out[3] = p1[1];
-  out[4] = p2[0]; out[5] = p2[1]; out[6] = p3[0]; out[7] = p3[1];
-  return out;
-}
-// ... and the multiply by the block's whole scale (half B of the FP16 pair),
-// exact: an e2m1 value times an E4M3 scale has at most 6 significant bits and
-// lies in [2^-10, 2688] or is zero.  (Before: the conversion took 2^E from an
-// FP32 scale and the multiply only (1 + f), which cost two more instructions
-// per scale pair to build; same bits, 1.2-2.4% slower.)
-template <int B>
-__device__ __forceinline__ v8h scale8_f16(const v8h& v, uint32_t mp) {
-  v2h m;
-  __builtin_memcpy(&m, &mp, 4);
-  const v8h mm = {m[B], m[B], m[B], m[B], m[B], m[B], m[B], m[B]};
-  return v * mm;
-}
+// The two halves of the exact expansion are issued apart: the code values
+// (e2m1x8_f16) under one half of a sub-step's MFMAs and the multiply by the
+// block's whole scale (scale8_f16) under the other.  (An earlier form had the
+// conversion take 2^E from an FP32 scale and the multiply only (1 + f), which
+// cost two more instructions per scale pair to build; same bits, 1.2-2.4%
+// slower.)
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& q, int sp) {
   return sp == 0 ? q.x : sp == 1 ? q.y : sp == 2 ? q.z : q.w;
@@ -414,24 +375,22 @@ __global__ __launch_bounds__(NT, 1) void nvfp4_gemm_ring_kernel(
   auto dequant = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      av[i] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.ca[i], sp)), d.a[i].mp)
-                     : scale8_f16<0>(convert8_f16(dword_of(x.ca[i], sp)), d.a[i].mp);
+      av[i] = scale8_f16(e2m1x8_f16(dword_of(x.ca[i], sp)), d.a[i].mp, sp >> 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      bv[j] = (sp >> 1) ? scale8_f16<1>(convert8_f16(dword_of(x.cb[j], sp)), d.b[j].mp)
-                     : scale8_f16<0>(convert8_f16(dword_of(x.cb[j], sp)), d.b[j].mp);
+      bv[j] = scale8_f16(e2m1x8_f16(dword_of(x.cb[j], sp)), d.b[j].mp, sp >> 1);
   };
   auto convert = [&](const NHalf& x, const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = convert8_f16(dword_of(x.ca[i], sp));
+    for (int i = 0; i < 4; ++i) av[i] = e2m1x8_f16(dword_of(x.ca[i], sp));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = convert8_f16(dword_of(x.cb[j], sp));
+    for (int j = 0; j < 4; ++j) bv[j] = e2m1x8_f16(dword_of(x.cb[j], sp));
   };
   auto rescale = [&](const NDec& d, int sp, v8h* av, v8h* bv) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) av[i] = (sp >> 1) ? scale8_f16<1>(av[i], d.a[i].mp) : scale8_f16<0>(av[i], d.a[i].mp);
+    for (int i = 0; i < 4; ++i) av[i] = scale8_f16(av[i], d.a[i].mp, sp >> 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = (sp >> 1) ? scale8_f16<1>(bv[j], d.b[j].mp) : scale8_f16<0>(bv[j], d.b[j].mp);
+    for (int j = 0; j < 4; ++j) bv[j] = scale8_f16(bv[j], d.b[j].mp, sp >> 1);
   };
 
   v16f acc[4][4];
@@ -622,22 +581,15 @@ __global__ __launch_bounds__(256) void nvfp4_small_kernel(
     const uint32_t sa1 = buffer_load_u16(sa, in1 ? r * KB + k0 / 16 + 2 : OOB);
     const uint32_t sb0 = buffer_load_u16(sb, in0 ? r * KB + k0 / 16 : OOB);
     const uint32_t sb1 = buffer_load_u16(sb, in1 ? r * KB + k0 / 16 + 2 : OOB);
-    float xs[4], ys[4];
-    uint32_t xm[4], ym[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t wa = b < 2 ? sa0 : sa1, wb = b < 2 ? sb0 : sb1;
-      xs[b] = e4m3_scale_value((wa >> (8 * (b & 1))) & 0xFFu);
-      ys[b] = e4m3_scale_value((wb >> (8 * (b & 1))) & 0xFFu);
-      xm[b] = scale_mantissa_f16x2(xs[b]);
-      ym[b] = scale_mantissa_f16x2(ys[b]);
-    }
+    // blocks 0-1 and 2-3 of the lane's range as FP16 scale pairs
+    const uint32_t xp[2] = {e4m3_pair_f16(sa0), e4m3_pair_f16(sa1)};
+    const uint32_t yp[2] = {e4m3_pair_f16(sb0), e4m3_pair_f16(sb1)};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t da = t < 4 ? dword_of(a0, t) : dword_of(a1, t - 4);
       const uint32_t db = t < 4 ? dword_of(b0, t) : dword_of(b1, t - 4);
-      const v8h av = dequant8_f16(da, xs[t / 2], xm[t / 2]);
-      const v8h bv = dequant8_f16(db, ys[t / 2], ym[t / 2]);
+      const v8h av = dequant8_f16(da, xp[t / 4], (t / 2) & 1);
+      const v8h bv = dequant8_f16(db, yp[t / 4], (t / 2) & 1);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bv, acc, 0, 0, 0);
     }
   }

@@ -92,10 +92,10 @@ struct GArgs {
 template <bool F16> struct GMath;
 template <> struct GMath<false> {
   typedef v8bf vec;
-  // (1 + f) of the scale as FP32 bits (0 for a zero scale)
-  static __device__ __forceinline__ uint32_t mant(float s) { return __float_as_uint(scale_mantissa_f32(s)); }
-  static __device__ __forceinline__ vec dq8(uint32_t codes, float s, uint32_t m) {
-    return dequant8_bf16(codes, s, __uint_as_float(m));
+  typedef v2f scales;   // a lane's two block scales (bytes 0, 1 of a word), FP32
+  static __device__ __forceinline__ scales decode(uint32_t word) { return e4m3_pair_f32(word); }
+  static __device__ __forceinline__ vec dq8(uint32_t codes, const scales& s, int b) {
+    return dequant8_bf16(codes, b ? s[1] : s[0]);
   }
   static __device__ __forceinline__ v16f mfma(const vec& a, const vec& b, const v16f& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -103,9 +103,9 @@ template <> struct GMath<false> {
 };
 template <> struct GMath<true> {
   typedef v8h vec;
-  // (1 + f) of the scale as an FP16 pair (0 for a zero scale)
-  static __device__ __forceinline__ uint32_t mant(float s) { return scale_mantissa_f16x2(s); }
-  static __device__ __forceinline__ vec dq8(uint32_t codes, float s, uint32_t m) { return dequant8_f16(codes, s, m); }
+  typedef uint32_t scales;   // the two block scales as an FP16 pair
+  static __device__ __forceinline__ scales decode(uint32_t word) { return e4m3_pair_f16(word); }
+  static __device__ __forceinline__ vec dq8(uint32_t codes, const scales& s, int b) { return dequant8_f16(codes, s, b); }
   static __device__ __forceinline__ v16f mfma(const vec& a, const vec& b, const v16f& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -261,18 +261,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(const GArgs p) {
     const int buf = kt & 1;
     if (kt + 1 < KT) gload(kt + 1);
     uint4 ca[4];
-    float sc[4][2];
-    uint32_t mant[4][2];
+    typename GM::scales sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + r;
       ca[i] = sm.a[buf][aswz(row, g)];
       const uint32_t sw = sm.as[buf][row];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        sc[i][b] = e4m3_scale_value((sw >> (16 * g + 8 * b)) & 0xFFu);
-        mant[i][b] = GM::mant(sc[i][b]);
-      }
+      sc[i] = GM::decode(sw >> (16 * g));
     }
 #pragma unroll
     for (int sp = 0; sp < 4; ++sp) {
@@ -280,7 +275,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_kernel(const GArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t d = sp == 0 ? ca[i].x : sp == 1 ? ca[i].y : sp == 2 ? ca[i].z : ca[i].w;
-        av[i] = GM::dq8(d, sc[i][sp >> 1], mant[i][sp >> 1]);
+        av[i] = GM::dq8(d, sc[i], sp >> 1);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -477,8 +472,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
 
   struct AFrag {
     uint4 c[2];
-    float s[2][2];
-    uint32_t m[2][2];   // (1 + f) in the weight type's form (GMath::mant)
+    typename GM::scales s[2];   // the lane's two block scales per row fragment
   };
   // A codes and decoded scales of stage st for this lane's 2 row fragments.
   // The step's 4 scale bytes are dword `in` of the row's SB-byte entry; lane
@@ -491,12 +485,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
       const int row = wave * 64 + i * 32 + r;
       f.c[i] = sm.a[slot][aswz(row, g)];
       const uint32_t word = sm.as[sbuf][row * (SB / 4) + in] >> (16 * g);
-      const v2f sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);   // exact E4M3
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        f.s[i][b] = sv[b];
-        f.m[i][b] = GM::mant(sv[b]);
-      }
+      f.s[i] = GM::decode(word);
     }
   };
   auto read_w = [&](int st, int sp, VT* bv) {
@@ -511,7 +500,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_ring_kernel(const GArgs p) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const uint32_t d = sp == 0 ? f.c[i].x : sp == 1 ? f.c[i].y : sp == 2 ? f.c[i].z : f.c[i].w;
-      av[i] = GM::dq8(d, f.s[i][sp >> 1], f.m[i][sp >> 1]);
+      av[i] = GM::dq8(d, f.s[i], sp >> 1);
     }
   };
 
@@ -871,12 +860,11 @@ __device__ __forceinline__ void pp_tile(const GArgs& p, int grp, int r0, int r1,
       const int row = wq * 32 * MI + i * 32 + r;
       const uint4 c = pp_sm.a[slot][aswz(row, g)];
       const uint32_t word = pp_sm.as[sbuf][row * 4 + IN] >> (16 * g);
-      const v2f sv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(word, 1.0f, false);   // exact E4M3
-      const uint32_t m0 = GM::mant(sv[0]), m1 = GM::mant(sv[1]);
-      av[0][i] = GM::dq8(c.x, sv[0], m0);
-      av[1][i] = GM::dq8(c.y, sv[0], m0);
-      av[2][i] = GM::dq8(c.z, sv[1], m1);
-      av[3][i] = GM::dq8(c.w, sv[1], m1);
+      const typename GM::scales sv = GM::decode(word);
+      av[0][i] = GM::dq8(c.x, sv, 0);
+      av[1][i] = GM::dq8(c.y, sv, 0);
+      av[2][i] = GM::dq8(c.z, sv, 1);
+      av[3][i] = GM::dq8(c.w, sv, 1);
     }
   };
   // This wave's 4 W fragments of sub-step sp of stage st.

@@ -163,10 +163,11 @@ __global__ __launch_bounds__(64 * GV_WAVES) void gemv_kernel(
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float a = acc[r];
-      a = fmaf(block_dot(c0[r].x, c0[r].y, x0[0], x0[1]), e4m3_scale_value(s0[r] & 0xFFu), a);
-      a = fmaf(block_dot(c0[r].z, c0[r].w, x0[2], x0[3]), e4m3_scale_value(s0[r] >> 8), a);
-      a = fmaf(block_dot(c1[r].x, c1[r].y, x1[0], x1[1]), e4m3_scale_value(s1[r] & 0xFFu), a);
-      a = fmaf(block_dot(c1[r].z, c1[r].w, x1[2], x1[3]), e4m3_scale_value(s1[r] >> 8), a);
+      const v2f e0 = e4m3_pair_f32(s0[r]), e1 = e4m3_pair_f32(s1[r]);
+      a = fmaf(block_dot(c0[r].x, c0[r].y, x0[0], x0[1]), e0[0], a);
+      a = fmaf(block_dot(c0[r].z, c0[r].w, x0[2], x0[3]), e0[1], a);
+      a = fmaf(block_dot(c1[r].x, c1[r].y, x1[0], x1[1]), e1[0], a);
+      a = fmaf(block_dot(c1[r].z, c1[r].w, x1[2], x1[3]), e1[1], a);
       acc[r] = a;
     }
   }
@@ -328,15 +329,9 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
                                                              wrow(il) * 8 * SB + 8 * jb + 2 * q)
                         : sr[B][b][il];
       __builtin_amdgcn_sched_barrier(0);
-      float sc[NT][2], mn[NT][2];
+      v2f sc[NT];
 #pragma unroll
-      for (int il = 0; il < NT; ++il) {
-        const uint32_t w16 = w16s[il];
-        sc[il][0] = e4m3_scale_value(w16 & 0xFFu);
-        sc[il][1] = e4m3_scale_value(w16 >> 8);
-        mn[il][0] = scale_mantissa_f32(sc[il][0]);
-        mn[il][1] = scale_mantissa_f32(sc[il][1]);
-      }
+      for (int il = 0; il < NT; ++il) sc[il] = e4m3_pair_f32(w16s[il]);
 #pragma unroll
       for (int sp = 0; sp < 4; ++sp) {
         v8bf_t wv[NT];
@@ -344,9 +339,9 @@ __global__ __launch_bounds__(SK_THREADS, 1) void skinny_kernel(
         for (int il = 0; il < NT; ++il) {
           const uint4& wq = wr[B][b][il];
           const uint32_t d = sp == 0 ? wq.x : sp == 1 ? wq.y : sp == 2 ? wq.z : wq.w;
-          const float sv = sc[il][sp >> 1], mv = mn[il][sp >> 1];
-          const uint32_t w4[4] = {dequant2_bf16<0>(d, sv, mv), dequant2_bf16<1>(d, sv, mv),
-                                  dequant2_bf16<2>(d, sv, mv), dequant2_bf16<3>(d, sv, mv)};
+          const float sv = sc[il][sp >> 1];
+          const uint32_t w4[4] = {dequant2_bf16<0>(d, sv), dequant2_bf16<1>(d, sv),
+                                  dequant2_bf16<2>(d, sv), dequant2_bf16<3>(d, sv)};
           __builtin_memcpy(&wv[il], w4, 16);
         }
 #pragma unroll

@@ -188,7 +188,7 @@ __global__ __launch_bounds__(64 * WN * KS, 1) void w4_tile_kernel(
     };
     uint4 xf[2][MJ];
     read_x(0, xf[0]);
-    float s[WT][NSB], mn[WT][NSB];
+    float s[WT][NSB];
 #pragma unroll
     for (int wt = 0; wt < WT; ++wt) {
       static_for<0, (NSB + 1) / 2>([&](auto BC) {
@@ -197,8 +197,6 @@ __global__ __launch_bounds__(64 * WN * KS, 1) void w4_tile_kernel(
         s[wt][b] = v[0];
         if constexpr (b + 1 < NSB) s[wt][b + 1] = v[1];
       });
-#pragma unroll
-      for (int b = 0; b < NSB; ++b) mn[wt][b] = scale_mantissa_f32(s[wt][b]);
     }
     static_for<0, SUB>([&](auto TC) {
       constexpr int t = decltype(TC)::value;
@@ -208,7 +206,7 @@ __global__ __launch_bounds__(64 * WN * KS, 1) void w4_tile_kernel(
       for (int wt = 0; wt < WT; ++wt) {
         const uint4& q = wc[wt][t / 4];
         const uint32_t d = (t & 3) == 0 ? q.x : (t & 3) == 1 ? q.y : (t & 3) == 2 ? q.z : q.w;
-        wv[wt] = dequant8_bf16(d, s[wt][t >> 1], mn[wt][t >> 1]);
+        wv[wt] = dequant8_bf16(d, s[wt][t >> 1]);
       }
 #pragma unroll
       for (int j = 0; j < MJ; ++j) {

@@ -26,6 +26,8 @@
  *     scales uint8 [R][K/16]  E4M3 (FN) scale of each 16-element block along K
  *     tscale float            FP32 per-tensor decode scale
  *     value  = e2m1(code) * e4m3(scale) * tscale
+ *              e4m3(scale) keeps its sign bit; a NaN scale code (0x7F, 0xFF)
+ *              makes every output its block contributes to NaN
  *   MXFP8 operand [R][K], K % 32 == 0:
  *     codes  uint8 [R][K]     E4M3 (FN) values
  *     scales uint8 [R][K/32]  E8M0 scale of each 32-element block along K

@@ -969,6 +969,93 @@ def test_gemm_nvfp4_every_scale_code(gpu_lib, m, n, k):
     assert_ok(G.check(c, *G.gemm_nvfp4(*qa, *qb)), f"nvfp4 every scale code k={k}")
 
 
+
+# The block scale is a signed E4M3 value (the format's sign bit is part of
+# e4m3(scale)); the quantizer only writes non-negative scales, so these cases
+# set sign bits at random on its output.
+
+def _signed(scales, seed):
+    r = np.random.Generator(np.random.PCG64(seed))
+    return scales | (r.integers(0, 2, scales.shape).astype(np.uint8) << 7)
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 260, 256), (1600, 1400, 256 + 128), (1600, 1400, 1024)])
+def test_gemm_nvfp4_signed_scale_codes(gpu_lib, m, n, k):
+    """All 254 finite E4M3 scale codes, both signs: the small-problem,
+    register-staged and ring kernels."""
+    r = np.random.Generator(np.random.PCG64(7 * k + m))
+    def scales(rows):
+        c = r.integers(0, 254, (rows, k // 16))
+        return (c + (c >= 0x7F)).astype(np.uint8)          # skip the NaN code 0x7F (and 0xFF)
+    qa = (r.integers(0, 256, (m, k // 2)).astype(np.uint8), scales(m), np.float32(0.75))
+    qb = (r.integers(0, 256, (n, k // 2)).astype(np.uint8), scales(n), np.float32(-1.5))
+    say("gemm nvfp4 signed scale codes", m, n, k)
+    c = _gpu_gemm(L.BSGEMM_NVFP4, qa, qb, k)
+    assert_ok(G.check(c, *G.gemm_nvfp4(*qa, *qb)), f"nvfp4 signed scale codes {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 260, 256), (1600, 1400, 256 + 128), (1600, 1400, 1024)])
+def test_gemm_nvfp4_nan_scale_code(gpu_lib, m, n, k):
+    """A NaN scale code (0x7F in A row 5, 0xFF in B row 7) makes every output
+    its block feeds NaN, as the format defines; the rest is unaffected."""
+    qa = Q.quantize_nvfp4(synth.normal_f32((m, k), m + k))
+    qb = Q.quantize_nvfp4(synth.normal_f32((n, k), n + k + 1))
+    qa = (qa[0], qa[1].copy(), qa[2])
+    qb = (qb[0], qb[1].copy(), qb[2])
+    qa[1][5, 0] = 0x7F
+    qb[1][7, k // 16 - 1] = 0xFF
+    say("gemm nvfp4 NaN scale code", m, n, k)
+    c = _gpu_gemm(L.BSGEMM_NVFP4, qa, qb, k)
+    nan = ((c & 0x7F80) == 0x7F80) & ((c & 0x7F) != 0)
+    assert nan[5, :].all() and nan[:, 7].all()
+    keep_r = np.setdiff1d(np.arange(m), [5])
+    keep_c = np.setdiff1d(np.arange(n), [7])
+    assert not nan[np.ix_(keep_r, keep_c)].any()
+    cref, tref = G.gemm_nvfp4(*qa, *qb)
+    assert_ok(G.check(c[np.ix_(keep_r, keep_c)], cref[np.ix_(keep_r, keep_c)], tref[np.ix_(keep_r, keep_c)]),
+              f"nvfp4 NaN scale {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("counts,n,k", [([257, 0, 256, 255], 260, 96), ([77, 256], 260, 320),
+                                        ([512, 256, 0, 300], 512, 1280)])
+def test_grouped_signed_scale_codes(gpu_lib, w_dtype, counts, n, k):
+    qa, off, w, v = _variant_case(counts, n, k, sum(counts) + k, w_dtype)
+    qa = (qa[0], _signed(qa[1], k), qa[2])
+    m = int(off[-1])
+    say("grouped signed scale codes", w_dtype, counts, n, k)
+    c = _gpu_grouped_ex(qa, off, w, k, w_dtype, v, (), m)
+    assert_ok(G.check(c, *_ref_ex(qa, off, w, w_dtype, v, ())), f"grouped signed scales {counts} {w_dtype}")
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+def test_grouped_kragged_signed_scale_codes(gpu_lib, w_dtype):
+    counts, m, n = [100, 0, 700, 256], 300, 260
+    qa, off, w, k = _kragged_case(counts, m, n, 4242, w_dtype)
+    qa = (qa[0], _signed(qa[1], 4243), qa[2])
+    say("grouped K-ragged signed scale codes", w_dtype)
+    c = torch.full((len(counts), m, n), SENTINEL, dtype=torch.int16, device="cuda")
+    L.bsgemm_grouped_kragged_run(dev(qa[0]), dev(qa[1]), dev(np.array([qa[2]], np.float32)), dev(off), dev(w), k,
+                                 w_dtype=L.BSGEMM_W_F16 if w_dtype == "f16" else L.BSGEMM_W_BF16, c=c)
+    got = u16(c)
+    cref, t = G.grouped_kragged(*qa, off, w, w_dtype)
+    for g in range(len(counts)):
+        assert_ok(G.check(got[g], cref[g], t[g]), f"K-ragged signed scales group {g} {w_dtype}")
+
+
+def test_w4a16_signed_scale_codes(gpu_lib):
+    """Every W4A16 configuration, forced, with signed weight scales."""
+    for config, name in enumerate(L.w4a16_configs()):
+        for (m, n, k) in [(1, 300, 1024), (33, 129, 2048)]:
+            x, qw = _w4_case(m, n, k, 31 * config + m)
+            qw = (qw[0], _signed(qw[1], config + k), qw[2])
+            say("w4a16 signed scale codes", name, m, n, k)
+            c = out_bf16(m, n)
+            L.bsgemm_w4a16_run_config(config, dev(x.view(np.int16)), dev(qw[0]), dev(qw[1]),
+                                      dev(np.array([qw[2]], np.float32)), c=c)
+            assert_ok(G.check(u16(c), *G.w4a16(x, *qw)), f"w4a16 signed scales {name} {m}x{n}x{k}")
+
+
 def _group_max_products(a, b, group=8):
     """G[m, n] = sum over aligned groups of `group` K elements of
     max_k |a[m, k] b[n, k]| (float64)."""
