@@ -1056,6 +1056,48 @@ def test_w4a16_signed_scale_codes(gpu_lib):
             assert_ok(G.check(u16(c), *G.w4a16(x, *qw)), f"w4a16 signed scales {name} {m}x{n}x{k}")
 
 
+
+def _bf16_nan(c):
+    return ((c & 0x7F80) == 0x7F80) & ((c & 0x7F) != 0)
+
+
+@pytest.mark.parametrize("w_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("counts,n,k", [([257, 0, 256, 255], 260, 96), ([512, 256, 0, 300], 512, 1280)])
+def test_grouped_nan_scale_code(gpu_lib, w_dtype, counts, n, k):
+    """A NaN scale code in A row 5 makes output row 5 NaN; the rest matches."""
+    qa, off, w, v = _variant_case(counts, n, k, sum(counts) + n, w_dtype)
+    qa = (qa[0], qa[1].copy(), qa[2])
+    qa[1][5, 0] = 0x7F
+    m = int(off[-1])
+    say("grouped NaN scale code", w_dtype, counts, n, k)
+    c = _gpu_grouped_ex(qa, off, w, k, w_dtype, v, (), m)
+    nan = _bf16_nan(c)
+    keep = np.setdiff1d(np.arange(m), [5])
+    assert nan[5].all() and not nan[keep].any()
+    cref, tref = _ref_ex(qa, off, w, w_dtype, v, ())
+    assert_ok(G.check(c[keep], cref[keep], tref[keep]), f"grouped NaN scale {counts} {w_dtype}")
+
+
+def test_w4a16_nan_scale_code(gpu_lib):
+    """Every W4A16 configuration: a NaN scale code in W row 3 makes output
+    column 3 NaN for every activation row; the rest matches."""
+    for config, name in enumerate(L.w4a16_configs()):
+        for (m, n, k) in [(1, 300, 1024), (33, 129, 2048)]:
+            x, qw = _w4_case(m, n, k, 17 * config + m)
+            qw = (qw[0], qw[1].copy(), qw[2])
+            qw[1][3, 1] = 0xFF
+            say("w4a16 NaN scale code", name, m, n, k)
+            c = out_bf16(m, n)
+            L.bsgemm_w4a16_run_config(config, dev(x.view(np.int16)), dev(qw[0]), dev(qw[1]),
+                                      dev(np.array([qw[2]], np.float32)), c=c)
+            got = u16(c)
+            nan = _bf16_nan(got)
+            keep = np.setdiff1d(np.arange(n), [3])
+            assert nan[:, 3].all() and not nan[:, keep].any(), name
+            cref, tref = G.w4a16(x, *qw)
+            assert_ok(G.check(got[:, keep], cref[:, keep], tref[:, keep]), f"w4a16 NaN scale {name} {m}x{n}x{k}")
+
+
 def _group_max_products(a, b, group=8):
     """G[m, n] = sum over aligned groups of `group` K elements of
     max_k |a[m, k] b[n, k]| (float64)."""
